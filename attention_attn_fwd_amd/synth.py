@@ -1,0 +1,109 @@
+"""Seeded synthetic inputs for sink attention (CPU torch tensors).
+
+This module only draws random numbers; it holds none of the attention
+arithmetic.  Tests feed the same draws to the HIP library and to the fp64
+oracle, and bench.py times the library on them.
+
+Workload shapes are gpt-oss shaped: 64 query heads over 8 KV heads, head
+dimension 64, alternating sliding-window-128 / full-causal layers (Megatron-LM
+issue "gpt-oss implementation", "Alternating Sliding-Window Attention
+Pattern"), and a decode batch of 128 sequences of at most 1024 tokens (the
+serve command in tpu-inference PR "[GPT-OSS] JAX implementation of GPT-OSS":
+max-num-seqs 128, max-model-len 1024).  Values are bf16 draws of N(0, std^2)
+and the per-head sinks fp32 draws of N(0, 1).
+
+Draw order inside one generator: (decode lengths), q, k, v, sinks, (dout).
+"""
+
+from dataclasses import dataclass
+
+import torch
+
+__all__ = ["PrefillCase", "DecodeCase", "CONFIGS", "make_prefill", "make_dout",
+           "make_decode", "config_inputs"]
+
+SLIDING_WINDOW = 128
+
+
+@dataclass
+class PrefillCase:
+    q: torch.Tensor      # bf16 [B, S, Hq, D]
+    k: torch.Tensor      # bf16 [B, S, Hkv, D]
+    v: torch.Tensor      # bf16 [B, S, Hkv, D]
+    sinks: torch.Tensor  # fp32 [Hq]
+    scale: float
+
+
+@dataclass
+class DecodeCase:
+    q: torch.Tensor           # bf16 [N, Hq, D]
+    k_cache: torch.Tensor     # bf16 [T, Hkv, D]
+    v_cache: torch.Tensor     # bf16 [T, Hkv, D]
+    cu_seqlens: torch.Tensor  # int32 [N + 1]
+    sinks: torch.Tensor       # fp32 [Hq]
+    max_seqlen: int
+    scale: float
+
+
+def _normal_bf16(gen, shape, std):
+    x = torch.randn(shape, generator=gen, dtype=torch.float32)
+    if std != 1.0:
+        x = x * std
+    return x.to(torch.bfloat16)
+
+
+def make_prefill(B, S, Hq, Hkv, D=64, std=1.0, seed=0, scale=None):
+    gen = torch.Generator().manual_seed(seed)
+    q = _normal_bf16(gen, (B, S, Hq, D), std)
+    k = _normal_bf16(gen, (B, S, Hkv, D), std)
+    v = _normal_bf16(gen, (B, S, Hkv, D), std)
+    sinks = torch.randn((Hq,), generator=gen, dtype=torch.float32)
+    return PrefillCase(q, k, v, sinks, (1.0 / D ** 0.5) if scale is None else scale)
+
+
+def make_dout(shape, seed):
+    gen = torch.Generator().manual_seed(seed)
+    return _normal_bf16(gen, shape, 1.0)
+
+
+def make_decode(N, Hq, Hkv, D=64, max_len=1024, seed=0, lengths=None, std=1.0):
+    """Packed decode batch; lengths ~ U{1..max_len} unless given explicitly."""
+    gen = torch.Generator().manual_seed(seed)
+    if lengths is None:
+        lengths = torch.randint(1, max_len + 1, (N,), generator=gen, dtype=torch.int64)
+    else:
+        lengths = torch.as_tensor(lengths, dtype=torch.int64)
+    cu = torch.zeros(N + 1, dtype=torch.int64)
+    cu[1:] = torch.cumsum(lengths, 0)
+    T = int(cu[-1])
+    q = _normal_bf16(gen, (N, Hq, D), std)
+    kc = _normal_bf16(gen, (T, Hkv, D), std)
+    vc = _normal_bf16(gen, (T, Hkv, D), std)
+    sinks = torch.randn((Hq,), generator=gen, dtype=torch.float32)
+    max_seqlen = max(1, int(lengths.max())) if N > 0 else 1
+    return DecodeCase(q, kc, vc, cu.to(torch.int32), sinks, max_seqlen, 1.0 / D ** 0.5)
+
+
+# The five workloads.  Each prefill config runs one sliding-window-128 layer
+# and one full-causal layer (window 0) over the same tensors.
+CONFIGS = {
+    "c0_b1_s512_h8x1": dict(kind="fwd", B=1, S=512, Hq=8, Hkv=1, std=1.0, seed=1000),
+    "c1_b4_s4096_h64x8": dict(kind="fwd", B=4, S=4096, Hq=64, Hkv=8, std=1.0, seed=1001),
+    "c2_b1_s65536_h64x8": dict(kind="fwd", B=1, S=65536, Hq=64, Hkv=8, std=0.5, seed=1002),
+    "c3_bwd_b4_s4096_h64x8": dict(kind="bwd", B=4, S=4096, Hq=64, Hkv=8, std=1.0, seed=1001,
+                                  dout_seed=1003),
+    "c4_decode_n128_l1024_h64x8": dict(kind="decode", N=128, Hq=64, Hkv=8, max_len=1024,
+                                       seed=1004),
+}
+
+
+def config_inputs(name):
+    """Inputs of one named workload (CPU tensors)."""
+    c = CONFIGS[name]
+    if c["kind"] == "decode":
+        return make_decode(c["N"], c["Hq"], c["Hkv"], max_len=c["max_len"], seed=c["seed"])
+    case = make_prefill(c["B"], c["S"], c["Hq"], c["Hkv"], std=c["std"], seed=c["seed"],
+                        scale=0.125)
+    if c["kind"] == "bwd":
+        return case, make_dout(tuple(case.q.shape), c["dout_seed"])
+    return case

@@ -1,0 +1,198 @@
+"""Plain fp64 CPU oracle for sink attention.  TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this module.  The library (the HIP path behind the C
+ABI) never imports, links or calls it, and it shares no code with that path.
+
+What is computed (the method these pages describe, written out as a plain
+definition, materialising the masked score rows):
+
+* Attention sinks -- Megatron-LM issue "gpt-oss implementation", section
+  "Attention Mechanisms / Attention Sinks"; HF blog "Tricks from OpenAI
+  gpt-oss YOU can use with transformers", paragraph on Flash Attention 3 with
+  attention sinks; tpu-inference PR "[GPT-OSS] JAX implementation of GPT-OSS",
+  review thread on the kernel's ``attention_sink`` argument.  The pages name
+  the feature only.  The reading used here: each query head h owns one learned
+  logit ``sink[h]`` that joins the softmax denominator of every row and has no
+  value vector (so it only drains probability mass); it is not multiplied by
+  the softmax scale.
+* Alternating sliding-window / full-causal layers -- Megatron-LM issue, section
+  "Alternating Sliding-Window Attention Pattern"; HF blog list item "Dynamic
+  Sliding Window Layer & Cache"; torchtitan PR "[WIP] Experimental
+  implementation of gpt-oss (grouped GEMM MoE + FlexAttention sink/sliding)",
+  title and notes.  Reading: ``window == 0`` is full causal; ``window = W >= 1``
+  lets query i see keys j with ``i - W < j <= i`` (W keys including itself).
+* Grouped-query heads: query head h reads K/V head ``h // (Hq // Hkv)``.
+* Decode (one new token per sequence over a packed per-sequence KV cache) is
+  row ``L - 1`` of the same definition over that sequence's ``L`` cached keys
+  (the HF blog's "Continuous Batching & Paged Attention" and the serve command
+  in the tpu-inference PR give the workload; the maths is the prefill row).
+
+Definition, per batch b, query head h, query row i (kv head c = h // G):
+
+    s_ij  = scale * <q[b,i,h,:], k[b,j,c,:]>     for allowed (i, j), else -inf
+    M_i   = max(sink_h, max_j s_ij)
+    Z_i   = exp(sink_h - M_i) + sum_j exp(s_ij - M_i)
+    P_ij  = exp(s_ij - M_i) / Z_i
+    out[b,i,h,:] = sum_j P_ij v[b,j,c,:]
+    lse[b,h,i]   = M_i + ln Z_i            (natural log, sink included)
+
+Backward of L = sum(dout * out) (the sink's value vector is zero, so its
+score gradient is P_sink * (0 - Dvec)):
+
+    Dvec_i  = <dout_i, out_i>
+    dS_ij   = P_ij * (<dout_i, v_j> - Dvec_i)
+    dq_i    = scale * sum_j dS_ij k_j
+    dk_j    = scale * sum_{h in group} sum_i dS_ij q_i
+    dv_j    = sum_{h in group} sum_i P_ij dout_i
+    dsink_h = - sum_{b,i} exp(sink_h - lse_{b,h,i}) * Dvec_{b,h,i}
+
+Arrays are float64 numpy arrays in the layouts [B, S, H, D] (q, k, v, out,
+dout) and [B, H, S] (lse).  Callers upcast bf16 inputs exactly.  The only
+library primitives used are numpy's matrix product, exp, log and sums; the
+row loop is a memory bound only (every row is independent).
+
+Pins: tests/test_oracle.py checks this module against a scalar brute force,
+hand-derived exact cases (tests/golden/hand_cases.json), torch's fp64
+scaled_dot_product_attention through an augmented-key reduction, closed forms,
+the four invariants, and central finite differences for the backward.
+"""
+
+import numpy as np
+
+__all__ = ["allowed_mask", "ref_fwd", "ref_bwd", "ref_decode", "unmasked_pairs"]
+
+
+def allowed_mask(rows, keys, window):
+    """Boolean [len(rows), len(keys)]: key j visible from query i.
+
+    Causal (j <= i) and, for window W >= 1, inside the window (i - j < W).
+    """
+    i = np.asarray(rows, dtype=np.int64)[:, None]
+    j = np.asarray(keys, dtype=np.int64)[None, :]
+    ok = j <= i
+    if window > 0:
+        ok &= (i - j) < window
+    return ok
+
+
+def unmasked_pairs(S, window):
+    """Number of allowed (i, j) pairs of one (batch, head) -- counted directly."""
+    total = 0
+    for i in range(S):
+        lo = 0 if window == 0 else max(0, i - window + 1)
+        total += i - lo + 1
+    return total
+
+
+def _key_range(rows, window):
+    """Keys [lo, hi] that can be visible from any of ``rows``."""
+    lo = 0 if window == 0 else max(0, int(np.min(rows)) - window + 1)
+    hi = int(np.max(rows))
+    return lo, hi
+
+
+def _row_softmax(s, sink):
+    """Return (P, lse) for score rows ``s`` (masked = -inf) and one sink logit."""
+    M = np.maximum(sink, s.max(axis=1))
+    e = np.exp(s - M[:, None])
+    Z = np.exp(sink - M) + e.sum(axis=1)
+    return e / Z[:, None], M + np.log(Z)
+
+
+def ref_fwd(q, k, v, sinks, window, scale, rows=None, heads=None,
+            batches=None, row_block=512):
+    """Forward: returns (out [B,S,Hq,D], lse [B,Hq,S]) in fp64.
+
+    ``rows``/``heads``/``batches`` restrict which outputs are computed (others
+    are left NaN); each computed row uses all of its visible keys, so it is
+    exact.  ``row_block`` only bounds memory.
+    """
+    B, S, Hq, D = q.shape
+    Hkv = k.shape[2]
+    G = Hq // Hkv
+    out = np.full((B, S, Hq, D), np.nan)
+    lse = np.full((B, Hq, S), np.nan)
+    rows = np.arange(S) if rows is None else np.asarray(rows, dtype=np.int64)
+    heads = range(Hq) if heads is None else heads
+    batches = range(B) if batches is None else batches
+    for b in batches:
+        for h in heads:
+            c = h // G
+            for r0 in range(0, len(rows), row_block):
+                rb = rows[r0:r0 + row_block]
+                lo, hi = _key_range(rb, window)
+                keys = np.arange(lo, hi + 1)
+                s = scale * (q[b, rb, h, :] @ k[b, lo:hi + 1, c, :].T)
+                s = np.where(allowed_mask(rb, keys, window), s, -np.inf)
+                P, l = _row_softmax(s, float(sinks[h]))
+                out[b, rb, h, :] = P @ v[b, lo:hi + 1, c, :]
+                lse[b, h, rb] = l
+    return out, lse
+
+
+def ref_bwd(q, k, v, sinks, dout, window, scale, heads=None, batches=None):
+    """Backward of sum(dout * out): returns (dq, dk, dv, dsinks) in fp64.
+
+    Recomputes the forward (its own fp64 out and lse) per (batch, head).
+    With ``heads``/``batches`` given, dq covers those heads only, dk/dv sum the
+    contributions of those heads only, and dsinks sums over those batches.
+    """
+    B, S, Hq, D = q.shape
+    Hkv = k.shape[2]
+    G = Hq // Hkv
+    dq = np.zeros_like(q, dtype=np.float64)
+    dk = np.zeros_like(k, dtype=np.float64)
+    dv = np.zeros_like(v, dtype=np.float64)
+    dsinks = np.zeros(Hq)
+    heads = range(Hq) if heads is None else heads
+    batches = range(B) if batches is None else batches
+    pos = np.arange(S)
+    mask = allowed_mask(pos, pos, window)
+    for b in batches:
+        for h in heads:
+            c = h // G
+            Q, K, V, dO = q[b, :, h, :], k[b, :, c, :], v[b, :, c, :], dout[b, :, h, :]
+            s = np.where(mask, scale * (Q @ K.T), -np.inf)
+            P, lse = _row_softmax(s, float(sinks[h]))
+            O = P @ V
+            Dvec = (dO * O).sum(axis=1)
+            dP = dO @ V.T
+            dS = P * (dP - Dvec[:, None])
+            dq[b, :, h, :] = scale * (dS @ K)
+            dk[b, :, c, :] += scale * (dS.T @ Q)
+            dv[b, :, c, :] += P.T @ dO
+            dsinks[h] -= np.sum(np.exp(float(sinks[h]) - lse) * Dvec)
+    return dq, dk, dv, dsinks
+
+
+def ref_decode(q, k_cache, v_cache, cu_seqlens, sinks, window, scale):
+    """Decode: one query per sequence over its packed KV rows.
+
+    q [N, Hq, D]; k_cache, v_cache [T, Hkv, D]; sequence n owns cache rows
+    cu_seqlens[n] .. cu_seqlens[n+1]-1 (L_n of them, the new token's K/V last).
+    The query sits at position L_n - 1.  Returns (out [N,Hq,D], lse [N,Hq]).
+    An empty sequence (L_n = 0) sees only the sink: out = 0, lse = sink.
+    """
+    N, Hq, D = q.shape
+    Hkv = k_cache.shape[1]
+    G = Hq // Hkv
+    out = np.zeros((N, Hq, D))
+    lse = np.zeros((N, Hq))
+    for n in range(N):
+        base, L = int(cu_seqlens[n]), int(cu_seqlens[n + 1] - cu_seqlens[n])
+        for h in range(Hq):
+            sink = float(sinks[h])
+            if L == 0:
+                out[n, h, :] = 0.0
+                lse[n, h] = sink
+                continue
+            c = h // G
+            keys = np.arange(L)
+            ok = allowed_mask([L - 1], keys, window)[0]
+            s = scale * (k_cache[base:base + L, c, :] @ q[n, h, :])
+            s = np.where(ok, s, -np.inf)[None, :]
+            P, l = _row_softmax(s, sink)
+            out[n, h, :] = (P @ v_cache[base:base + L, c, :])[0]
+            lse[n, h] = l[0]
+    return out, lse
