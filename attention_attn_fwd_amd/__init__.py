@@ -1,0 +1,132 @@
+"""MI355X (gfx950) sink attention: causal / sliding-window grouped-query
+attention with a learned per-head sink logit, behind a C ABI.
+
+Python layer = argument marshalling over libgptoss_attn.so (see
+include/gptoss_attn.h).  torch provides device memory and the current stream;
+all computation runs in the library's HIP kernels.
+
+    out, lse = fwd(q, k, v, sinks, window, scale)
+    dq, dk, dv, dsinks = bwd(q, k, v, sinks, out, lse, dout, window, scale)
+    out, lse = decode(q, k_cache, v_cache, cu_seqlens, sinks, max_seqlen, window, scale)
+"""
+
+import torch
+
+from . import _lib
+from ._lib import AttnError
+
+__all__ = ["fwd", "bwd", "decode", "bwd_workspace_size", "decode_workspace_size", "AttnError",
+           "abi_version"]
+
+
+def _need(t, name, dtype, ndim):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got shape {tuple(t.shape)}")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a HIP device, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _stream(dev):
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+def abi_version():
+    return _lib.load().gptoss_attn_abi_version()
+
+
+def fwd(q, k, v, sinks, window=0, scale=None, out=None, lse=None):
+    """Prefill forward.  q [B,S,Hq,D], k/v [B,S,Hkv,D] bf16; sinks [Hq] fp32.
+
+    Returns (out bf16 [B,S,Hq,D], lse fp32 [B,Hq,S]).
+    """
+    _need(q, "q", torch.bfloat16, 4)
+    _need(k, "k", torch.bfloat16, 4)
+    _need(v, "v", torch.bfloat16, 4)
+    _need(sinks, "sinks", torch.float32, 1)
+    B, S, Hq, D = q.shape
+    Hkv = k.shape[2]
+    if k.shape != (B, S, Hkv, D) or v.shape != k.shape or sinks.shape != (Hq,):
+        raise ValueError("shape mismatch among q, k, v, sinks")
+    scale = (1.0 / D ** 0.5) if scale is None else float(scale)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, Hq, S), dtype=torch.float32, device=q.device)
+    _need(out, "out", torch.bfloat16, 4)
+    _need(lse, "lse", torch.float32, 3)
+    lib = _lib.load()
+    st = lib.gptoss_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), sinks.data_ptr(), B, S, Hq, Hkv, D,
+                             int(window), scale, out.data_ptr(), lse.data_ptr(), _stream(q.device))
+    _lib.check(st, lib)
+    return out, lse
+
+
+def bwd_workspace_size(B, S, Hq, Hkv, D=64, window=0):
+    return int(_lib.load().gptoss_attn_bwd_workspace_size(B, S, Hq, Hkv, D, int(window)))
+
+
+def bwd(q, k, v, sinks, out, lse, dout, window=0, scale=None, workspace=None):
+    """Backward of sum(dout * out).  Returns (dq, dk, dv bf16, dsinks fp32 [Hq])."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (out, "out"), (dout, "dout")):
+        _need(t, n, torch.bfloat16, 4)
+    _need(sinks, "sinks", torch.float32, 1)
+    _need(lse, "lse", torch.float32, 3)
+    B, S, Hq, D = q.shape
+    Hkv = k.shape[2]
+    if (k.shape != (B, S, Hkv, D) or v.shape != k.shape or out.shape != q.shape or dout.shape != q.shape
+            or lse.shape != (B, Hq, S) or sinks.shape != (Hq,)):
+        raise ValueError("shape mismatch among backward inputs")
+    scale = (1.0 / D ** 0.5) if scale is None else float(scale)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    dsinks = torch.empty((Hq,), dtype=torch.float32, device=q.device)
+    need = bwd_workspace_size(B, S, Hq, Hkv, D, window)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    lib = _lib.load()
+    st = lib.gptoss_attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), sinks.data_ptr(), out.data_ptr(),
+                             lse.data_ptr(), dout.data_ptr(), B, S, Hq, Hkv, D, int(window), scale,
+                             dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), dsinks.data_ptr(),
+                             workspace.data_ptr(), workspace.numel(), _stream(q.device))
+    _lib.check(st, lib)
+    return dq, dk, dv, dsinks
+
+
+def decode_workspace_size(N, Hq, Hkv, D=64, max_seqlen=1, window=0):
+    return int(_lib.load().gptoss_attn_decode_workspace_size(N, Hq, Hkv, D, max_seqlen, int(window)))
+
+
+def decode(q, k_cache, v_cache, cu_seqlens, sinks, max_seqlen, window=0, scale=None, out=None, lse=None,
+           workspace=None):
+    """Decode one token per sequence.  q [N,Hq,D]; caches [T,Hkv,D] bf16;
+    cu_seqlens int32 [N+1] on the device.  Returns (out bf16 [N,Hq,D], lse fp32 [N,Hq])."""
+    _need(q, "q", torch.bfloat16, 3)
+    _need(k_cache, "k_cache", torch.bfloat16, 3)
+    _need(v_cache, "v_cache", torch.bfloat16, 3)
+    _need(cu_seqlens, "cu_seqlens", torch.int32, 1)
+    _need(sinks, "sinks", torch.float32, 1)
+    N, Hq, D = q.shape
+    Hkv = k_cache.shape[1]
+    if (v_cache.shape != k_cache.shape or k_cache.shape[2] != D or cu_seqlens.shape != (N + 1,)
+            or sinks.shape != (Hq,)):
+        raise ValueError("shape mismatch among decode inputs")
+    scale = (1.0 / D ** 0.5) if scale is None else float(scale)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((N, Hq), dtype=torch.float32, device=q.device)
+    need = decode_workspace_size(N, Hq, Hkv, D, max_seqlen, window)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    lib = _lib.load()
+    st = lib.gptoss_attn_decode(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), cu_seqlens.data_ptr(),
+                                sinks.data_ptr(), N, Hq, Hkv, D, int(max_seqlen), int(window), scale,
+                                out.data_ptr(), lse.data_ptr(), workspace.data_ptr(), workspace.numel(),
+                                _stream(q.device))
+    _lib.check(st, lib)
+    return out, lse

@@ -1,0 +1,230 @@
+// C ABI of the sink-attention library: argument validation, device check,
+// workspace sizing and dispatch to the gfx950 kernels.  Every argument error
+// is caught here, before any HIP call, and reported through a status code
+// plus a per-thread message.
+#include "gptoss_attn.h"
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "launch.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+gptoss_status fail(gptoss_status st, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return st;
+}
+
+gptoss_status ok() {
+    g_last_error.clear();
+    return GPTOSS_OK;
+}
+
+constexpr long long kIndexLimit = (1LL << 31) - 1;  // kernels index rows in int32
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+#define CHECK_PTR(p, align)                                                                  \
+    do {                                                                                     \
+        if ((p) == nullptr) return fail(GPTOSS_ERR_INVALID_ARGUMENT, "%s is NULL", #p);      \
+        if (!aligned((p), (align)))                                                          \
+            return fail(GPTOSS_ERR_INVALID_ARGUMENT, "%s is not %d-byte aligned", #p, (int)(align)); \
+    } while (0)
+
+// Heads / dims / window / scale checks shared by the three entry points.
+gptoss_status check_common(int Hq, int Hkv, int D, int window, float scale) {
+    if (Hq < 1 || Hkv < 1)
+        return fail(GPTOSS_ERR_INVALID_ARGUMENT, "Hq (%d) and Hkv (%d) must be >= 1", Hq, Hkv);
+    if (Hq % Hkv != 0)
+        return fail(GPTOSS_ERR_INVALID_ARGUMENT, "Hq (%d) is not a multiple of Hkv (%d)", Hq, Hkv);
+    if (window < 0) return fail(GPTOSS_ERR_INVALID_ARGUMENT, "window (%d) must be >= 0", window);
+    if (!std::isfinite(scale) || !(scale > 0.0f))
+        return fail(GPTOSS_ERR_INVALID_ARGUMENT, "softmax_scale (%g) must be finite and > 0", (double)scale);
+    if (D != 64) return fail(GPTOSS_ERR_UNSUPPORTED, "head_dim %d is not supported (only 64)", D);
+    if (Hq / Hkv > 128)
+        return fail(GPTOSS_ERR_UNSUPPORTED, "group size Hq/Hkv = %d exceeds 128", Hq / Hkv);
+    return GPTOSS_OK;
+}
+
+// gfx950 check, cached per device (0 = unknown, 1 = ok, 2 = not gfx950).
+std::atomic<int> g_dev_ok[64];
+
+gptoss_status check_device() {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(GPTOSS_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev >= 0 && dev < 64 && g_dev_ok[dev].load(std::memory_order_relaxed) == 1) return GPTOSS_OK;
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess) return fail(GPTOSS_ERR_HIP, "hipGetDeviceProperties: %s", hipGetErrorString(e));
+    const bool is950 = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    if (dev >= 0 && dev < 64) g_dev_ok[dev].store(is950 ? 1 : 2, std::memory_order_relaxed);
+    if (!is950)
+        return fail(GPTOSS_ERR_UNSUPPORTED, "device %d is %s; this library is built for gfx950 only", dev,
+                    prop.gcnArchName);
+    return GPTOSS_OK;
+}
+
+gptoss_status launched(hipError_t e, const char* what) {
+    if (e != hipSuccess) return fail(GPTOSS_ERR_HIP, "%s launch failed: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int gptoss_attn_abi_version(void) { return GPTOSS_ATTN_ABI_VERSION; }
+
+const char* gptoss_attn_last_error(void) { return g_last_error.c_str(); }
+
+gptoss_status gptoss_attn_fwd(const void* q, const void* k, const void* v, const float* sinks, int B, int S,
+                              int Hq, int Hkv, int D, int window, float softmax_scale, void* out, float* lse,
+                              void* stream) {
+    if (B < 0 || S < 0) return fail(GPTOSS_ERR_INVALID_ARGUMENT, "B (%d) and S (%d) must be >= 0", B, S);
+    gptoss_status st = check_common(Hq, Hkv, D, window, softmax_scale);
+    if (st != GPTOSS_OK) return st;
+    if (B == 0 || S == 0) return ok();
+    if ((long long)B * S > kIndexLimit)
+        return fail(GPTOSS_ERR_INVALID_ARGUMENT, "B*S = %lld exceeds 2^31-1", (long long)B * S);
+    CHECK_PTR(q, 16);
+    CHECK_PTR(k, 16);
+    CHECK_PTR(v, 16);
+    CHECK_PTR(sinks, 4);
+    CHECK_PTR(out, 16);
+    CHECK_PTR(lse, 4);
+    st = check_device();
+    if (st != GPTOSS_OK) return st;
+    gptoss::FwdArgs a;
+    a.q = static_cast<const uint16_t*>(q);
+    a.k = static_cast<const uint16_t*>(k);
+    a.v = static_cast<const uint16_t*>(v);
+    a.sinks = sinks;
+    a.out = static_cast<uint16_t*>(out);
+    a.lse = lse;
+    a.B = B;
+    a.S = S;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.window = window;
+    a.scale = softmax_scale;
+    return launched(gptoss::launch_fwd(a, static_cast<hipStream_t>(stream)), "forward");
+}
+
+size_t gptoss_attn_bwd_workspace_size(int B, int S, int Hq, int Hkv, int D, int window) {
+    if (B <= 0 || S <= 0 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || D != 64 || window < 0) return 0;
+    return gptoss::bwd_workspace_bytes(B, S, Hq, Hkv, window);
+}
+
+gptoss_status gptoss_attn_bwd(const void* q, const void* k, const void* v, const float* sinks, const void* out,
+                              const float* lse, const void* dout, int B, int S, int Hq, int Hkv, int D,
+                              int window, float softmax_scale, void* dq, void* dk, void* dv, float* dsinks,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+    if (B < 0 || S < 0) return fail(GPTOSS_ERR_INVALID_ARGUMENT, "B (%d) and S (%d) must be >= 0", B, S);
+    gptoss_status st = check_common(Hq, Hkv, D, window, softmax_scale);
+    if (st != GPTOSS_OK) return st;
+    if (B == 0 || S == 0) return ok();
+    if ((long long)B * S > kIndexLimit)
+        return fail(GPTOSS_ERR_INVALID_ARGUMENT, "B*S = %lld exceeds 2^31-1", (long long)B * S);
+    CHECK_PTR(q, 16);
+    CHECK_PTR(k, 16);
+    CHECK_PTR(v, 16);
+    CHECK_PTR(sinks, 4);
+    CHECK_PTR(out, 16);
+    CHECK_PTR(lse, 4);
+    CHECK_PTR(dout, 16);
+    CHECK_PTR(dq, 16);
+    CHECK_PTR(dk, 16);
+    CHECK_PTR(dv, 16);
+    CHECK_PTR(dsinks, 4);
+    const size_t need = gptoss::bwd_workspace_bytes(B, S, Hq, Hkv, window);
+    if (workspace_bytes < need)
+        return fail(GPTOSS_ERR_INVALID_ARGUMENT, "workspace_bytes %zu < required %zu", workspace_bytes, need);
+    if (need > 0) CHECK_PTR(workspace, 256);
+    st = check_device();
+    if (st != GPTOSS_OK) return st;
+    gptoss::BwdArgs a;
+    a.q = static_cast<const uint16_t*>(q);
+    a.k = static_cast<const uint16_t*>(k);
+    a.v = static_cast<const uint16_t*>(v);
+    a.sinks = sinks;
+    a.out = static_cast<const uint16_t*>(out);
+    a.lse = lse;
+    a.dout = static_cast<const uint16_t*>(dout);
+    a.dq = static_cast<uint16_t*>(dq);
+    a.dk = static_cast<uint16_t*>(dk);
+    a.dv = static_cast<uint16_t*>(dv);
+    a.dsinks = dsinks;
+    a.workspace = workspace;
+    a.B = B;
+    a.S = S;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.window = window;
+    a.scale = softmax_scale;
+    return launched(gptoss::launch_bwd(a, static_cast<hipStream_t>(stream)), "backward");
+}
+
+size_t gptoss_attn_decode_workspace_size(int N, int Hq, int Hkv, int D, int max_seqlen, int window) {
+    if (N <= 0 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || D != 64 || max_seqlen < 1 || window < 0) return 0;
+    return gptoss::decode_workspace_bytes(N, Hq, Hkv, max_seqlen, window);
+}
+
+gptoss_status gptoss_attn_decode(const void* q, const void* k_cache, const void* v_cache, const int* cu_seqlens,
+                                 const float* sinks, int N, int Hq, int Hkv, int D, int max_seqlen, int window,
+                                 float softmax_scale, void* out, float* lse, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+    if (N < 0) return fail(GPTOSS_ERR_INVALID_ARGUMENT, "N (%d) must be >= 0", N);
+    if (max_seqlen < 1) return fail(GPTOSS_ERR_INVALID_ARGUMENT, "max_seqlen (%d) must be >= 1", max_seqlen);
+    gptoss_status st = check_common(Hq, Hkv, D, window, softmax_scale);
+    if (st != GPTOSS_OK) return st;
+    if (N == 0) return ok();
+    if ((long long)N > 65535)
+        return fail(GPTOSS_ERR_INVALID_ARGUMENT, "N (%d) exceeds 65535 sequences per call", N);
+    CHECK_PTR(q, 16);
+    CHECK_PTR(k_cache, 16);
+    CHECK_PTR(v_cache, 16);
+    CHECK_PTR(cu_seqlens, 4);
+    CHECK_PTR(sinks, 4);
+    CHECK_PTR(out, 16);
+    CHECK_PTR(lse, 4);
+    const size_t need = gptoss::decode_workspace_bytes(N, Hq, Hkv, max_seqlen, window);
+    if (workspace_bytes < need)
+        return fail(GPTOSS_ERR_INVALID_ARGUMENT, "workspace_bytes %zu < required %zu", workspace_bytes, need);
+    if (need > 0) CHECK_PTR(workspace, 256);
+    st = check_device();
+    if (st != GPTOSS_OK) return st;
+    gptoss::DecodeArgs a;
+    a.q = static_cast<const uint16_t*>(q);
+    a.k_cache = static_cast<const uint16_t*>(k_cache);
+    a.v_cache = static_cast<const uint16_t*>(v_cache);
+    a.cu_seqlens = cu_seqlens;
+    a.sinks = sinks;
+    a.out = static_cast<uint16_t*>(out);
+    a.lse = lse;
+    a.workspace = workspace;
+    a.N = N;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.max_seqlen = max_seqlen;
+    a.window = window;
+    a.scale = softmax_scale;
+    return launched(gptoss::launch_decode(a, static_cast<hipStream_t>(stream)), "decode");
+}
+
+}  // extern "C"

@@ -1,0 +1,545 @@
+// Training backward of grouped-query sink attention (gfx950).
+//
+// Loss L = sum(dout * out).  With P_ij = exp(s_ij - lse_i) (lse includes the
+// sink, so P is the exact softmax probability) and Dvec_i = <dout_i, out_i>:
+//   dS_ij   = P_ij (<dout_i, v_j> - Dvec_i)
+//   dq_i    = scale sum_j dS_ij k_j
+//   dk_j    = scale sum_{h in group} sum_i dS_ij q_i
+//   dv_j    = sum_{h in group} sum_i P_ij dout_i
+//   dsink_h = -sum_{b,i} exp(sink_h - lse_i) Dvec_i
+// (the sink's value vector is zero, so its score gradient is
+// P_sink (0 - Dvec); Megatron-LM issue "gpt-oss implementation", "Attention
+// Sinks", names the feature; the pages give no formula.)
+//
+// Four launches on the caller's stream (pre, dkdv, dq, dsink), no atomics,
+// deterministic:
+//   pre    : Dvec and lse*log2(e) per (b, position, head) -> workspace
+//   dkdv   : key-outer.  A workgroup owns 128 keys of one KV head (32 per
+//            wave) and walks the query columns (position, head-of-group) that
+//            can see them, 64 columns per step.  S = Q K^T and dP = dO V^T
+//            put one key per lane and the columns in the accumulator
+//            registers, which is the operand layout of the two products
+//            that contract over columns: dV^T += dO^T P and dK^T += Q^T dS.
+//            Q^T and dO^T come from the row-major LDS tiles through
+//            transposing LDS reads.
+//   dq     : query-outer, like the forward: S^T = K Q^T and dP^T = V dO^T
+//            put one column per lane, which is the operand layout of
+//            dQ^T += K^T dS^T (K^T through transposing LDS reads).
+//   dsink  : one workgroup per head reduces the per-row terms the dq kernel
+//            left in the workspace.
+// P and dP are recomputed in both the key-outer and query-outer kernels.
+// dsink does not use Dvec = <dout, out>, whose bf16 `out` carries rounding
+// that a cancelling sum over all rows would amplify: the dq kernel forms
+// r_i = sum_j P_ij dP_ij (= <dout_i, sum_j P_ij v_j>, the same quantity) in
+// fp32 while it sweeps row i's keys and stores exp(sink - lse_i) r_i.
+#include "common.h"
+#include "launch.h"
+
+namespace gptoss {
+namespace {
+
+constexpr int kThreads = 256;
+
+struct BwdParams {
+    const uint16_t* q;
+    const uint16_t* k;
+    const uint16_t* v;
+    const uint16_t* out;
+    const uint16_t* dout;
+    const float* lse;
+    const float* sinks;
+    uint16_t* dq;
+    uint16_t* dk;
+    uint16_t* dv;
+    float* dsinks;
+    float2* ld;  // [B][S][Hq] {lse * log2(e), Dvec}; .x later holds the dsink term
+    int B, S, Hq, Hkv, G, window;
+    float scale;
+    float c;  // scale * log2(e)
+};
+
+// ---------------------------------------------------------------------------
+// pre: 8 lanes per (b, position, head) row, 16 bytes of out and dout each.
+__global__ void __launch_bounds__(kThreads)
+bwd_pre_kernel(BwdParams p, long long rows) {
+    const long long row = (long long)blockIdx.x * 32 + (threadIdx.x >> 3);
+    const int chunk = threadIdx.x & 7;
+    float acc = 0.0f;
+    if (row < rows) {
+        const uint4 o = ld16(p.out + row * kHeadDim + 8 * chunk);
+        const uint4 d = ld16(p.dout + row * kHeadDim + 8 * chunk);
+        const uint32_t ow[4] = {o.x, o.y, o.z, o.w}, dw[4] = {d.x, d.y, d.z, d.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            acc = fmaf(bf16_lo(ow[i]), bf16_lo(dw[i]), acc);
+            acc = fmaf(bf16_hi(ow[i]), bf16_hi(dw[i]), acc);
+        }
+    }
+    acc += __shfl_xor(acc, 1);
+    acc += __shfl_xor(acc, 2);
+    acc += __shfl_xor(acc, 4);
+    if (row < rows && chunk == 0) {
+        const int h = (int)(row % p.Hq);
+        const long long bs = row / p.Hq;
+        const int pos = (int)(bs % p.S);
+        const int b = (int)(bs / p.S);
+        const float l = p.lse[((size_t)b * p.Hq + h) * p.S + pos];
+        p.ld[row] = make_float2(l * kLog2e, acc);
+    }
+}
+
+// dsink: one workgroup per head sums the rows' exp(sink - lse) r terms.
+__global__ void __launch_bounds__(kThreads)
+bwd_dsink_kernel(BwdParams p) {
+    __shared__ float red[kThreads / 64];
+    const int h = blockIdx.x;
+    const long long n = (long long)p.B * p.S;
+    float acc = 0.0f;
+    for (long long i = threadIdx.x; i < n; i += kThreads) acc += p.ld[i * p.Hq + h].x;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = acc;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        float t = 0.0f;
+        for (int w = 0; w < kThreads / 64; ++w) t += red[w];
+        p.dsinks[h] = -t;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// dkdv: key-outer.
+constexpr int kKeysPerBlock = 128;
+constexpr int kColsPerStep = 64;
+
+__device__ __forceinline__ void dkdv_coords(const BwdParams& p, int n_kt, int bid, int& grp, int& kt) {
+    const int n_groups = p.B * p.Hkv;
+    if ((n_groups & 7) == 0) {
+        const int xcd = bid & 7, slot = bid >> 3;
+        grp = xcd * (n_groups >> 3) + slot / n_kt;
+        kt = slot % n_kt;  // low key tiles (most queries) first
+    } else {
+        grp = bid % n_groups;
+        kt = bid / n_groups;
+    }
+}
+
+__global__ void __launch_bounds__(kThreads, 2)
+bwd_dkdv_kernel(BwdParams p, int n_kt) {
+    __shared__ uint4 sQ[2][512];
+    __shared__ uint4 sO[2][512];
+    __shared__ float2 sLD[2][kColsPerStep];
+    __shared__ int sPos[2][kColsPerStep];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int g = lane >> 5, l32 = lane & 31, i16 = lane & 15;
+    int grp, kt;
+    dkdv_coords(p, n_kt, blockIdx.x, grp, kt);
+    const int b = grp / p.Hkv, kvh = grp % p.Hkv;
+    const int S = p.S, W = p.window, G = p.G, Hq = p.Hq;
+    const int k0 = kt * kKeysPerBlock;
+    const int kw0 = k0 + 32 * wave;          // this wave's keys kw0 .. kw0+31
+    const int kw1 = min(kw0 + 31, S - 1);
+    const bool wave_active = kw0 < S;
+    const int my_key = kw0 + l32;
+
+    // K and V rows of this lane's key as B operands (d = 16 ks + 8 g + 0..7)
+    const size_t kv_stride = (size_t)p.Hkv * kHeadDim;
+    bf16x8 kb[4], vb[4];
+    {
+        const size_t off = ((size_t)b * S + my_key) * kv_stride + (size_t)kvh * kHeadDim;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            uint4 x = make_uint4(0, 0, 0, 0), y = make_uint4(0, 0, 0, 0);
+            if (my_key < S) {
+                x = ld16(p.k + off + 16 * ks + 8 * g);
+                y = ld16(p.v + off + 16 * ks + 8 * g);
+            }
+            kb[ks] = as_bf16x8(x);
+            vb[ks] = as_bf16x8(y);
+        }
+    }
+
+    // query columns that can see keys [k0, k0 + 127]
+    const int pos_lo = k0;
+    const int pos_hi = W > 0 ? min(S - 1, k0 + kKeysPerBlock - 1 + W - 1) : S - 1;
+    const int n_cols = (pos_hi - pos_lo + 1) * G;
+    const int n_steps = (n_cols + kColsPerStep - 1) / kColsPerStep;
+
+    f32x16 dkacc[2], dvacc[2];
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dkacc[db][r] = dvacc[db][r] = 0.0f;
+
+    // staging: rows (columns) tid/8 and tid/8 + 32, unit tid % 8
+    const int st_row = tid >> 3, st_unit = tid & 7;
+    uint4 rq[2], ro[2];
+    float2 rld = make_float2(INFINITY, 0.0f);
+    int rpos = 0;
+    auto col_addr = [&](int c, int& pos, int& head) {
+        pos = pos_lo + c / G;
+        head = kvh * G + c % G;
+    };
+    auto load_step = [&](int st) {
+        const int c0 = st * kColsPerStep;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int c = c0 + st_row + 32 * j;
+            rq[j] = make_uint4(0, 0, 0, 0);
+            ro[j] = make_uint4(0, 0, 0, 0);
+            if (c < n_cols) {
+                int pos, head;
+                col_addr(c, pos, head);
+                const size_t off = (((size_t)b * S + pos) * Hq + head) * kHeadDim + 8 * st_unit;
+                rq[j] = ld16(p.q + off);
+                ro[j] = ld16(p.dout + off);
+            }
+        }
+        if (tid < kColsPerStep) {
+            const int c = c0 + tid;
+            rld = make_float2(INFINITY, 0.0f);
+            rpos = 0x3fffffff;
+            if (c < n_cols) {
+                int pos, head;
+                col_addr(c, pos, head);
+                rld = p.ld[((size_t)b * S + pos) * Hq + head];
+                rpos = pos;
+            }
+        }
+    };
+    auto store_step = [&](int buf) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int row = st_row + 32 * j;
+            sQ[buf][tile_unit(row, st_unit)] = rq[j];
+            sO[buf][tile_unit(row, st_unit)] = ro[j];
+        }
+        if (tid < kColsPerStep) {
+            sLD[buf][tid] = rld;
+            sPos[buf][tid] = rpos;
+        }
+    };
+
+    if (n_steps > 0) {
+        load_step(0);
+        store_step(0);
+    }
+    __syncthreads();
+
+    for (int st = 0; st < n_steps; ++st) {
+        const int buf = st & 1;
+        const bool has_next = st + 1 < n_steps;
+        if (has_next) load_step(st + 1);
+
+        // positions of this step's columns
+        const int c0 = st * kColsPerStep;
+        const int tp_min = pos_lo + c0 / G;
+        const int tp_max = min(pos_lo + (min(c0 + kColsPerStep, n_cols) - 1) / G, S - 1);
+        const bool skip = !wave_active || tp_max < kw0 || (W > 0 && tp_min - kw1 >= W);
+        if (!skip) {
+            const bool need_mask = !(tp_min >= kw1 && (W == 0 || tp_max - kw0 < W));
+            const uint4* tq = sQ[buf];
+            const uint4* to = sO[buf];
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb) {
+                // S = Q K^T and dP = dO V^T for columns 32 mb .. 32 mb + 31
+                f32x16 sacc, dpacc;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) sacc[r] = dpacc[r] = 0.0f;
+                const int arow = 32 * mb + perm_row(l32);
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks) {
+                    const bf16x8 qa = as_bf16x8(tq[tile_unit(arow, 2 * ks + g)]);
+                    const bf16x8 oa = as_bf16x8(to[tile_unit(arow, 2 * ks + g)]);
+                    sacc = mfma32(qa, kb[ks], sacc);
+                    dpacc = mfma32(oa, vb[ks], dpacc);
+                }
+                // P = exp2(s c - lse2), dS = P (dP - Dvec); register 8h + s holds
+                // column 32 mb + 16 h + 8 g + s
+                bf16x8 pb[2], dsb[2];
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    bf16x8 pv, dv8;
+#pragma unroll
+                    for (int s = 0; s < 8; ++s) {
+                        const int col = 32 * mb + 16 * h + 8 * g + s;
+                        const float2 ldv = sLD[buf][col];
+                        float pr = fast_exp2(fmaf(sacc[8 * h + s], p.c, -ldv.x));
+                        if (need_mask) {
+                            const int pos = sPos[buf][col];
+                            const bool vis = my_key <= pos && (W == 0 || pos - my_key < W);
+                            pr = vis ? pr : 0.0f;
+                        }
+                        pv[s] = (__bf16)pr;
+                        dv8[s] = (__bf16)(pr * (dpacc[8 * h + s] - ldv.y));
+                    }
+                    pb[h] = pv;
+                    dsb[h] = dv8;
+                }
+                // dV^T += dO^T P and dK^T += Q^T dS  (contract over the 32 columns)
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int r0 = 32 * mb + 16 * h + 8 * g;
+#pragma unroll
+                    for (int db = 0; db < 2; ++db) {
+                        const int cbase = 32 * db + 16 * (l32 >> 4);
+                        const bf16x8 oT = tile_read_tr8(to, r0, cbase, i16);
+                        const bf16x8 qT = tile_read_tr8(tq, r0, cbase, i16);
+                        dvacc[db] = mfma32(oT, pb[h], dvacc[db]);
+                        dkacc[db] = mfma32(qT, dsb[h], dkacc[db]);
+                    }
+                }
+            }
+        }
+
+        if (has_next) store_step(buf ^ 1);
+        __syncthreads();
+    }
+
+    // epilogue: lane = key, registers = d rows (acc_row); 4 contiguous d per store
+    if (my_key < S) {
+        const size_t off = ((size_t)b * S + my_key) * kv_stride + (size_t)kvh * kHeadDim;
+#pragma unroll
+        for (int db = 0; db < 2; ++db)
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+                const int d0 = 32 * db + 8 * r4 + 4 * g;
+                uint2 wk, wv;
+                wk.x = pack_bf16x2(dkacc[db][4 * r4 + 0] * p.scale, dkacc[db][4 * r4 + 1] * p.scale);
+                wk.y = pack_bf16x2(dkacc[db][4 * r4 + 2] * p.scale, dkacc[db][4 * r4 + 3] * p.scale);
+                wv.x = pack_bf16x2(dvacc[db][4 * r4 + 0], dvacc[db][4 * r4 + 1]);
+                wv.y = pack_bf16x2(dvacc[db][4 * r4 + 2], dvacc[db][4 * r4 + 3]);
+                *reinterpret_cast<uint2*>(p.dk + off + d0) = wk;
+                *reinterpret_cast<uint2*>(p.dv + off + d0) = wv;
+            }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// dq: query-outer; 4 waves x 32 columns per workgroup, 64-key tiles.
+constexpr int kDqCols = 128;
+constexpr int kBk = 64;
+
+__device__ __forceinline__ void dq_coords(const BwdParams& p, int n_qt, int bid, int& grp, int& qt) {
+    const int n_groups = p.B * p.Hkv;
+    if ((n_groups & 7) == 0) {
+        const int xcd = bid & 7, slot = bid >> 3;
+        grp = xcd * (n_groups >> 3) + slot / n_qt;
+        qt = slot % n_qt;
+    } else {
+        grp = bid % n_groups;
+        qt = bid / n_groups;
+    }
+    qt = n_qt - 1 - qt;  // latest positions (most keys) first
+}
+
+__global__ void __launch_bounds__(kThreads, 2)
+bwd_dq_kernel(BwdParams p, int n_qt, int pos_per_block) {
+    __shared__ uint4 sK[2][512];
+    __shared__ uint4 sV[2][512];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int g = lane >> 5, l32 = lane & 31, i16 = lane & 15;
+    int grp, qt;
+    dq_coords(p, n_qt, blockIdx.x, grp, qt);
+    const int b = grp / p.Hkv, kvh = grp % p.Hkv;
+    const int S = p.S, W = p.window, G = p.G, Hq = p.Hq;
+    const int p0 = qt * pos_per_block;
+    const int used_cols = pos_per_block * G;
+    const int P1 = min(p0 + pos_per_block, S) - 1;
+
+    const int cw = wave * 32 + l32;
+    const int col_pos = p0 + cw / G;
+    const int col_head = kvh * G + cw % G;
+    const bool col_ok = cw < used_cols && col_pos < S;
+    const int wc0 = wave * 32;
+    const bool wave_active = wc0 < used_cols && p0 + wc0 / G < S;
+    const int wpmin = p0 + wc0 / G;
+    const int wpmax = min(p0 + min(wc0 + 31, used_cols - 1) / G, S - 1);
+
+    bf16x8 qf[4], of[4];
+    float lse2 = INFINITY, dvec = 0.0f, rsum = 0.0f;
+    {
+        const size_t off = (((size_t)b * S + col_pos) * Hq + col_head) * kHeadDim;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            uint4 x = make_uint4(0, 0, 0, 0), y = make_uint4(0, 0, 0, 0);
+            if (col_ok) {
+                x = ld16(p.q + off + 16 * ks + 8 * g);
+                y = ld16(p.dout + off + 16 * ks + 8 * g);
+            }
+            qf[ks] = as_bf16x8(x);
+            of[ks] = as_bf16x8(y);
+        }
+        if (col_ok) {
+            const float2 v = p.ld[((size_t)b * S + col_pos) * Hq + col_head];
+            lse2 = v.x;
+            dvec = v.y;
+        }
+    }
+
+    f32x16 dqacc[2];
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dqacc[db][r] = 0.0f;
+
+    const int key_lo = W > 0 ? max(0, p0 - W + 1) : 0;
+    const int t_begin = key_lo / kBk;
+    const int t_end = P1 / kBk;
+
+    const size_t kv_stride = (size_t)p.Hkv * kHeadDim;
+    const uint16_t* kbase = p.k + ((size_t)b * S * p.Hkv + kvh) * kHeadDim;
+    const uint16_t* vbase = p.v + ((size_t)b * S * p.Hkv + kvh) * kHeadDim;
+    const int st_row = tid >> 3, st_unit = tid & 7;
+    uint4 rk[2], rv[2];
+    auto load_tile = [&](int t) {
+        const int kt0 = t * kBk;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int key = kt0 + st_row + 32 * j;
+            rk[j] = make_uint4(0, 0, 0, 0);
+            rv[j] = make_uint4(0, 0, 0, 0);
+            if (key < S) {
+                rk[j] = ld16(kbase + key * kv_stride + 8 * st_unit);
+                rv[j] = ld16(vbase + key * kv_stride + 8 * st_unit);
+            }
+        }
+    };
+    auto store_tile = [&](int buf) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int row = st_row + 32 * j;
+            sK[buf][tile_unit(row, st_unit)] = rk[j];
+            sV[buf][tile_unit(row, st_unit)] = rv[j];
+        }
+    };
+
+    if (t_begin <= t_end) {
+        load_tile(t_begin);
+        store_tile(0);
+    }
+    __syncthreads();
+
+    for (int t = t_begin; t <= t_end; ++t) {
+        const int buf = (t - t_begin) & 1;
+        const bool has_next = t < t_end;
+        if (has_next) load_tile(t + 1);
+        const int kt0 = t * kBk;
+        const bool skip = !wave_active || kt0 > wpmax || (W > 0 && wpmin - (kt0 + kBk - 1) >= W);
+        if (!skip) {
+            const bool need_mask = !(kt0 + kBk - 1 <= wpmin && (W == 0 || wpmax - kt0 < W));
+            const uint4* tk = sK[buf];
+            const uint4* tv = sV[buf];
+            bf16x8 dsb[4];
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb) {
+                f32x16 sacc, dpacc;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) sacc[r] = dpacc[r] = 0.0f;
+                const int arow = 32 * mb + perm_row(l32);
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks) {
+                    sacc = mfma32(as_bf16x8(tk[tile_unit(arow, 2 * ks + g)]), qf[ks], sacc);
+                    dpacc = mfma32(as_bf16x8(tv[tile_unit(arow, 2 * ks + g)]), of[ks], dpacc);
+                }
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    bf16x8 d8;
+#pragma unroll
+                    for (int s = 0; s < 8; ++s) {
+                        float pr = fast_exp2(fmaf(sacc[8 * h + s], p.c, -lse2));
+                        if (need_mask) {
+                            const int key = kt0 + 32 * mb + 16 * h + 8 * g + s;
+                            const bool vis = key <= col_pos && (W == 0 || col_pos - key < W);
+                            pr = vis ? pr : 0.0f;
+                        }
+                        rsum = fmaf(pr, dpacc[8 * h + s], rsum);
+                        d8[s] = (__bf16)(pr * (dpacc[8 * h + s] - dvec));
+                    }
+                    dsb[2 * mb + h] = d8;
+                }
+            }
+            // dQ^T += K^T dS^T over the 64 keys (16 per step)
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+#pragma unroll
+                for (int db = 0; db < 2; ++db) {
+                    const bf16x8 kT = tile_read_tr8(tk, 16 * kk + 8 * g, 32 * db + 16 * (l32 >> 4), i16);
+                    dqacc[db] = mfma32(kT, dsb[kk], dqacc[db]);
+                }
+            }
+        }
+        if (has_next) store_tile(buf ^ 1);
+        __syncthreads();
+    }
+
+    rsum = sum_across_halves(rsum);
+    if (col_ok) {
+        if (g == 0) {
+            // this row's dsink term; the row's own Q/dO/lse were read above
+            const float s2 = p.sinks[col_head] * kLog2e;
+            p.ld[((size_t)b * S + col_pos) * Hq + col_head].x = fast_exp2(s2 - lse2) * rsum;
+        }
+        uint16_t* row = p.dq + (((size_t)b * S + col_pos) * Hq + col_head) * kHeadDim;
+#pragma unroll
+        for (int db = 0; db < 2; ++db)
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+                const int d0 = 32 * db + 8 * r4 + 4 * g;
+                uint2 w;
+                w.x = pack_bf16x2(dqacc[db][4 * r4 + 0] * p.scale, dqacc[db][4 * r4 + 1] * p.scale);
+                w.y = pack_bf16x2(dqacc[db][4 * r4 + 2] * p.scale, dqacc[db][4 * r4 + 3] * p.scale);
+                *reinterpret_cast<uint2*>(row + d0) = w;
+            }
+    }
+}
+
+}  // namespace
+
+size_t bwd_workspace_bytes(int B, int S, int Hq, int Hkv, int window) {
+    (void)Hkv;
+    (void)window;
+    return (size_t)B * S * Hq * sizeof(float2);
+}
+
+hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
+    BwdParams p;
+    p.q = a.q;
+    p.k = a.k;
+    p.v = a.v;
+    p.out = a.out;
+    p.dout = a.dout;
+    p.lse = a.lse;
+    p.sinks = a.sinks;
+    p.dq = a.dq;
+    p.dk = a.dk;
+    p.dv = a.dv;
+    p.dsinks = a.dsinks;
+    p.ld = static_cast<float2*>(a.workspace);
+    p.B = a.B;
+    p.S = a.S;
+    p.Hq = a.Hq;
+    p.Hkv = a.Hkv;
+    p.G = a.Hq / a.Hkv;
+    p.window = a.window >= a.S ? 0 : a.window;
+    p.scale = a.scale;
+    p.c = a.scale * kLog2e;
+
+    const long long rows = (long long)a.B * a.S * a.Hq;
+    hipLaunchKernelGGL(bwd_pre_kernel, dim3((unsigned)((rows + 31) / 32)), dim3(kThreads), 0, stream, p, rows);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int n_kt = (a.S + kKeysPerBlock - 1) / kKeysPerBlock;
+    hipLaunchKernelGGL(bwd_dkdv_kernel, dim3((unsigned)(n_kt * a.B * a.Hkv)), dim3(kThreads), 0, stream, p, n_kt);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const int ppb = kDqCols / p.G >= 1 ? kDqCols / p.G : 1;
+    const int n_qt = (a.S + ppb - 1) / ppb;
+    hipLaunchKernelGGL(bwd_dq_kernel, dim3((unsigned)(n_qt * a.B * a.Hkv)), dim3(kThreads), 0, stream, p, n_qt, ppb);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(bwd_dsink_kernel, dim3(a.Hq), dim3(kThreads), 0, stream, p);
+    return hipGetLastError();
+}
+
+}  // namespace gptoss

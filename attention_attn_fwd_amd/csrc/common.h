@@ -1,0 +1,115 @@
+// Device helpers shared by the gfx950 sink-attention kernels.
+//
+// MFMA lane layouts used throughout (v_mfma_f32_32x32x16_bf16, wave64):
+//   A operand (32 x 16, M x K): lane l supplies row m = l % 32 and the eight
+//     K elements of slot group g = l / 32.
+//   B operand (16 x 32, K x N): lane l supplies column n = l % 32 and the
+//     eight K elements of slot group g = l / 32.
+//   C/D (32 x 32): lane l holds column n = l % 32; accumulator register r
+//     (0..15) holds row m = 8 * (r / 4) + 4 * g + (r % 4).
+// A and B assign K elements to (slot group, slot) the same way, so a kernel
+// may use any fixed map between its logical contraction index and
+// (g, slot) as long as both operands use it.  Only the C/D row map is relied
+// on as stated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gptoss {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr int kHeadDim = 64;
+
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// 16-byte global load / store through uint4 (8 bf16).
+__device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+__device__ __forceinline__ void st16(void* p, uint4 v) { *reinterpret_cast<uint4*>(p) = v; }
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// Round-to-nearest-even fp32 -> bf16 pairs (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    bf16x2 r;
+    r[0] = (__bf16)lo;
+    r[1] = (__bf16)hi;
+    return __builtin_bit_cast(uint32_t, r);
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Value held by the lane 32 positions away (l ^ 32), via v_permlane32_swap.
+// Returns (own, partner) combined by the caller through a symmetric op.
+struct Pair { float a, b; };
+__device__ __forceinline__ Pair swap32(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false, false);
+    return Pair{__int_as_float(r[0]), __int_as_float(r[1])};
+}
+__device__ __forceinline__ float max_across_halves(float x) {
+    Pair p = swap32(x);
+    return fmaxf(p.a, p.b);
+}
+__device__ __forceinline__ float sum_across_halves(float x) {
+    Pair p = swap32(x);
+    return p.a + p.b;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// Row of the 32x32 accumulator held in register r by slot group g.
+__device__ __forceinline__ constexpr int acc_row(int r, int g) { return 8 * (r >> 2) + 4 * g + (r & 3); }
+
+// Swap bits 2 and 3 of a 0..31 row index (an involution).  An A operand whose
+// lane m supplies row perm_row(m) leaves, in accumulator registers 8h..8h+7
+// of slot group g, the 8 consecutive rows 16h + 8g + 0..7 -- exactly the
+// K-slot order of a following MFMA that contracts over those rows.
+__device__ __forceinline__ int perm_row(int m) { return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1); }
+
+// LDS tiles of 64 rows x 64 bf16 are stored as 8 sixteen-byte units per row
+// with the unit index XOR-swizzled by the row, so that the 8 rows read by
+// one ds_read_b128 phase (rows perm_row(0..7)) and the 4 consecutive rows of
+// a transposing read fall into different bank groups.
+__device__ __forceinline__ int kswz(int row) { return (row & 3) | ((row >> 1) & 4); }
+__device__ __forceinline__ int tile_unit(int row, int unit) { return row * 8 + (unit ^ kswz(row)); }
+
+// ds_read_b64_tr_b16: within each 16-lane block, lane i receives element
+// (i % 4) of the 8-byte chunk addressed by block lane 4 j + i / 4, for
+// j = 0..3.  If block lane s addresses tile[r0 + s / 4][c0 + 4 (s % 4)], lane
+// i receives tile[r0 + j][c0 + i] for j = 0..3: a 4 x 16 transpose.
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint2 lds_read_tr16(const void* lds_ptr) {
+    typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+    const i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(lds_ptr));
+    return __builtin_bit_cast(uint2, r);
+}
+
+// Transposed 8-slot operand from a swizzled row-major tile: lane (block
+// position i = lane % 16) receives tile[r0 + 0..7][c0 + i] where c0 is the
+// first column of its 16-lane block.  Rows r0..r0+3 come from the first
+// read, r0+4..r0+7 from the second.
+__device__ __forceinline__ bf16x8 tile_read_tr8(const uint4* tile, int r0, int c0, int i) {
+    const int row_a = r0 + (i >> 2), row_b = row_a + 4;
+    const int col = c0 + 4 * (i & 3);
+    const char* base = reinterpret_cast<const char*>(tile);
+    const uint2 lo = lds_read_tr16(base + tile_unit(row_a, col >> 3) * 16 + ((col >> 2) & 1) * 8);
+    const uint2 hi = lds_read_tr16(base + tile_unit(row_b, col >> 3) * 16 + ((col >> 2) & 1) * 8);
+    return __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+}
+
+}  // namespace gptoss

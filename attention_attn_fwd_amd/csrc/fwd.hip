@@ -1,0 +1,359 @@
+// Prefill forward of causal / sliding-window grouped-query attention with a
+// per-head sink logit (gfx950).
+//
+// Method (Megatron-LM issue "gpt-oss implementation": "Attention Sinks",
+// "Alternating Sliding-Window Attention Pattern"; HF blog "Tricks from OpenAI
+// gpt-oss YOU can use with transformers": one fused kernel keeps the scores
+// on chip; Flash Attention 3 with sinks): for each query row the softmax runs
+// over the visible keys plus one sink logit that has no value vector.  The
+// running max starts at the sink (in log2 units) and the running denominator
+// at exp(0) = 1, so the sink enters exactly once and no score matrix ever
+// reaches HBM.
+//
+// Work decomposition
+//   One workgroup = 4 waves = 256 "columns".  A column is one (query position,
+//   query head) pair; the G = Hq / Hkv heads of one KV head are packed next to
+//   each other, so every K/V tile staged in LDS serves all G heads (GQA
+//   sharing) and the workgroup covers floor(256 / G) positions.
+//   Each wave owns 64 columns (two 32-column MFMA N-blocks).
+//   Key tiles of 64 rows are staged HBM -> LDS with 16-byte coalesced loads,
+//   double buffered: K row-major, V transposed (d-major) so that the P.V
+//   contraction over keys reads 8 consecutive keys per lane.
+//   Only tiles that intersect the causal/window band are visited; inside a
+//   wave, tiles fully outside its rows' band are skipped and tiles fully
+//   inside it skip the mask.
+//
+// Per key tile and wave (scores transposed, S^T = K Q^T, so that each lane
+// holds one column's scores and the row reductions are in-lane):
+//   S^T  : 2 (key blocks) x 2 (column blocks) x 4 (d steps) 32x32x16 bf16 MFMAs
+//   mask, row max (in-lane + one permlane32 swap), lazy rescale of the output
+//   accumulator (only when some row max grew), p = exp2(s * c - m) with
+//   c = scale * log2(e), row sums kept per lane-half until the epilogue
+//   O^T += V^T P^T : 2 (d blocks) x 2 (column blocks) x 4 (key steps) MFMAs;
+//   the fp32 score accumulator converts in-register into the bf16 B operand.
+// The key rows fed to the S^T MFMA are permuted (bits 2 and 3 of the row
+// index swapped) so that accumulator registers 8h..8h+7 of lane half g hold
+// the 8 consecutive keys 16 * (2 * block + h) + 8 g + 0..7 that the P.V MFMA
+// expects in its B-operand slots.
+#include "common.h"
+#include "launch.h"
+
+namespace gptoss {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kCols = 256;        // columns per workgroup
+constexpr int kBk = 64;           // keys per LDS tile
+constexpr int kTileUnits = 512;   // 16-byte units per 64 x 64 bf16 tile
+
+struct FwdParams {
+    const uint16_t* q;
+    const uint16_t* k;
+    const uint16_t* v;
+    const float* sinks;
+    uint16_t* out;
+    float* lse;
+    int S, Hq, Hkv, G, window;
+    int pos_per_block;  // positions per workgroup = floor(256 / G)
+    int n_qtiles;       // ceil(S / pos_per_block)
+    int n_groups;       // B * Hkv
+    float c;            // softmax scale * log2(e)
+};
+
+
+// V^T tile rows are indexed by d; the 8 lanes of a ds_read_b128 phase read
+// d rows 8 apart, so the unit swizzle is d & 7.
+__device__ __forceinline__ int vswz(int d) { return d & 7; }
+
+// Workgroup -> (KV group, query tile).  Workgroups are dispatched round-robin
+// over the 8 XCDs, so when the groups split evenly each XCD walks its own
+// groups and their K/V stay in that XCD's L2.  Query tiles run heaviest
+// (latest positions, most keys) first.
+__device__ __forceinline__ void block_coords(const FwdParams& p, int bid, int& grp, int& qt) {
+    const int nq = p.n_qtiles;
+    if ((p.n_groups & 7) == 0) {
+        const int xcd = bid & 7, slot = bid >> 3;
+        grp = xcd * (p.n_groups >> 3) + slot / nq;
+        qt = slot % nq;
+    } else {
+        grp = bid % p.n_groups;
+        qt = bid / p.n_groups;
+    }
+    qt = nq - 1 - qt;
+}
+
+__global__ void __launch_bounds__(kThreads, 2)
+fwd_kernel(FwdParams p) {
+    __shared__ uint4 smem[2][2][kTileUnits];  // [buffer][K | V^T][unit]
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int g = lane >> 5;     // slot group / lane half
+    const int l32 = lane & 31;
+
+    int grp, qt;
+    block_coords(p, blockIdx.x, grp, qt);
+    const int b = grp / p.Hkv;
+    const int kvh = grp % p.Hkv;
+    const int G = p.G;
+    const int S = p.S;
+    const int W = p.window;
+    const int p0 = qt * p.pos_per_block;
+    const int used_cols = p.pos_per_block * G;
+    const int P1 = min(p0 + p.pos_per_block, S) - 1;
+
+    // ---- this lane's two columns (one per N-block)
+    int col_pos[2], col_head[2];
+    bool col_ok[2];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+        const int cw = wave * 64 + nb * 32 + l32;
+        col_pos[nb] = p0 + cw / G;
+        col_head[nb] = kvh * G + cw % G;
+        col_ok[nb] = cw < used_cols && col_pos[nb] < S;
+    }
+    // positions covered by this wave (for tile classification)
+    const int wc0 = wave * 64;
+    const bool wave_active = wc0 < used_cols && p0 + wc0 / G < S;
+    const int wpmin = p0 + wc0 / G;
+    const int wpmax = min(p0 + (min(wc0 + 63, used_cols - 1)) / G, S - 1);
+
+    // ---- Q fragments (B operand of S^T = K Q^T): column n, d = 16ks + 8g + 0..7
+    bf16x8 qf[2][4];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+        const uint16_t* qrow = p.q + ((size_t)(b * S + col_pos[nb]) * p.Hq + col_head[nb]) * kHeadDim;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            uint4 x = make_uint4(0, 0, 0, 0);
+            if (col_ok[nb]) x = ld16(qrow + 16 * ks + 8 * g);
+            qf[nb][ks] = as_bf16x8(x);
+        }
+    }
+
+    // ---- softmax state, seeded by the sink: m = sink * log2(e), l = 1
+    float m_run[2], l_run[2];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+        const float sink = col_ok[nb] ? p.sinks[col_head[nb]] : -INFINITY;
+        const bool has_sink = sink != -INFINITY;
+        m_run[nb] = has_sink ? sink * kLog2e : -INFINITY;
+        l_run[nb] = (has_sink && g == 0) ? 1.0f : 0.0f;
+    }
+    f32x16 oacc[2][2];
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) oacc[db][nb][r] = 0.0f;
+
+    // ---- key tile range of the workgroup
+    const int key_lo = W > 0 ? max(0, p0 - W + 1) : 0;
+    const int t_begin = key_lo / kBk;
+    const int t_end = P1 / kBk;  // inclusive
+
+    // global -> register staging of one K/V tile
+    const size_t kv_row_stride = (size_t)p.Hkv * kHeadDim;
+    const uint16_t* kbase = p.k + ((size_t)b * S * p.Hkv + kvh) * kHeadDim;
+    const uint16_t* vbase = p.v + ((size_t)b * S * p.Hkv + kvh) * kHeadDim;
+    const int k_key0 = tid >> 3, k_unit = tid & 7;  // K: rows k_key0, k_key0 + 32
+    const int v_kp = tid & 31, v_dc = tid >> 5;      // V: rows 2kp, 2kp+1; d chunk
+    uint4 kreg[2], vreg[2];
+
+    auto load_tile = [&](int t) {
+        const int kt0 = t * kBk;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int key = kt0 + k_key0 + 32 * j;
+            kreg[j] = key < S ? ld16(kbase + key * kv_row_stride + 8 * k_unit) : make_uint4(0, 0, 0, 0);
+            const int vkey = kt0 + 2 * v_kp + j;
+            vreg[j] = vkey < S ? ld16(vbase + vkey * kv_row_stride + 8 * v_dc) : make_uint4(0, 0, 0, 0);
+        }
+    };
+    auto store_tile = [&](int buf) {
+        uint4* ks = smem[buf][0];
+        uint32_t* vs = reinterpret_cast<uint32_t*>(smem[buf][1]);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int key = k_key0 + 32 * j;
+            ks[key * 8 + (k_unit ^ kswz(key))] = kreg[j];
+        }
+        const uint32_t a[4] = {vreg[0].x, vreg[0].y, vreg[0].z, vreg[0].w};
+        const uint32_t c[4] = {vreg[1].x, vreg[1].y, vreg[1].z, vreg[1].w};
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+            const int d = 8 * v_dc + s;
+            const uint32_t lo = (s & 1) ? (a[s >> 1] >> 16) : (a[s >> 1] & 0xffffu);
+            const uint32_t hi = (s & 1) ? (c[s >> 1] & 0xffff0000u) : (c[s >> 1] << 16);
+            vs[(d * 8 + ((v_kp >> 2) ^ vswz(d))) * 4 + (v_kp & 3)] = lo | hi;
+        }
+    };
+
+    if (t_begin <= t_end) {
+        load_tile(t_begin);
+        store_tile(0);
+    }
+    __syncthreads();
+
+    for (int t = t_begin; t <= t_end; ++t) {
+        const int buf = (t - t_begin) & 1;
+        const bool has_next = t < t_end;
+        if (has_next) load_tile(t + 1);
+
+        const int kt0 = t * kBk;
+        const bool skip = !wave_active || kt0 > wpmax || (W > 0 && wpmin - (kt0 + kBk - 1) >= W);
+        if (!skip) {
+            const bool need_mask = !(kt0 + kBk - 1 <= wpmin && (W == 0 || wpmax - kt0 < W));
+            const uint4* ks = smem[buf][0];
+            const uint4* vs = smem[buf][1];
+
+            // S^T = K Q^T
+            f32x16 sacc[2][2];
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+                for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) sacc[mb][nb][r] = 0.0f;
+#pragma unroll
+            for (int ks_ = 0; ks_ < 4; ++ks_) {
+#pragma unroll
+                for (int mb = 0; mb < 2; ++mb) {
+                    const int key = 32 * mb + perm_row(l32);
+                    const bf16x8 a = as_bf16x8(ks[key * 8 + ((2 * ks_ + g) ^ kswz(key))]);
+#pragma unroll
+                    for (int nb = 0; nb < 2; ++nb) sacc[mb][nb] = mfma32(a, qf[nb][ks_], sacc[mb][nb]);
+                }
+            }
+
+            if (need_mask) {
+#pragma unroll
+                for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int key = kt0 + 32 * mb + perm_row(acc_row(r, g));
+#pragma unroll
+                        for (int nb = 0; nb < 2; ++nb) {
+                            const int pos = col_pos[nb];
+                            const bool vis = key <= pos && (W == 0 || pos - key < W);
+                            sacc[mb][nb][r] = vis ? sacc[mb][nb][r] : -INFINITY;
+                        }
+                    }
+            }
+
+            // online softmax (log2 domain), one column per lane-pair
+            float m_use[2];
+            bool grow = false;
+            float m_new[2];
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb) {
+                float mx = -INFINITY;
+#pragma unroll
+                for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[mb][nb][r]);
+                mx = max_across_halves(mx);
+                m_new[nb] = fmaxf(m_run[nb], mx * p.c);
+                grow |= m_new[nb] > m_run[nb];
+            }
+            if (__any(grow)) {
+#pragma unroll
+                for (int nb = 0; nb < 2; ++nb) {
+                    const float alpha = m_new[nb] > m_run[nb] ? fast_exp2(m_run[nb] - m_new[nb]) : 1.0f;
+                    l_run[nb] *= alpha;
+#pragma unroll
+                    for (int db = 0; db < 2; ++db)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) oacc[db][nb][r] *= alpha;
+                    m_run[nb] = m_new[nb];
+                }
+            }
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb) m_use[nb] = m_run[nb] == -INFINITY ? 0.0f : m_run[nb];
+
+            bf16x8 pb[4][2];
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb) {
+                float lsum = 0.0f;
+#pragma unroll
+                for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        bf16x8 v8;
+#pragma unroll
+                        for (int s = 0; s < 8; ++s) {
+                            const float e = fast_exp2(fmaf(sacc[mb][nb][8 * h + s], p.c, -m_use[nb]));
+                            lsum += e;
+                            v8[s] = (__bf16)e;
+                        }
+                        pb[2 * mb + h][nb] = v8;
+                    }
+                l_run[nb] += lsum;
+            }
+
+            // O^T += V^T P^T
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+#pragma unroll
+                for (int db = 0; db < 2; ++db) {
+                    const int d = 32 * db + l32;
+                    const bf16x8 a = as_bf16x8(vs[d * 8 + ((2 * kk + g) ^ vswz(d))]);
+#pragma unroll
+                    for (int nb = 0; nb < 2; ++nb) oacc[db][nb] = mfma32(a, pb[kk][nb], oacc[db][nb]);
+                }
+            }
+        }
+
+        if (has_next) store_tile(buf ^ 1);
+        __syncthreads();
+    }
+
+    // ---- epilogue: O = acc / l (bf16, RNE); lse = ln2 * (m + log2 l)
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+        const float l_tot = sum_across_halves(l_run[nb]);
+        if (!col_ok[nb]) continue;
+        const float inv = 1.0f / l_tot;
+        uint16_t* orow = p.out + ((size_t)(b * S + col_pos[nb]) * p.Hq + col_head[nb]) * kHeadDim;
+#pragma unroll
+        for (int db = 0; db < 2; ++db)
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+                const int d0 = 32 * db + 8 * r4 + 4 * g;
+                uint2 w;
+                w.x = pack_bf16x2(oacc[db][nb][4 * r4 + 0] * inv, oacc[db][nb][4 * r4 + 1] * inv);
+                w.y = pack_bf16x2(oacc[db][nb][4 * r4 + 2] * inv, oacc[db][nb][4 * r4 + 3] * inv);
+                *reinterpret_cast<uint2*>(orow + d0) = w;
+            }
+        if (g == 0)
+            p.lse[((size_t)b * p.Hq + col_head[nb]) * S + col_pos[nb]] = (m_run[nb] + fast_log2(l_tot)) * kLn2;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {
+    FwdParams p;
+    p.q = a.q;
+    p.k = a.k;
+    p.v = a.v;
+    p.sinks = a.sinks;
+    p.out = a.out;
+    p.lse = a.lse;
+    p.S = a.S;
+    p.Hq = a.Hq;
+    p.Hkv = a.Hkv;
+    p.G = a.Hq / a.Hkv;
+    p.window = a.window >= a.S ? 0 : a.window;
+    p.pos_per_block = kCols / p.G;
+    p.n_qtiles = (a.S + p.pos_per_block - 1) / p.pos_per_block;
+    p.n_groups = a.B * a.Hkv;
+    p.c = a.scale * kLog2e;
+    const long long blocks = (long long)p.n_groups * p.n_qtiles;
+    hipLaunchKernelGGL(fwd_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream, p);
+    return hipGetLastError();
+}
+
+}  // namespace gptoss

@@ -1,0 +1,60 @@
+// Internal launch interface between the C ABI (api.cpp) and the kernels.
+// Arguments are validated by the caller; launchers only plan grids and launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace gptoss {
+
+struct FwdArgs {
+    const uint16_t* q;
+    const uint16_t* k;
+    const uint16_t* v;
+    const float* sinks;
+    uint16_t* out;
+    float* lse;
+    int B, S, Hq, Hkv, window;
+    float scale;
+};
+
+struct BwdArgs {
+    const uint16_t* q;
+    const uint16_t* k;
+    const uint16_t* v;
+    const float* sinks;
+    const uint16_t* out;
+    const float* lse;
+    const uint16_t* dout;
+    uint16_t* dq;
+    uint16_t* dk;
+    uint16_t* dv;
+    float* dsinks;
+    void* workspace;
+    int B, S, Hq, Hkv, window;
+    float scale;
+};
+
+struct DecodeArgs {
+    const uint16_t* q;
+    const uint16_t* k_cache;
+    const uint16_t* v_cache;
+    const int* cu_seqlens;
+    const float* sinks;
+    uint16_t* out;
+    float* lse;
+    void* workspace;
+    int N, Hq, Hkv, max_seqlen, window;
+    float scale;
+};
+
+hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
+
+size_t bwd_workspace_bytes(int B, int S, int Hq, int Hkv, int window);
+hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream);
+
+size_t decode_workspace_bytes(int N, int Hq, int Hkv, int max_seqlen, int window);
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+
+}  // namespace gptoss

@@ -1,0 +1,141 @@
+/*
+ * gptoss_attn.h -- C ABI of the MI355X (gfx950) sink-attention library.
+ *
+ * The operation (cited pages: Megatron-LM issue "gpt-oss implementation",
+ * sections "Attention Sinks" and "Alternating Sliding-Window Attention
+ * Pattern"; HF blog "Tricks from OpenAI gpt-oss YOU can use with
+ * transformers", the Flash Attention 3 with attention sinks paragraph and the
+ * "Dynamic Sliding Window Layer & Cache" / "Continuous Batching & Paged
+ * Attention" items; tpu-inference PR "[GPT-OSS] JAX implementation of
+ * GPT-OSS", the kernel's attention_sink argument and the serve command):
+ *
+ *   causal grouped-query attention in which every query head h owns one
+ *   learned logit sinks[h] that joins the softmax denominator of each row and
+ *   has no value vector.  For batch b, query head h (kv head c = h / G,
+ *   G = Hq / Hkv) and query position i:
+ *
+ *     s_ij   = softmax_scale * dot(q[b,i,h,:], k[b,j,c,:])   visible j only
+ *     M_i    = max(sinks[h], max_j s_ij)
+ *     Z_i    = exp(sinks[h] - M_i) + sum_j exp(s_ij - M_i)
+ *     out[b,i,h,:] = sum_j exp(s_ij - M_i) / Z_i * v[b,j,c,:]
+ *     lse[b,h,i]   = M_i + ln Z_i          (natural log, sink included)
+ *
+ *   Key j is visible from query i when j <= i and, for window W >= 1, also
+ *   i - j < W (W keys including the query itself).  window = 0 is full causal;
+ *   a window >= S gives the same result as window = 0.  The sink is not
+ *   multiplied by softmax_scale; sinks[h] = -INFINITY removes it.
+ *
+ * Conventions for every entry point
+ *   - Tensors are dense, contiguous, row-major, in DEVICE memory of the current
+ *     HIP device, and 16-byte aligned.  bf16 is IEEE bfloat16 (stored as
+ *     uint16).  Layouts: q/out/dout/dq [B, S, Hq, D]; k/v/dk/dv [B, S, Hkv, D];
+ *     lse [B, Hq, S]; sinks/dsinks [Hq].
+ *   - head_dim D must be 64 and the group size Hq / Hkv at most 128
+ *     (GPTOSS_ERR_UNSUPPORTED otherwise).
+ *   - The caller owns every buffer (inputs, outputs, workspace).  The library
+ *     allocates no device memory and keeps no state between calls beyond a
+ *     per-device capability check and the per-thread error message.
+ *   - Calls enqueue work on `stream` (a hipStream_t; NULL = the null stream)
+ *     and return without synchronising.  Outputs are overwritten, never
+ *     accumulated into.  Calls on different streams must not share outputs or
+ *     workspace.
+ *   - Argument errors are detected on the host before any HIP call and
+ *     nothing is written.  A zero-sized problem (B == 0, S == 0 or N == 0)
+ *     returns GPTOSS_OK without touching memory.  Contents of device buffers
+ *     (NaN/Inf in inputs, cu_seqlens values) are caller contracts and are not
+ *     checked.
+ *   - gptoss_attn_last_error() returns the message of this thread's last
+ *     non-OK status.
+ */
+#ifndef GPTOSS_ATTN_H
+#define GPTOSS_ATTN_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GPTOSS_ATTN_ABI_VERSION 1
+
+typedef enum {
+    GPTOSS_OK = 0,
+    GPTOSS_ERR_INVALID_ARGUMENT = 1, /* bad pointer, size, alignment, workspace */
+    GPTOSS_ERR_UNSUPPORTED = 2,      /* head_dim != 64, device is not gfx950 */
+    GPTOSS_ERR_HIP = 3               /* a HIP runtime call or launch failed */
+} gptoss_status;
+
+/* ABI version of the loaded library (GPTOSS_ATTN_ABI_VERSION it was built with). */
+int gptoss_attn_abi_version(void);
+
+/* Message for this thread's last non-OK status ("" if none).  The pointer
+ * stays valid until the next library call on the same thread. */
+const char* gptoss_attn_last_error(void);
+
+/*
+ * Prefill forward.  Computes out and lse as defined above.
+ *   q      bf16 [B, S, Hq, D]          read
+ *   k, v   bf16 [B, S, Hkv, D]         read
+ *   sinks  fp32 [Hq]                   read
+ *   out    bf16 [B, S, Hq, D]          written (round-to-nearest-even)
+ *   lse    fp32 [B, Hq, S]             written
+ * Requires B, S >= 0, Hq >= 1, Hkv >= 1, Hq % Hkv == 0, window >= 0,
+ * softmax_scale finite and > 0.
+ */
+gptoss_status gptoss_attn_fwd(const void* q, const void* k, const void* v,
+                              const float* sinks, int B, int S, int Hq, int Hkv,
+                              int D, int window, float softmax_scale, void* out,
+                              float* lse, void* stream);
+
+/*
+ * Training backward of the forward above for the loss sum(dout * out):
+ *   dq = dL/dq, dk = dL/dk, dv = dL/dv (bf16, RNE), dsinks = dL/dsinks (fp32,
+ *   summed over batch and positions).  With Dvec_i = dot(dout_i, out_i):
+ *   dS_ij = P_ij (dot(dout_i, v_j) - Dvec_i) and
+ *   dsinks[h] = -sum_{b,i} exp(sinks[h] - lse[b,h,i]) * Dvec[b,h,i].
+ *   out and lse must be the forward's outputs for the same inputs.
+ *   q, k, v, out, dout bf16 (layouts as above); sinks fp32 [Hq];
+ *   lse fp32 [B, Hq, S]                          read
+ *   dq bf16 [B,S,Hq,D]; dk, dv bf16 [B,S,Hkv,D]; dsinks fp32 [Hq]   written
+ *   workspace  device scratch of at least gptoss_attn_bwd_workspace_size()
+ *              bytes, 256-byte aligned; its contents on entry do not matter.
+ */
+size_t gptoss_attn_bwd_workspace_size(int B, int S, int Hq, int Hkv, int D, int window);
+gptoss_status gptoss_attn_bwd(const void* q, const void* k, const void* v,
+                              const float* sinks, const void* out, const float* lse,
+                              const void* dout, int B, int S, int Hq, int Hkv, int D,
+                              int window, float softmax_scale, void* dq, void* dk,
+                              void* dv, float* dsinks, void* workspace,
+                              size_t workspace_bytes, void* stream);
+
+/*
+ * Decode: one new query token per sequence against a packed KV cache
+ * (split-KV partial softmax per chunk of keys, then an lse merge in which the
+ * sink enters exactly once).
+ *   q           bf16 [N, Hq, D]                 read
+ *   k_cache,
+ *   v_cache     bf16 [T, Hkv, D]                read; sequence n owns rows
+ *               cu_seqlens[n] .. cu_seqlens[n+1]-1 (L_n rows, the new token's
+ *               K/V last); its query sits at position L_n - 1.
+ *   cu_seqlens  int32 [N + 1], device, cu_seqlens[0] = 0, non-decreasing
+ *   max_seqlen  host-side upper bound of every L_n (>= 1); it sizes the split
+ *               grid without reading device memory.  L_n > max_seqlen is a
+ *               caller error whose keys beyond max_seqlen are ignored.
+ *   out         bf16 [N, Hq, D]   written;  lse fp32 [N, Hq] written.
+ *               An empty sequence (L_n = 0) gives out = 0, lse = sinks[h].
+ *   workspace   at least gptoss_attn_decode_workspace_size() bytes,
+ *               256-byte aligned (split partials); contents on entry ignored.
+ */
+size_t gptoss_attn_decode_workspace_size(int N, int Hq, int Hkv, int D, int max_seqlen,
+                                         int window);
+gptoss_status gptoss_attn_decode(const void* q, const void* k_cache, const void* v_cache,
+                                 const int* cu_seqlens, const float* sinks, int N, int Hq,
+                                 int Hkv, int D, int max_seqlen, int window,
+                                 float softmax_scale, void* out, float* lse,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GPTOSS_ATTN_H */

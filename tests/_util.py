@@ -1,0 +1,45 @@
+"""Shared helpers of the test suite (comparison bars, device plumbing)."""
+
+import numpy as np
+import pytest
+import torch
+
+# Numeric bars for the HIP path against the fp64 oracle.
+OUT_MAX_ABS = 1e-2
+OUT_MEAN_ABS = 1e-3
+LSE_MAX_ABS = 1e-3
+GRAD_REL_L2 = 1e-2
+
+
+def need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no HIP device")
+    return torch.device("cuda:0")
+
+
+def f64(t):
+    """Exact upcast of a (CPU or GPU) tensor to a float64 numpy array."""
+    return t.detach().to("cpu", torch.float64).numpy()
+
+
+def check_out_lse(out, lse, ref_out, ref_lse, what=""):
+    """out/ref_out [..., D] and lse/ref_lse arrays; NaN entries of the
+    reference (rows the oracle did not compute) are ignored."""
+    out, lse = np.asarray(out), np.asarray(lse)
+    sel = ~np.isnan(ref_lse)
+    assert sel.any(), "nothing to compare"
+    osel = ~np.isnan(ref_out)
+    d_out = np.abs(out[osel] - ref_out[osel])
+    d_lse = np.abs(lse[sel] - ref_lse[sel])
+    msg = (f"{what}: out max {d_out.max():.3e} mean {d_out.mean():.3e}; "
+           f"lse max {d_lse.max():.3e}")
+    assert np.isfinite(out[osel]).all() and np.isfinite(lse[sel]).all(), msg
+    assert d_out.max() <= OUT_MAX_ABS, msg
+    assert d_out.mean() <= OUT_MEAN_ABS, msg
+    assert d_lse.max() <= LSE_MAX_ABS, msg
+    return d_out.max(), d_out.mean(), d_lse.max()
+
+
+def rel_l2(x, ref):
+    x, ref = np.asarray(x, dtype=np.float64), np.asarray(ref, dtype=np.float64)
+    return float(np.linalg.norm(x - ref) / max(np.linalg.norm(ref), 1e-300))

@@ -1,0 +1,158 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, and rejects bad arguments on the host before any HIP call."""
+
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+from attention_attn_fwd_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gptoss_attn.h")
+
+P = 0x10000  # a 256-byte aligned, never dereferenced stand-in pointer
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gptoss_attn_\w+)\s*\(", text)))
+
+
+def test_header_declares_expected_entry_points():
+    names = _declared_functions()
+    assert set(names) == set(_lib.EXPORTS), names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_abi_version(lib):
+    assert lib.gptoss_attn_abi_version() == 1
+
+
+def _fwd(lib, **kw):
+    a = dict(q=P, k=P, v=P, sinks=P, B=1, S=16, Hq=8, Hkv=1, D=64, window=0, scale=0.125, out=P, lse=P,
+             stream=None)
+    a.update(kw)
+    return lib.gptoss_attn_fwd(a["q"], a["k"], a["v"], a["sinks"], a["B"], a["S"], a["Hq"], a["Hkv"], a["D"],
+                               a["window"], a["scale"], a["out"], a["lse"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status,frag", [
+    (dict(q=None), 1, "q is NULL"),
+    (dict(k=None), 1, "k is NULL"),
+    (dict(out=None), 1, "out is NULL"),
+    (dict(lse=None), 1, "lse is NULL"),
+    (dict(sinks=None), 1, "sinks is NULL"),
+    (dict(q=P + 8), 1, "aligned"),
+    (dict(lse=P + 2), 1, "aligned"),
+    (dict(B=-1), 1, "must be >= 0"),
+    (dict(S=-3), 1, "must be >= 0"),
+    (dict(Hq=0), 1, ">= 1"),
+    (dict(Hkv=0), 1, ">= 1"),
+    (dict(Hq=8, Hkv=3), 1, "multiple"),
+    (dict(window=-1), 1, "window"),
+    (dict(scale=0.0), 1, "softmax_scale"),
+    (dict(scale=-1.0), 1, "softmax_scale"),
+    (dict(scale=math.inf), 1, "softmax_scale"),
+    (dict(scale=math.nan), 1, "softmax_scale"),
+    (dict(D=128), 2, "head_dim"),
+    (dict(Hq=512, Hkv=1), 2, "group size"),
+    (dict(B=65536, S=65536), 1, "exceeds"),
+])
+def test_fwd_rejects_bad_arguments(lib, kw, status, frag):
+    st = _fwd(lib, **kw)
+    assert st == status
+    assert frag in lib.gptoss_attn_last_error().decode()
+
+
+def test_zero_sized_problems_are_noops(lib):
+    assert _fwd(lib, B=0, q=None, k=None, v=None, sinks=None, out=None, lse=None) == 0
+    assert _fwd(lib, S=0, q=None, k=None, v=None, sinks=None, out=None, lse=None) == 0
+    st = lib.gptoss_attn_decode(None, None, None, None, None, 0, 8, 1, 64, 1, 0, 0.125, None, None, None, 0,
+                                None)
+    assert st == 0
+    st = lib.gptoss_attn_bwd(*([None] * 7), 0, 4, 8, 1, 64, 0, 0.125, *([None] * 5), 0, None)
+    assert st == 0
+
+
+def _bwd(lib, ws=P, ws_bytes=None, **kw):
+    a = dict(B=1, S=256, Hq=8, Hkv=1, D=64, window=0, scale=0.125)
+    a.update(kw)
+    need = lib.gptoss_attn_bwd_workspace_size(a["B"], a["S"], a["Hq"], a["Hkv"], a["D"], a["window"])
+    ptrs = [P] * 7
+    outs = [P] * 4
+    if "dq" in kw:
+        outs[0] = kw.pop("dq")
+    return lib.gptoss_attn_bwd(*ptrs, a["B"], a["S"], a["Hq"], a["Hkv"], a["D"], a["window"], a["scale"],
+                               *outs, ws, need if ws_bytes is None else ws_bytes, None), need
+
+
+def test_bwd_rejects_small_workspace(lib):
+    st, need = _bwd(lib)
+    if need > 0:
+        st, _ = _bwd(lib, ws_bytes=need - 1)
+        assert st == 1 and "workspace" in lib.gptoss_attn_last_error().decode()
+        st, _ = _bwd(lib, ws=P + 64)
+        assert st == 1 and "aligned" in lib.gptoss_attn_last_error().decode()
+
+
+def test_bwd_rejects_bad_arguments(lib):
+    st = lib.gptoss_attn_bwd(*([P] * 7), 1, 64, 8, 3, 64, 0, 0.125, *([P] * 4), P, 1 << 30, None)
+    assert st == 1 and "multiple" in lib.gptoss_attn_last_error().decode()
+    st = lib.gptoss_attn_bwd(*([P] * 7), 1, 64, 8, 1, 64, 0, 0.125, None, P, P, P, P, 1 << 30, None)
+    assert st == 1 and "dq is NULL" in lib.gptoss_attn_last_error().decode()
+
+
+def _dec(lib, **kw):
+    a = dict(q=P, kc=P, vc=P, cu=P, sinks=P, N=128, Hq=64, Hkv=8, D=64, max_seqlen=1024, window=0,
+             scale=0.125, out=P, lse=P, ws=P, ws_bytes=None)
+    a.update(kw)
+    need = lib.gptoss_attn_decode_workspace_size(a["N"], a["Hq"], a["Hkv"], a["D"], a["max_seqlen"],
+                                                 a["window"])
+    wb = need if a["ws_bytes"] is None else a["ws_bytes"]
+    return lib.gptoss_attn_decode(a["q"], a["kc"], a["vc"], a["cu"], a["sinks"], a["N"], a["Hq"], a["Hkv"],
+                                  a["D"], a["max_seqlen"], a["window"], a["scale"], a["out"], a["lse"],
+                                  a["ws"], wb, None)
+
+
+@pytest.mark.parametrize("kw,frag", [
+    (dict(cu=None), "cu_seqlens is NULL"),
+    (dict(max_seqlen=0), "max_seqlen"),
+    (dict(N=-1), "N"),
+    (dict(N=70000), "exceeds"),
+    (dict(window=-2), "window"),
+    (dict(ws_bytes=1), "workspace"),
+    (dict(ws=None), "workspace is NULL"),
+    (dict(kc=P + 4), "aligned"),
+])
+def test_decode_rejects_bad_arguments(lib, kw, frag):
+    assert _dec(lib, **kw) == 1
+    assert frag in lib.gptoss_attn_last_error().decode()
+
+
+def test_workspace_size_queries(lib):
+    assert lib.gptoss_attn_decode_workspace_size(128, 64, 8, 64, 1024, 0) > 0
+    # a sliding layer fits one split per sequence: no partials
+    assert lib.gptoss_attn_decode_workspace_size(128, 64, 8, 64, 1024, 128) == 0
+    assert lib.gptoss_attn_decode_workspace_size(128, 64, 8, 128, 1024, 0) == 0  # unsupported D
+    assert lib.gptoss_attn_bwd_workspace_size(4, 4096, 64, 8, 64, 0) >= 0
+    assert lib.gptoss_attn_bwd_workspace_size(4, 4096, 64, 7, 64, 0) == 0
+
+
+def test_error_message_cleared_on_success(lib):
+    _fwd(lib, q=None)
+    assert lib.gptoss_attn_last_error().decode() != ""
+    assert _fwd(lib, B=0) == 0
+    assert lib.gptoss_attn_last_error().decode() == ""

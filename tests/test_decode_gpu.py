@@ -1,0 +1,115 @@
+"""Decode parity of the HIP path against the fp64 oracle (GPU)."""
+
+import numpy as np
+import pytest
+import torch
+
+import attention_attn_fwd_amd as attn
+from attention_attn_fwd_amd import synth
+from oracle import ref_decode
+
+from _util import check_out_lse, f64, need_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(case, window, dev, max_seqlen=None):
+    t = [x.to(dev) for x in (case.q, case.k_cache, case.v_cache, case.cu_seqlens, case.sinks)]
+    out, lse = attn.decode(*t, case.max_seqlen if max_seqlen is None else max_seqlen, window, case.scale)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+def _oracle(case, window):
+    return ref_decode(f64(case.q), f64(case.k_cache), f64(case.v_cache), case.cu_seqlens.numpy(),
+                      f64(case.sinks), window, case.scale)
+
+
+@pytest.mark.parametrize("window", [128, 0])
+def test_decode_c4(window):
+    dev = need_gpu()
+    case = synth.config_inputs("c4_decode_n128_l1024_h64x8")
+    print(f"decode C4 W={window}", flush=True)
+    out, lse = _run(case, window, dev)
+    ro, rl = _oracle(case, window)
+    check_out_lse(f64(out), f64(lse), ro, rl, f"C4 W={window}")
+
+
+EDGE_LENGTHS = [1, 2, 63, 64, 65, 127, 128, 129, 255, 256, 257, 511, 512, 513, 1000, 1024]
+
+
+@pytest.mark.parametrize("window", [0, 1, 127, 128, 129])
+@pytest.mark.parametrize("heads", [(64, 8), (8, 1), (8, 8), (6, 2), (40, 1)])
+def test_decode_edge_lengths(window, heads):
+    dev = need_gpu()
+    Hq, Hkv = heads
+    case = synth.make_decode(len(EDGE_LENGTHS), Hq, Hkv, lengths=EDGE_LENGTHS, seed=window + 3 * Hq)
+    out, lse = _run(case, window, dev)
+    ro, rl = _oracle(case, window)
+    check_out_lse(f64(out), f64(lse), ro, rl, f"edges W={window} heads={heads}")
+
+
+def test_decode_empty_sequences():
+    dev = need_gpu()
+    lengths = [0, 5, 0, 300, 0]
+    case = synth.make_decode(len(lengths), 8, 1, lengths=lengths, seed=5)
+    case.sinks[3] = -np.inf
+    out, lse = _run(case, 0, dev, max_seqlen=1024)
+    ro, rl = _oracle(case, 0)
+    o, l = f64(out), f64(lse)
+    for n in (0, 2, 4):
+        assert (o[n] == 0).all()
+        np.testing.assert_array_equal(l[n], f64(case.sinks))
+    check_out_lse(o[[1, 3]], l[[1, 3]], ro[[1, 3]], rl[[1, 3]], "non-empty rows")
+
+
+@pytest.mark.parametrize("window", [0, 128])
+def test_decode_multi_step(window):
+    """Append one token per sequence and decode again, five times over; every
+    step is compared with the oracle on the grown cache."""
+    dev = need_gpu()
+    gen = torch.Generator().manual_seed(77)
+    N, Hq, Hkv, D = 16, 64, 8, 64
+    lengths = torch.randint(120, 300, (N,), generator=gen).tolist()
+    lengths[0], lengths[1] = 1, 127
+    seqs_k = [torch.randn(L, Hkv, D, generator=gen).to(torch.bfloat16) for L in lengths]
+    seqs_v = [torch.randn(L, Hkv, D, generator=gen).to(torch.bfloat16) for L in lengths]
+    sinks = torch.randn(Hq, generator=gen)
+    for step in range(5):
+        q = torch.randn(N, Hq, D, generator=gen).to(torch.bfloat16)
+        lens = [s.shape[0] for s in seqs_k]
+        cu = torch.zeros(N + 1, dtype=torch.int32)
+        cu[1:] = torch.cumsum(torch.tensor(lens), 0)
+        case = synth.DecodeCase(q, torch.cat(seqs_k), torch.cat(seqs_v), cu, sinks, max(lens), 0.125)
+        out, lse = _run(case, window, dev)
+        ro, rl = _oracle(case, window)
+        check_out_lse(f64(out), f64(lse), ro, rl, f"step {step}")
+        # the next token's K/V join every cache
+        for n in range(N):
+            seqs_k[n] = torch.cat([seqs_k[n], torch.randn(1, Hkv, D, generator=gen).to(torch.bfloat16)])
+            seqs_v[n] = torch.cat([seqs_v[n], torch.randn(1, Hkv, D, generator=gen).to(torch.bfloat16)])
+
+
+def test_decode_matches_prefill_last_row():
+    """Decode of the last token equals row L-1 of the GPU prefill (both
+    within the bar of the oracle; compared to each other here)."""
+    dev = need_gpu()
+    S = 700
+    case = synth.make_prefill(1, S, 16, 2, seed=12)
+    for window in (0, 128):
+        out_p, lse_p = attn.fwd(case.q.to(dev), case.k.to(dev), case.v.to(dev), case.sinks.to(dev), window,
+                                case.scale)
+        cu = torch.tensor([0, S], dtype=torch.int32, device=dev)
+        out_d, lse_d = attn.decode(case.q[0, S - 1:S].to(dev).contiguous(), case.k[0].to(dev), case.v[0].to(dev),
+                                   cu, case.sinks.to(dev), S, window, case.scale)
+        torch.cuda.synchronize()
+        assert (out_d.float() - out_p[0, S - 1].float()).abs().max().item() <= 1e-2
+        assert (lse_d[0] - lse_p[0, :, S - 1]).abs().max().item() <= 1e-3
+
+
+def test_decode_is_deterministic():
+    dev = need_gpu()
+    case = synth.make_decode(32, 64, 8, max_len=1024, seed=13)
+    a = _run(case, 0, dev)
+    b = _run(case, 0, dev)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
