@@ -50,6 +50,12 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, r);
 }
 
+// Sum of the two bf16 halves of w added to acc (v_dot2c_f32_bf16 against 1.0).
+__device__ __forceinline__ float add_bf16_pair(uint32_t w, float acc) {
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), ones, acc, false);
+}
+
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
@@ -82,10 +88,13 @@ __device__ __forceinline__ constexpr int acc_row(int r, int g) { return 8 * (r >
 __device__ __forceinline__ int perm_row(int m) { return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1); }
 
 // LDS tiles of 64 rows x 64 bf16 are stored as 8 sixteen-byte units per row
-// with the unit index XOR-swizzled by the row, so that the 8 rows read by
-// one ds_read_b128 phase (rows perm_row(0..7)) and the 4 consecutive rows of
-// a transposing read fall into different bank groups.
-__device__ __forceinline__ int kswz(int row) { return (row & 3) | ((row >> 1) & 4); }
+// with the unit index XOR-swizzled by the row.  gfx950 LDS has 64 four-byte
+// banks (256 bytes per cycle), i.e. 16 sixteen-byte units: a row pair (2r,
+// 2r+1) spans all 16, and XOR-ing the unit with (row >> 1) & 7 sends the 16
+// rows read by one 16-lane ds_read_b128 phase (any 16 consecutive rows, in
+// any order) and the 4 consecutive rows x 2 units of a transposing read to
+// distinct units.
+__device__ __forceinline__ int kswz(int row) { return (row >> 1) & 7; }
 __device__ __forceinline__ int tile_unit(int row, int unit) { return row * 8 + (unit ^ kswz(row)); }
 
 // ds_read_b64_tr_b16: within each 16-lane block, lane i receives element

@@ -49,7 +49,9 @@ struct DecParams {
     float c;          // scale * log2(e)
 };
 
-__device__ __forceinline__ int vswz(int d) { return d & 7; }
+// V^T tile rows are indexed by d and swizzled like the forward's tiles: a
+// 16-lane ds_read_b128 phase reads 16 consecutive d rows.
+__device__ __forceinline__ int vswz(int d) { return (d >> 1) & 7; }
 
 __device__ __forceinline__ void seq_range(const DecParams& p, int n, int& base, int& L, int& vis_lo) {
     base = p.cu[n];
@@ -132,11 +134,13 @@ decode_split_kernel(DecParams p) {
         const int dc = g + 2 * pass;
         const uint32_t a[4] = {vr[pass][0].x, vr[pass][0].y, vr[pass][0].z, vr[pass][0].w};
         const uint32_t c[4] = {vr[pass][1].x, vr[pass][1].y, vr[pass][1].z, vr[pass][1].w};
+        // the two half-waves store rows of opposite parity (disjoint banks)
 #pragma unroll
         for (int s = 0; s < 8; ++s) {
-            const int d = 8 * dc + s;
-            const uint32_t lo = (s & 1) ? (a[s >> 1] >> 16) : (a[s >> 1] & 0xffffu);
-            const uint32_t hi = (s & 1) ? (c[s >> 1] & 0xffff0000u) : (c[s >> 1] << 16);
+            const int e = s ^ g;
+            const int d = 8 * dc + e;
+            const uint32_t lo = (e & 1) ? (a[s >> 1] >> 16) : (a[s >> 1] & 0xffffu);
+            const uint32_t hi = (e & 1) ? (c[s >> 1] & 0xffff0000u) : (c[s >> 1] << 16);
             vs[(d * 8 + ((kp >> 2) ^ vswz(d))) * 4 + (kp & 3)] = lo | hi;
         }
     }

@@ -61,9 +61,39 @@ struct FwdParams {
 };
 
 
-// V^T tile rows are indexed by d; the 8 lanes of a ds_read_b128 phase read
-// d rows 8 apart, so the unit swizzle is d & 7.
-__device__ __forceinline__ int vswz(int d) { return d & 7; }
+// V^T tile rows are indexed by d and swizzled like the K tile: a 16-lane
+// ds_read_b128 phase reads 16 consecutive d rows.
+__device__ __forceinline__ int vswz(int d) { return (d >> 1) & 7; }
+
+// Lazy rescaling bound: a tile's probabilities are exponentiated against the
+// running max m as long as every lane's tile sum stays below this bound
+// (so every p <= 2^12); otherwise the tile is redone against its true max.
+constexpr float kRescaleBound = 4096.0f;
+
+// p = exp2(s * c - m) for the 32 scores of one column held by this lane
+// (two 32-key blocks), packed into the bf16 B operands of the four 16-key
+// P.V steps; returns the fp32 sum of the unrounded values (summing the bf16
+// values would cost lse up to 2^-9 relative when one key dominates).
+__device__ __forceinline__ float exp_pack(const f32x16& s0, const f32x16& s1, float c, float m, bf16x8* pb,
+                                          int stride) {
+    float la = 0.0f, lb = 0.0f;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+        const f32x16& sv = kk < 2 ? s0 : s1;
+        uint32_t w[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int r = 8 * (kk & 1) + 2 * j;
+            const float e0 = fast_exp2(fmaf(sv[r], c, -m));
+            const float e1 = fast_exp2(fmaf(sv[r + 1], c, -m));
+            w[j] = pack_bf16x2(e0, e1);
+            la += e0;
+            lb += e1;
+        }
+        pb[kk * stride] = __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
+    }
+    return la + lb;
+}
 
 // Workgroup -> (KV group, query tile).  Workgroups are dispatched round-robin
 // over the 8 XCDs, so when the groups split evenly each XCD walks its own
@@ -99,6 +129,7 @@ fwd_kernel(FwdParams p) {
     const int G = p.G;
     const int S = p.S;
     const int W = p.window;
+    const unsigned Weff = W > 0 ? (unsigned)W : 0x7fffffffu;
     const int p0 = qt * p.pos_per_block;
     const int used_cols = p.pos_per_block * G;
     const int P1 = min(p0 + p.pos_per_block, S) - 1;
@@ -178,15 +209,19 @@ fwd_kernel(FwdParams p) {
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             const int key = k_key0 + 32 * j;
-            ks[key * 8 + (k_unit ^ kswz(key))] = kreg[j];
+            ks[tile_unit(key, k_unit)] = kreg[j];
         }
         const uint32_t a[4] = {vreg[0].x, vreg[0].y, vreg[0].z, vreg[0].w};
         const uint32_t c[4] = {vreg[1].x, vreg[1].y, vreg[1].z, vreg[1].w};
+        // lanes 32..63 (odd d chunk) walk the rows in the order s ^ 1 so the
+        // two half-waves of each store hit rows of opposite parity (disjoint banks)
+        const int flip = v_dc & 1;
 #pragma unroll
         for (int s = 0; s < 8; ++s) {
-            const int d = 8 * v_dc + s;
-            const uint32_t lo = (s & 1) ? (a[s >> 1] >> 16) : (a[s >> 1] & 0xffffu);
-            const uint32_t hi = (s & 1) ? (c[s >> 1] & 0xffff0000u) : (c[s >> 1] << 16);
+            const int e = s ^ flip;
+            const int d = 8 * v_dc + e;
+            const uint32_t lo = (e & 1) ? (a[s >> 1] >> 16) : (a[s >> 1] & 0xffffu);
+            const uint32_t hi = (e & 1) ? (c[s >> 1] & 0xffff0000u) : (c[s >> 1] << 16);
             vs[(d * 8 + ((v_kp >> 2) ^ vswz(d))) * 4 + (v_kp & 3)] = lo | hi;
         }
     };
@@ -197,6 +232,7 @@ fwd_kernel(FwdParams p) {
     }
     __syncthreads();
 
+    bool fresh[2] = {true, true};  // row has not seen a key yet
     for (int t = t_begin; t <= t_end; ++t) {
         const int buf = (t - t_begin) & 1;
         const bool has_next = t < t_end;
@@ -209,89 +245,104 @@ fwd_kernel(FwdParams p) {
             const uint4* ks = smem[buf][0];
             const uint4* vs = smem[buf][1];
 
-            // S^T = K Q^T
-            f32x16 sacc[2][2];
+            // S^T = K Q^T for the tile, masked on edge tiles.  Register r of
+            // key block mb holds key kt0 + 32 mb + 16 (r / 8) + 8 g + r % 8;
+            // it is visible iff 0 <= pos - key < Weff (one unsigned compare).
+            auto scores = [&](f32x16 (&sacc)[2][2]) {
 #pragma unroll
-            for (int mb = 0; mb < 2; ++mb)
+                for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+                    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) sacc[mb][nb][r] = 0.0f;
+#pragma unroll
+                for (int ks_ = 0; ks_ < 4; ++ks_) {
+#pragma unroll
+                    for (int mb = 0; mb < 2; ++mb) {
+                        const int key = 32 * mb + perm_row(l32);
+                        const bf16x8 a = as_bf16x8(ks[tile_unit(key, 2 * ks_ + g)]);
+#pragma unroll
+                        for (int nb = 0; nb < 2; ++nb) sacc[mb][nb] = mfma32(a, qf[nb][ks_], sacc[mb][nb]);
+                    }
+                }
+                if (need_mask) {
+#pragma unroll
+                    for (int nb = 0; nb < 2; ++nb) {
+                        const int dd = col_pos[nb] - kt0 - 8 * g;
+#pragma unroll
+                        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+                            for (int r = 0; r < 16; ++r) {
+                                const int cr = 32 * mb + 16 * (r >> 3) + (r & 7);
+                                const bool vis = (unsigned)(dd - cr) < Weff;
+                                sacc[mb][nb][r] = vis ? sacc[mb][nb][r] : -INFINITY;
+                            }
+                    }
+                }
+            };
+
+            // Online softmax (log2 domain), one column per lane pair.  Fast
+            // path: exponentiate against the running max.  Slow path (the
+            // first tile in which some row sees keys, a row still at -inf, or
+            // a tile sum above the bound): scores against the true row max,
+            // rescale.  A row's first tile always takes the exact path so the
+            // dominant key of a short row gets p = 1 exactly (no bf16
+            // rounding on it).
+            bf16x8 pb[4][2];
+            float lt[2] = {0.0f, 0.0f};
+            bool first = false;
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb) {
+                const int pos = col_pos[nb];
+                const bool sees = kt0 <= pos && (W == 0 || kt0 + kBk - 1 > pos - W);
+                first |= fresh[nb] && sees;
+                fresh[nb] = fresh[nb] && !sees;
+            }
+            bool slow = __any(first || m_run[0] == -INFINITY || m_run[1] == -INFINITY);
+            if (!slow) {
+                f32x16 sacc[2][2];
+                scores(sacc);
 #pragma unroll
                 for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) sacc[mb][nb][r] = 0.0f;
-#pragma unroll
-            for (int ks_ = 0; ks_ < 4; ++ks_) {
-#pragma unroll
-                for (int mb = 0; mb < 2; ++mb) {
-                    const int key = 32 * mb + perm_row(l32);
-                    const bf16x8 a = as_bf16x8(ks[key * 8 + ((2 * ks_ + g) ^ kswz(key))]);
-#pragma unroll
-                    for (int nb = 0; nb < 2; ++nb) sacc[mb][nb] = mfma32(a, qf[nb][ks_], sacc[mb][nb]);
-                }
+                    lt[nb] = exp_pack(sacc[0][nb], sacc[1][nb], p.c, m_run[nb], &pb[0][nb], 2);
+                slow = __any(lt[0] > kRescaleBound || lt[1] > kRescaleBound);
             }
-
-            if (need_mask) {
-#pragma unroll
-                for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int key = kt0 + 32 * mb + perm_row(acc_row(r, g));
-#pragma unroll
-                        for (int nb = 0; nb < 2; ++nb) {
-                            const int pos = col_pos[nb];
-                            const bool vis = key <= pos && (W == 0 || pos - key < W);
-                            sacc[mb][nb][r] = vis ? sacc[mb][nb][r] : -INFINITY;
-                        }
-                    }
-            }
-
-            // online softmax (log2 domain), one column per lane-pair
-            float m_use[2];
-            bool grow = false;
-            float m_new[2];
-#pragma unroll
-            for (int nb = 0; nb < 2; ++nb) {
-                float mx = -INFINITY;
-#pragma unroll
-                for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[mb][nb][r]);
-                mx = max_across_halves(mx);
-                m_new[nb] = fmaxf(m_run[nb], mx * p.c);
-                grow |= m_new[nb] > m_run[nb];
-            }
-            if (__any(grow)) {
+            if (slow) {
+                f32x16 sacc[2][2];
+                scores(sacc);
+                float alpha[2];
+                bool grow = false;
 #pragma unroll
                 for (int nb = 0; nb < 2; ++nb) {
-                    const float alpha = m_new[nb] > m_run[nb] ? fast_exp2(m_run[nb] - m_new[nb]) : 1.0f;
-                    l_run[nb] *= alpha;
+                    float mx = -INFINITY;
 #pragma unroll
-                    for (int db = 0; db < 2; ++db)
+                    for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-                        for (int r = 0; r < 16; ++r) oacc[db][nb][r] *= alpha;
-                    m_run[nb] = m_new[nb];
+                        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[mb][nb][r]);
+                    mx = max_across_halves(mx);
+                    const float m_new = fmaxf(m_run[nb], mx * p.c);
+                    alpha[nb] = m_new > m_run[nb] ? fast_exp2(m_run[nb] - m_new) : 1.0f;
+                    grow |= m_new > m_run[nb];
+                    m_run[nb] = m_new;
+                }
+                if (__any(grow)) {
+#pragma unroll
+                    for (int nb = 0; nb < 2; ++nb) {
+                        l_run[nb] *= alpha[nb];
+#pragma unroll
+                        for (int db = 0; db < 2; ++db)
+#pragma unroll
+                            for (int r = 0; r < 16; ++r) oacc[db][nb][r] *= alpha[nb];
+                    }
+                }
+#pragma unroll
+                for (int nb = 0; nb < 2; ++nb) {
+                    const float m_use = m_run[nb] == -INFINITY ? 0.0f : m_run[nb];
+                    lt[nb] = exp_pack(sacc[0][nb], sacc[1][nb], p.c, m_use, &pb[0][nb], 2);
                 }
             }
-#pragma unroll
-            for (int nb = 0; nb < 2; ++nb) m_use[nb] = m_run[nb] == -INFINITY ? 0.0f : m_run[nb];
-
-            bf16x8 pb[4][2];
-#pragma unroll
-            for (int nb = 0; nb < 2; ++nb) {
-                float lsum = 0.0f;
-#pragma unroll
-                for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-                    for (int h = 0; h < 2; ++h) {
-                        bf16x8 v8;
-#pragma unroll
-                        for (int s = 0; s < 8; ++s) {
-                            const float e = fast_exp2(fmaf(sacc[mb][nb][8 * h + s], p.c, -m_use[nb]));
-                            lsum += e;
-                            v8[s] = (__bf16)e;
-                        }
-                        pb[2 * mb + h][nb] = v8;
-                    }
-                l_run[nb] += lsum;
-            }
+            l_run[0] += lt[0];
+            l_run[1] += lt[1];
 
             // O^T += V^T P^T
 #pragma unroll

@@ -1,0 +1,238 @@
+#!/usr/bin/env python3
+"""Benchmark of the sink-attention hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of synthetic input:
+  gpt-oss layer pair at B=4, S=4096, 64 query / 8 KV heads, head_dim 64 --
+  forward + backward of the sliding-window-128 layer and of the full-causal
+  layer -- plus decode of both layers for 128 sequences with KV lengths
+  U{1..1024}.
+Inputs and outputs stay resident in HBM; the timed region holds exactly
+`--steps` steps between two stream synchronisations.
+
+value = unmasked FLOPs of the step (forward 4*D, backward 10*D per visible
+(batch, query head, query, key) pair; decode 4*D per visible key and head)
+divided by the step time, in TFLOP/s.  Per-part figures (TFLOP/s, GB/s and
+the fraction of the bounding roof) are printed in `parts`.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2516.6      # MI355X dense bf16 MFMA (256 CU x 2.4 GHz x 4096 FLOP/clk)
+D = 64
+WINDOWS = (128, 0)             # sliding layer, full-causal layer
+
+
+def pairs_per_head(S, W):
+    """Visible (query, key) pairs of one (batch, head): closed form."""
+    if W == 0 or W >= S:
+        return S * (S + 1) // 2
+    return W * (W + 1) // 2 + (S - W) * W
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", choices=["fwd", "bwd", "decode"], default=None,
+                    help="run only this part in a loop (for profiling); prints no JSON line")
+    ap.add_argument("--verbose", action="store_true")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the path is "
+              "single-GPU by design, see DESIGN.md for how it would shard", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import attention_attn_fwd_amd as attn
+    from attention_attn_fwd_amd import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log = (lambda *a: print(*a, file=sys.stderr, flush=True)) if args.verbose else (lambda *a: None)
+
+    # ---- inputs (seeded, synthetic, gpt-oss shaped), resident in HBM
+    case, dout_cpu = synth.config_inputs("c3_bwd_b4_s4096_h64x8")
+    B, S, Hq, _ = case.q.shape
+    Hkv = case.k.shape[2]
+    q, k, v = case.q.to(dev), case.k.to(dev), case.v.to(dev)
+    sinks = case.sinks.to(dev)
+    dout = dout_cpu.to(dev)
+    dec = synth.config_inputs("c4_decode_n128_l1024_h64x8")
+    N = dec.q.shape[0]
+    dq_, dk_, dv_ = dec.q.to(dev), dec.k_cache.to(dev), dec.v_cache.to(dev)
+    dcu, dsinks_ = dec.cu_seqlens.to(dev), dec.sinks.to(dev)
+    lengths = (dec.cu_seqlens[1:] - dec.cu_seqlens[:-1]).tolist()
+    scale = case.scale
+
+    outs = {w: (torch.empty_like(q), torch.empty(B, Hq, S, device=dev)) for w in WINDOWS}
+    dec_out = {w: (torch.empty_like(dq_), torch.empty(N, Hq, device=dev)) for w in WINDOWS}
+    bws = torch.empty(attn.bwd_workspace_size(B, S, Hq, Hkv, D, 0), dtype=torch.uint8, device=dev)
+    dws = torch.empty(max(1, attn.decode_workspace_size(N, Hq, Hkv, D, dec.max_seqlen, 0)),
+                      dtype=torch.uint8, device=dev)
+
+    def fwd(w):
+        o, l = outs[w]
+        attn.fwd(q, k, v, sinks, w, scale, out=o, lse=l)
+
+    def bwd(w):
+        o, l = outs[w]
+        attn.bwd(q, k, v, sinks, o, l, dout, w, scale, workspace=bws)
+
+    def decode(w):
+        o, l = dec_out[w]
+        attn.decode(dq_, dk_, dv_, dcu, dsinks_, dec.max_seqlen, w, dec.scale, out=o, lse=l, workspace=dws)
+
+    def step():
+        for w in WINDOWS:
+            fwd(w)
+            bwd(w)
+        for w in WINDOWS:
+            decode(w)
+
+    if args.only:
+        fn = {"fwd": fwd, "bwd": bwd, "decode": decode}[args.only]
+        for _ in range(args.warmup + args.steps):
+            for w in WINDOWS:
+                fn(w)
+        torch.cuda.synchronize()
+        print(f"done: {args.only} x {args.warmup + args.steps} per layer", flush=True)
+        return
+
+    # ---- work accounting
+    flops = {}
+    bytes_ = {}
+    for w in WINDOWS:
+        pairs = B * Hq * pairs_per_head(S, w)
+        flops[("fwd", w)] = 4 * D * pairs
+        flops[("bwd", w)] = 10 * D * pairs
+        # algorithmic bytes: every input read once, every output written once
+        bytes_[("fwd", w)] = 2 * (q.numel() + k.numel() + v.numel() + q.numel()) + 4 * B * Hq * S
+        bytes_[("bwd", w)] = (2 * (4 * q.numel() + 2 * k.numel()) + 4 * B * Hq * S + 4 * Hq   # q,out,dout,dq + k,v
+                              + 2 * 2 * k.numel() + 4 * Hq)                                  # dk, dv, sinks/dsinks
+        vis = sum(min(L, w) if w else L for L in lengths)
+        flops[("decode", w)] = 4 * D * Hq * vis
+        bytes_[("decode", w)] = (2 * 2 * vis * Hkv * D + 2 * 2 * N * Hq * D + 4 * N * Hq + 4 * Hq
+                                 + 4 * (N + 1))
+
+    # ---- warmup, then the timed region: exactly `steps` steps
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for _ in range(args.steps):
+        step()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = t0.elapsed_time(t1) / args.steps
+    total_flops = sum(flops.values())
+    value = total_flops / (ms_per_step * 1e-3) / 1e12
+
+    # ---- per-part timing (outside the timed region): events around each call
+    reps = max(3, args.steps)
+    part_ms = {}
+    for name, fn in (("fwd", fwd), ("bwd", bwd), ("decode", decode)):
+        for w in WINDOWS:
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(reps)]
+            for a, b_ in evs:
+                a.record(stream)
+                fn(w)
+                b_.record(stream)
+            torch.cuda.synchronize()
+            part_ms[(name, w)] = sorted(a.elapsed_time(b_) for a, b_ in evs)[reps // 2]
+    parts = {}
+    for (name, w), ms in part_ms.items():
+        tf = flops[(name, w)] / (ms * 1e-3) / 1e12
+        gbs = bytes_[(name, w)] / (ms * 1e-3) / 1e9
+        ai = flops[(name, w)] / bytes_[(name, w)]
+        roof_tf = min(BF16_PEAK_TFLOPS, ai * HBM_PEAK_GBS / 1e3)
+        parts[f"{name}_{'full' if w == 0 else 'w%d' % w}"] = {
+            "ms": round(ms, 4), "tflops": round(tf, 2), "gbs": round(gbs, 1),
+            "bound": "mfma" if roof_tf >= BF16_PEAK_TFLOPS else "hbm",
+            "frac_of_roof": round(tf / roof_tf, 4)}
+    log(json.dumps(parts, indent=1))
+
+    # dominant kernel: the single-launch forward of the full-causal layer
+    ms_f = part_ms[("fwd", 0)]
+    ach = flops[("fwd", 0)] / (ms_f * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "achieved": round(ach, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(ach / BF16_PEAK_TFLOPS, 4), "traffic": None, "kernel": "fwd_kernel (full causal)"}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(case, dout_cpu)
+
+    line = {
+        "metric": "attn fwd/bwd TFLOP/s (unmasked FLOPs) + decode GB/s, % of MI355X roofline",
+        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "gpt-oss sink attention layer pair (sliding-128 + full causal): fwd+bwd at "
+                               "B=4 S=4096 Hq=64 Hkv=8 D=64, plus decode N=128 L~U[1,1024]",
+                   "global_batch": B, "seq_len": S, "parallelism": "none (1 GPU)"},
+        "decode_gbs": {("full" if w == 0 else "w128"): parts["decode_" + ("full" if w == 0 else "w128")]["gbs"]
+                       for w in WINDOWS},
+        "parts": parts,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(case, dout_cpu):
+    """The fp64 oracle timed on this host on a bounded sample of the same step:
+    forward + backward of KV group 0 (query heads 0..7) of batch 0 at the full
+    S = 4096, for both layers.  Reported in the metric's unit over that
+    sample's unmasked FLOPs."""
+    from oracle import ref_bwd, ref_fwd
+
+    cores = len(os.sched_getaffinity(0))
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [i["num_threads"] for i in threadpool_info() if i.get("user_api") == "blas"]
+        if blas:
+            cores = min(cores, max(blas))
+    except Exception:
+        pass
+    f64 = lambda t: t.to(torch_float64()).numpy()
+    q = f64(case.q[:1])
+    k = f64(case.k[:1])
+    v = f64(case.v[:1])
+    s = f64(case.sinks)
+    do = f64(dout_cpu[:1])
+    heads = list(range(8))
+    S = q.shape[1]
+    t = time.perf_counter()
+    fl = 0
+    for w in WINDOWS:
+        ref_fwd(q, k, v, s, w, case.scale, heads=heads)
+        ref_bwd(q, k, v, s, do, w, case.scale, heads=heads)
+        fl += (4 + 10) * D * len(heads) * pairs_per_head(S, w)
+    el = time.perf_counter() - t
+    return {"value": round(fl / el / 1e12, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": "fp64 oracle fwd+bwd of batch 0, query heads 0-7 (KV group 0), S=4096, both layers "
+                      f"({el:.1f} s); decode not included"}
+
+
+def torch_float64():
+    import torch
+    return torch.float64
+
+
+if __name__ == "__main__":
+    main()
