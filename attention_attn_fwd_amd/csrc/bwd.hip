@@ -26,7 +26,7 @@
 //            put one column per lane, which is the operand layout of
 //            dQ^T += K^T dS^T (K^T through transposing LDS reads).
 //   dsink  : one workgroup per head reduces the per-row terms the dq kernel
-//            left in the workspace.
+//            left in the workspace ([head][batch][position], contiguous).
 // P and dP are recomputed in both the key-outer and query-outer kernels.
 // dsink does not use Dvec = <dout, out>, whose bf16 `out` carries rounding
 // that a cancelling sum over all rows would amplify: the dq kernel forms
@@ -34,6 +34,8 @@
 // fp32 while it sweeps row i's keys and stores exp(sink - lse_i) r_i.
 #include "common.h"
 #include "launch.h"
+
+#include <type_traits>
 
 namespace gptoss {
 namespace {
@@ -52,7 +54,8 @@ struct BwdParams {
     uint16_t* dk;
     uint16_t* dv;
     float* dsinks;
-    float2* ld;  // [B][S][Hq] {lse * log2(e), Dvec}; .x later holds the dsink term
+    float2* ld;      // [B][S][Hq] {lse * log2(e), Dvec}
+    float* dsterm;   // [Hq][B][S] exp(sink - lse) * sum_j P dP per row
     int B, S, Hq, Hkv, G, window;
     float scale;
     float c;  // scale * log2(e)
@@ -95,7 +98,8 @@ bwd_dsink_kernel(BwdParams p) {
     const int h = blockIdx.x;
     const long long n = (long long)p.B * p.S;
     float acc = 0.0f;
-    for (long long i = threadIdx.x; i < n; i += kThreads) acc += p.ld[i * p.Hq + h].x;
+    const float* src = p.dsterm + (size_t)h * n;
+    for (long long i = threadIdx.x; i < n; i += kThreads) acc += src[i];
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = acc;
@@ -128,8 +132,9 @@ __global__ void __launch_bounds__(kThreads, 2)
 bwd_dkdv_kernel(BwdParams p, int n_kt) {
     __shared__ uint4 sQ[2][512];
     __shared__ uint4 sO[2][512];
-    __shared__ float2 sLD[2][kColsPerStep];
-    __shared__ int sPos[2][kColsPerStep];
+    __shared__ float4 sL[2][kColsPerStep / 4];  // lse * log2(e) per column
+    __shared__ float4 sD[2][kColsPerStep / 4];  // Dvec per column
+    __shared__ int4 sP[2][kColsPerStep / 4];    // position per column
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 5, l32 = lane & 31, i16 = lane & 15;
@@ -137,6 +142,7 @@ bwd_dkdv_kernel(BwdParams p, int n_kt) {
     dkdv_coords(p, n_kt, blockIdx.x, grp, kt);
     const int b = grp / p.Hkv, kvh = grp % p.Hkv;
     const int S = p.S, W = p.window, G = p.G, Hq = p.Hq;
+    const unsigned Weff = W > 0 ? (unsigned)W : 0x7fffffffu;
     const int k0 = kt * kKeysPerBlock;
     const int kw0 = k0 + 32 * wave;          // this wave's keys kw0 .. kw0+31
     const int kw1 = min(kw0 + 31, S - 1);
@@ -160,7 +166,8 @@ bwd_dkdv_kernel(BwdParams p, int n_kt) {
         }
     }
 
-    // query columns that can see keys [k0, k0 + 127]
+    // query columns (position, head of the group; head fastest) that can see
+    // keys [k0, k0 + 127]
     const int pos_lo = k0;
     const int pos_hi = W > 0 ? min(S - 1, k0 + kKeysPerBlock - 1 + W - 1) : S - 1;
     const int n_cols = (pos_hi - pos_lo + 1) * G;
@@ -172,15 +179,19 @@ bwd_dkdv_kernel(BwdParams p, int n_kt) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) dkacc[db][r] = dvacc[db][r] = 0.0f;
 
-    // staging: rows (columns) tid/8 and tid/8 + 32, unit tid % 8
+    // staging: thread stages rows (columns) st_row and st_row + 32 (unit
+    // st_unit) of each 64-column step, and threads 0..63 the per-column
+    // scalars.  A column c maps to (pos_lo + c / G, kvh * G + c % G); when G
+    // divides 64 a step advances every staged column by 64 / G positions.
     const int st_row = tid >> 3, st_unit = tid & 7;
+    const bool g64 = (kColsPerStep % G) == 0;
+    const size_t pos_stride = (size_t)Hq * kHeadDim;  // elements per position
+    const uint16_t* qcol_base = p.q + (((size_t)b * S) * Hq + (size_t)kvh * G) * kHeadDim + 8 * st_unit;
+    const uint16_t* ocol_base = p.dout + (((size_t)b * S) * Hq + (size_t)kvh * G) * kHeadDim + 8 * st_unit;
+    const float2* ld_base = p.ld + ((size_t)b * S) * Hq + (size_t)kvh * G;
     uint4 rq[2], ro[2];
     float2 rld = make_float2(INFINITY, 0.0f);
-    int rpos = 0;
-    auto col_addr = [&](int c, int& pos, int& head) {
-        pos = pos_lo + c / G;
-        head = kvh * G + c % G;
-    };
+    int rpos = 0x3fffffff;
     auto load_step = [&](int st) {
         const int c0 = st * kColsPerStep;
 #pragma unroll
@@ -189,11 +200,11 @@ bwd_dkdv_kernel(BwdParams p, int n_kt) {
             rq[j] = make_uint4(0, 0, 0, 0);
             ro[j] = make_uint4(0, 0, 0, 0);
             if (c < n_cols) {
-                int pos, head;
-                col_addr(c, pos, head);
-                const size_t off = (((size_t)b * S + pos) * Hq + head) * kHeadDim + 8 * st_unit;
-                rq[j] = ld16(p.q + off);
-                ro[j] = ld16(p.dout + off);
+                const int cq = g64 ? (st_row + 32 * j) : c;
+                const int pos = pos_lo + (g64 ? st * (kColsPerStep / G) + cq / G : cq / G);
+                const size_t off = (size_t)pos * pos_stride + (size_t)(cq % G) * kHeadDim;
+                rq[j] = ld16(qcol_base + off);
+                ro[j] = ld16(ocol_base + off);
             }
         }
         if (tid < kColsPerStep) {
@@ -201,9 +212,9 @@ bwd_dkdv_kernel(BwdParams p, int n_kt) {
             rld = make_float2(INFINITY, 0.0f);
             rpos = 0x3fffffff;
             if (c < n_cols) {
-                int pos, head;
-                col_addr(c, pos, head);
-                rld = p.ld[((size_t)b * S + pos) * Hq + head];
+                const int cq = g64 ? tid : c;
+                const int pos = pos_lo + (g64 ? st * (kColsPerStep / G) + cq / G : cq / G);
+                rld = ld_base[(size_t)pos * Hq + cq % G];
                 rpos = pos;
             }
         }
@@ -216,8 +227,65 @@ bwd_dkdv_kernel(BwdParams p, int n_kt) {
             sO[buf][tile_unit(row, st_unit)] = ro[j];
         }
         if (tid < kColsPerStep) {
-            sLD[buf][tid] = rld;
-            sPos[buf][tid] = rpos;
+            reinterpret_cast<float*>(sL[buf])[tid] = rld.x;
+            reinterpret_cast<float*>(sD[buf])[tid] = rld.y;
+            reinterpret_cast<int*>(sP[buf])[tid] = rpos;
+        }
+    };
+
+    // One 32-column block: S = Q K^T and dP = dO V^T (one key per lane,
+    // register 8h + s = column 32 mb + 16 h + 8 g + s), P and dS, then
+    // dV^T += dO^T P and dK^T += Q^T dS over those 32 columns.
+    auto block = [&](const uint4* tq, const uint4* to, const float4* tl, const float4* td, const int4* tp, int mb,
+                     auto masked) {
+        constexpr bool kMask = decltype(masked)::value;
+        f32x16 sacc, dpacc;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sacc[r] = dpacc[r] = 0.0f;
+        const int arow = 32 * mb + perm_row(l32);
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            sacc = mfma32(as_bf16x8(tq[tile_unit(arow, 2 * ks + g)]), kb[ks], sacc);
+            dpacc = mfma32(as_bf16x8(to[tile_unit(arow, 2 * ks + g)]), vb[ks], dpacc);
+        }
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int q4 = (32 * mb + 16 * h + 8 * g) >> 2;  // float4 index of the 8 columns
+            const float4 la = tl[q4], lb = tl[q4 + 1];
+            const float4 da = td[q4], dbv = td[q4 + 1];
+            const float lv[8] = {la.x, la.y, la.z, la.w, lb.x, lb.y, lb.z, lb.w};
+            const float dv[8] = {da.x, da.y, da.z, da.w, dbv.x, dbv.y, dbv.z, dbv.w};
+            int pv[8];
+            if (kMask) {
+                const int4 pa = tp[q4], pbp = tp[q4 + 1];
+                pv[0] = pa.x; pv[1] = pa.y; pv[2] = pa.z; pv[3] = pa.w;
+                pv[4] = pbp.x; pv[5] = pbp.y; pv[6] = pbp.z; pv[7] = pbp.w;
+            }
+            uint32_t wp[4], wd[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                float pr[2], ds[2];
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    const int s = 2 * j + e;
+                    float x = fast_exp2(fmaf(sacc[8 * h + s], p.c, -lv[s]));
+                    if (kMask) x = (unsigned)(pv[s] - my_key) < Weff ? x : 0.0f;
+                    pr[e] = x;
+                    ds[e] = x * (dpacc[8 * h + s] - dv[s]);
+                }
+                wp[j] = pack_bf16x2(pr[0], pr[1]);
+                wd[j] = pack_bf16x2(ds[0], ds[1]);
+            }
+            const bf16x8 pb = __builtin_bit_cast(bf16x8, make_uint4(wp[0], wp[1], wp[2], wp[3]));
+            const bf16x8 dsb = __builtin_bit_cast(bf16x8, make_uint4(wd[0], wd[1], wd[2], wd[3]));
+            // dV^T += dO^T P and dK^T += Q^T dS over these 16 columns
+            const int r0 = 32 * mb + 16 * h + 8 * g;
+#pragma unroll
+            for (int db = 0; db < 2; ++db) {
+                const int cbase = 32 * db + 16 * (l32 >> 4);
+                dvacc[db] = mfma32(tile_read_tr8(to, r0, cbase, i16), pb, dvacc[db]);
+                dkacc[db] = mfma32(tile_read_tr8(tq, r0, cbase, i16), dsb, dkacc[db]);
+            }
         }
     };
 
@@ -232,64 +300,20 @@ bwd_dkdv_kernel(BwdParams p, int n_kt) {
         const bool has_next = st + 1 < n_steps;
         if (has_next) load_step(st + 1);
 
-        // positions of this step's columns
         const int c0 = st * kColsPerStep;
         const int tp_min = pos_lo + c0 / G;
         const int tp_max = min(pos_lo + (min(c0 + kColsPerStep, n_cols) - 1) / G, S - 1);
         const bool skip = !wave_active || tp_max < kw0 || (W > 0 && tp_min - kw1 >= W);
         if (!skip) {
             const bool need_mask = !(tp_min >= kw1 && (W == 0 || tp_max - kw0 < W));
-            const uint4* tq = sQ[buf];
-            const uint4* to = sO[buf];
-#pragma unroll
-            for (int mb = 0; mb < 2; ++mb) {
-                // S = Q K^T and dP = dO V^T for columns 32 mb .. 32 mb + 31
-                f32x16 sacc, dpacc;
-#pragma unroll
-                for (int r = 0; r < 16; ++r) sacc[r] = dpacc[r] = 0.0f;
-                const int arow = 32 * mb + perm_row(l32);
-#pragma unroll
-                for (int ks = 0; ks < 4; ++ks) {
-                    const bf16x8 qa = as_bf16x8(tq[tile_unit(arow, 2 * ks + g)]);
-                    const bf16x8 oa = as_bf16x8(to[tile_unit(arow, 2 * ks + g)]);
-                    sacc = mfma32(qa, kb[ks], sacc);
-                    dpacc = mfma32(oa, vb[ks], dpacc);
-                }
-                // P = exp2(s c - lse2), dS = P (dP - Dvec); register 8h + s holds
-                // column 32 mb + 16 h + 8 g + s
-                bf16x8 pb[2], dsb[2];
-#pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    bf16x8 pv, dv8;
-#pragma unroll
-                    for (int s = 0; s < 8; ++s) {
-                        const int col = 32 * mb + 16 * h + 8 * g + s;
-                        const float2 ldv = sLD[buf][col];
-                        float pr = fast_exp2(fmaf(sacc[8 * h + s], p.c, -ldv.x));
-                        if (need_mask) {
-                            const int pos = sPos[buf][col];
-                            const bool vis = my_key <= pos && (W == 0 || pos - my_key < W);
-                            pr = vis ? pr : 0.0f;
-                        }
-                        pv[s] = (__bf16)pr;
-                        dv8[s] = (__bf16)(pr * (dpacc[8 * h + s] - ldv.y));
-                    }
-                    pb[h] = pv;
-                    dsb[h] = dv8;
-                }
-                // dV^T += dO^T P and dK^T += Q^T dS  (contract over the 32 columns)
-#pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    const int r0 = 32 * mb + 16 * h + 8 * g;
-#pragma unroll
-                    for (int db = 0; db < 2; ++db) {
-                        const int cbase = 32 * db + 16 * (l32 >> 4);
-                        const bf16x8 oT = tile_read_tr8(to, r0, cbase, i16);
-                        const bf16x8 qT = tile_read_tr8(tq, r0, cbase, i16);
-                        dvacc[db] = mfma32(oT, pb[h], dvacc[db]);
-                        dkacc[db] = mfma32(qT, dsb[h], dkacc[db]);
-                    }
-                }
+            if (need_mask) {
+                block(sQ[buf], sO[buf], sL[buf], sD[buf], sP[buf], 0, std::true_type{});
+                __builtin_amdgcn_sched_barrier(0);  // keep the two blocks' live ranges apart
+                block(sQ[buf], sO[buf], sL[buf], sD[buf], sP[buf], 1, std::true_type{});
+            } else {
+                block(sQ[buf], sO[buf], sL[buf], sD[buf], sP[buf], 0, std::false_type{});
+                __builtin_amdgcn_sched_barrier(0);  // keep the two blocks' live ranges apart
+                block(sQ[buf], sO[buf], sL[buf], sD[buf], sP[buf], 1, std::false_type{});
             }
         }
 
@@ -345,6 +369,7 @@ bwd_dq_kernel(BwdParams p, int n_qt, int pos_per_block) {
     dq_coords(p, n_qt, blockIdx.x, grp, qt);
     const int b = grp / p.Hkv, kvh = grp % p.Hkv;
     const int S = p.S, W = p.window, G = p.G, Hq = p.Hq;
+    const unsigned Weff = W > 0 ? (unsigned)W : 0x7fffffffu;
     const int p0 = qt * pos_per_block;
     const int used_cols = pos_per_block * G;
     const int P1 = min(p0 + pos_per_block, S) - 1;
@@ -432,35 +457,46 @@ bwd_dq_kernel(BwdParams p, int n_qt, int pos_per_block) {
             const bool need_mask = !(kt0 + kBk - 1 <= wpmin && (W == 0 || wpmax - kt0 < W));
             const uint4* tk = sK[buf];
             const uint4* tv = sV[buf];
+            // S^T = K Q^T and dP^T = V dO^T (one column per lane; register
+            // 8h + s of key block mb = key kt0 + 32 mb + 16 h + 8 g + s), then
+            // P, dS and this row's sum_j P dP
             bf16x8 dsb[4];
+            auto keys = [&](auto masked) {
+                constexpr bool kMask = decltype(masked)::value;
+                const int dd = col_pos - kt0 - 8 * g;
 #pragma unroll
-            for (int mb = 0; mb < 2; ++mb) {
-                f32x16 sacc, dpacc;
+                for (int mb = 0; mb < 2; ++mb) {
+                    f32x16 sacc, dpacc;
 #pragma unroll
-                for (int r = 0; r < 16; ++r) sacc[r] = dpacc[r] = 0.0f;
-                const int arow = 32 * mb + perm_row(l32);
+                    for (int r = 0; r < 16; ++r) sacc[r] = dpacc[r] = 0.0f;
+                    const int arow = 32 * mb + perm_row(l32);
 #pragma unroll
-                for (int ks = 0; ks < 4; ++ks) {
-                    sacc = mfma32(as_bf16x8(tk[tile_unit(arow, 2 * ks + g)]), qf[ks], sacc);
-                    dpacc = mfma32(as_bf16x8(tv[tile_unit(arow, 2 * ks + g)]), of[ks], dpacc);
-                }
-#pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    bf16x8 d8;
-#pragma unroll
-                    for (int s = 0; s < 8; ++s) {
-                        float pr = fast_exp2(fmaf(sacc[8 * h + s], p.c, -lse2));
-                        if (need_mask) {
-                            const int key = kt0 + 32 * mb + 16 * h + 8 * g + s;
-                            const bool vis = key <= col_pos && (W == 0 || col_pos - key < W);
-                            pr = vis ? pr : 0.0f;
-                        }
-                        rsum = fmaf(pr, dpacc[8 * h + s], rsum);
-                        d8[s] = (__bf16)(pr * (dpacc[8 * h + s] - dvec));
+                    for (int ks = 0; ks < 4; ++ks) {
+                        sacc = mfma32(as_bf16x8(tk[tile_unit(arow, 2 * ks + g)]), qf[ks], sacc);
+                        dpacc = mfma32(as_bf16x8(tv[tile_unit(arow, 2 * ks + g)]), of[ks], dpacc);
                     }
-                    dsb[2 * mb + h] = d8;
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        uint32_t w[4];
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            float ds[2];
+#pragma unroll
+                            for (int e = 0; e < 2; ++e) {
+                                const int r = 8 * h + 2 * j + e;
+                                float pr = fast_exp2(fmaf(sacc[r], p.c, -lse2));
+                                if (kMask) pr = (unsigned)(dd - (32 * mb + 16 * h + 2 * j + e)) < Weff ? pr : 0.0f;
+                                rsum = fmaf(pr, dpacc[r], rsum);
+                                ds[e] = pr * (dpacc[r] - dvec);
+                            }
+                            w[j] = pack_bf16x2(ds[0], ds[1]);
+                        }
+                        dsb[2 * mb + h] = __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
+                    }
                 }
-            }
+            };
+            if (need_mask) keys(std::true_type{});
+            else keys(std::false_type{});
             // dQ^T += K^T dS^T over the 64 keys (16 per step)
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) {
@@ -480,7 +516,7 @@ bwd_dq_kernel(BwdParams p, int n_qt, int pos_per_block) {
         if (g == 0) {
             // this row's dsink term; the row's own Q/dO/lse were read above
             const float s2 = p.sinks[col_head] * kLog2e;
-            p.ld[((size_t)b * S + col_pos) * Hq + col_head].x = fast_exp2(s2 - lse2) * rsum;
+            p.dsterm[((size_t)col_head * p.B + b) * S + col_pos] = fast_exp2(s2 - lse2) * rsum;
         }
         uint16_t* row = p.dq + (((size_t)b * S + col_pos) * Hq + col_head) * kHeadDim;
 #pragma unroll
@@ -501,7 +537,7 @@ bwd_dq_kernel(BwdParams p, int n_qt, int pos_per_block) {
 size_t bwd_workspace_bytes(int B, int S, int Hq, int Hkv, int window) {
     (void)Hkv;
     (void)window;
-    return (size_t)B * S * Hq * sizeof(float2);
+    return (size_t)B * S * Hq * (sizeof(float2) + sizeof(float));
 }
 
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
@@ -518,6 +554,7 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
     p.dv = a.dv;
     p.dsinks = a.dsinks;
     p.ld = static_cast<float2*>(a.workspace);
+    p.dsterm = reinterpret_cast<float*>(p.ld + (size_t)a.B * a.S * a.Hq);
     p.B = a.B;
     p.S = a.S;
     p.Hq = a.Hq;
