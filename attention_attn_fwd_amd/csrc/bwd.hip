@@ -130,8 +130,8 @@ __device__ __forceinline__ void dkdv_coords(const BwdParams& p, int n_kt, int bi
 
 __global__ void __launch_bounds__(kThreads, 2)
 bwd_dkdv_kernel(BwdParams p, int n_kt) {
-    __shared__ uint4 sQ[2][512];
-    __shared__ uint4 sO[2][512];
+    __shared__ uint4 sQ[2][kTileUnits];
+    __shared__ uint4 sO[2][kTileUnits];
     __shared__ float4 sL[2][kColsPerStep / 4];  // lse * log2(e) per column
     __shared__ float4 sD[2][kColsPerStep / 4];  // Dvec per column
     __shared__ int4 sP[2][kColsPerStep / 4];    // position per column
@@ -360,8 +360,8 @@ __device__ __forceinline__ void dq_coords(const BwdParams& p, int n_qt, int bid,
 
 __global__ void __launch_bounds__(kThreads, 2)
 bwd_dq_kernel(BwdParams p, int n_qt, int pos_per_block) {
-    __shared__ uint4 sK[2][512];
-    __shared__ uint4 sV[2][512];
+    __shared__ uint4 sK[2][kTileUnits];
+    __shared__ uint4 sV[2][kTileUnits];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 5, l32 = lane & 31, i16 = lane & 15;

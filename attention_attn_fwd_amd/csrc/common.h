@@ -87,15 +87,17 @@ __device__ __forceinline__ constexpr int acc_row(int r, int g) { return 8 * (r >
 // K-slot order of a following MFMA that contracts over those rows.
 __device__ __forceinline__ int perm_row(int m) { return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1); }
 
-// LDS tiles of 64 rows x 64 bf16 are stored as 8 sixteen-byte units per row
-// with the unit index XOR-swizzled by the row.  gfx950 LDS has 64 four-byte
-// banks (256 bytes per cycle), i.e. 16 sixteen-byte units: a row pair (2r,
-// 2r+1) spans all 16, and XOR-ing the unit with (row >> 1) & 7 sends the 16
+// LDS tiles hold 64 rows x 64 bf16 with a row pitch of 144 bytes (9
+// sixteen-byte units: 8 of data, 1 of padding).  gfx950 LDS has 64 four-byte
+// banks; a 144-byte pitch puts consecutive rows 36 banks apart, so the 16
 // rows read by one 16-lane ds_read_b128 phase (any 16 consecutive rows, in
-// any order) and the 4 consecutive rows x 2 units of a transposing read to
-// distinct units.
-__device__ __forceinline__ int kswz(int row) { return (row >> 1) & 7; }
-__device__ __forceinline__ int tile_unit(int row, int unit) { return row * 8 + (unit ^ kswz(row)); }
+// any order) land on distinct 4-bank groups, and two rows 8 apart fall in
+// opposite bank halves.  Every address a lane uses is then its own base plus
+// a compile-time offset.
+constexpr int kTilePitch = 144;                 // bytes per row
+constexpr int kTilePitchUnits = kTilePitch / 16;
+constexpr int kTileUnits = 64 * kTilePitchUnits;  // uint4 per tile
+__device__ __forceinline__ int tile_unit(int row, int unit) { return row * kTilePitchUnits + unit; }
 
 // ds_read_b64_tr_b16: within each 16-lane block, lane i receives element
 // (i % 4) of the 8-byte chunk addressed by block lane 4 j + i / 4, for
@@ -108,16 +110,14 @@ __device__ __forceinline__ uint2 lds_read_tr16(const void* lds_ptr) {
     return __builtin_bit_cast(uint2, r);
 }
 
-// Transposed 8-slot operand from a swizzled row-major tile: lane (block
-// position i = lane % 16) receives tile[r0 + 0..7][c0 + i] where c0 is the
-// first column of its 16-lane block.  Rows r0..r0+3 come from the first
-// read, r0+4..r0+7 from the second.
+// Transposed 8-slot operand from a row-major tile: lane (block position
+// i = lane % 16) receives tile[r0 + 0..7][c0 + i] where c0 is the first
+// column of its 16-lane block.  Rows r0..r0+3 come from the first read,
+// r0+4..r0+7 from the second.
 __device__ __forceinline__ bf16x8 tile_read_tr8(const uint4* tile, int r0, int c0, int i) {
-    const int row_a = r0 + (i >> 2), row_b = row_a + 4;
-    const int col = c0 + 4 * (i & 3);
-    const char* base = reinterpret_cast<const char*>(tile);
-    const uint2 lo = lds_read_tr16(base + tile_unit(row_a, col >> 3) * 16 + ((col >> 2) & 1) * 8);
-    const uint2 hi = lds_read_tr16(base + tile_unit(row_b, col >> 3) * 16 + ((col >> 2) & 1) * 8);
+    const char* p = reinterpret_cast<const char*>(tile) + (r0 + (i >> 2)) * kTilePitch + (c0 + 4 * (i & 3)) * 2;
+    const uint2 lo = lds_read_tr16(p);
+    const uint2 hi = lds_read_tr16(p + 4 * kTilePitch);
     return __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
 }
 

@@ -13,7 +13,7 @@
 //   split kernel : grid (split, KV head x head block, sequence).  A split is
 //     256 visible keys; each of the 4 waves takes 64 of them.  A wave reads
 //     its K rows straight into MFMA A-operand registers, stages its V rows
-//     transposed in LDS, and computes S^T = K Q^T and O^T = V^T P^T with
+//     in LDS (read back transposed), and computes S^T = K Q^T and O^T = V^T P^T with
 //     32x32x16 bf16 MFMAs (columns = the query heads of the group).  The 4
 //     waves merge through LDS and the workgroup writes one partial
 //     (unnormalised O, running max m in log2 units, sum l) per head.  A
@@ -49,10 +49,6 @@ struct DecParams {
     float c;          // scale * log2(e)
 };
 
-// V^T tile rows are indexed by d and swizzled like the forward's tiles: a
-// 16-lane ds_read_b128 phase reads 16 consecutive d rows.
-__device__ __forceinline__ int vswz(int d) { return (d >> 1) & 7; }
-
 __device__ __forceinline__ void seq_range(const DecParams& p, int n, int& base, int& L, int& vis_lo) {
     base = p.cu[n];
     L = min(p.cu[n + 1] - base, p.max_seqlen);
@@ -61,8 +57,9 @@ __device__ __forceinline__ void seq_range(const DecParams& p, int n, int& base, 
 
 __global__ void __launch_bounds__(kThreads)
 decode_split_kernel(DecParams p) {
-    // per wave: V^T tile (64 d x 64 keys) = 512 units; reused for the merge
-    __shared__ uint4 vsm[kWaves][512];
+    // per wave: one row-major V tile (64 keys x 64 d, 144-byte rows); the
+    // space is reused for the cross-wave merge
+    __shared__ uint4 vsm[kWaves][kTileUnits];
     __shared__ float wm[kWaves][32], wl[kWaves][32];
 
     const int split = blockIdx.x;
@@ -92,7 +89,7 @@ decode_split_kernel(DecParams p) {
 
     // K A-operand rows (permuted as in the forward) and V rows for staging
     bf16x8 ka[2][4];
-    uint4 vr[4][2];
+    uint4 vr[8];
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
         const int key = t0 + 32 * mb + perm_row(l32);
@@ -104,17 +101,13 @@ decode_split_kernel(DecParams p) {
             ka[mb][ks] = as_bf16x8(x);
         }
     }
-    const int kp = lane & 31;  // key pair 2kp, 2kp+1
+    // V rows: lane loads 16-byte unit (lane % 8) of rows lane / 8 + 8 j
 #pragma unroll
-    for (int pass = 0; pass < 4; ++pass) {
-        const int dc = g + 2 * pass;  // d chunk of 8
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int key = t0 + 2 * kp + j;
-            uint4 x = make_uint4(0, 0, 0, 0);
-            if (wave_active && key < t_end) x = ld16(vb + key * row_stride + 8 * dc);
-            vr[pass][j] = x;
-        }
+    for (int j = 0; j < 8; ++j) {
+        const int key = t0 + (lane >> 3) + 8 * j;
+        uint4 x = make_uint4(0, 0, 0, 0);
+        if (wave_active && key < t_end) x = ld16(vb + key * row_stride + 8 * (lane & 7));
+        vr[j] = x;
     }
     bf16x8 qf[4];
     {
@@ -127,23 +120,9 @@ decode_split_kernel(DecParams p) {
         }
     }
 
-    // V^T into this wave's LDS tile
-    uint32_t* vs = reinterpret_cast<uint32_t*>(vsm[wave]);
+    // V into this wave's LDS tile (row-major; read transposed for P.V)
 #pragma unroll
-    for (int pass = 0; pass < 4; ++pass) {
-        const int dc = g + 2 * pass;
-        const uint32_t a[4] = {vr[pass][0].x, vr[pass][0].y, vr[pass][0].z, vr[pass][0].w};
-        const uint32_t c[4] = {vr[pass][1].x, vr[pass][1].y, vr[pass][1].z, vr[pass][1].w};
-        // the two half-waves store rows of opposite parity (disjoint banks)
-#pragma unroll
-        for (int s = 0; s < 8; ++s) {
-            const int e = s ^ g;
-            const int d = 8 * dc + e;
-            const uint32_t lo = (e & 1) ? (a[s >> 1] >> 16) : (a[s >> 1] & 0xffffu);
-            const uint32_t hi = (e & 1) ? (c[s >> 1] & 0xffff0000u) : (c[s >> 1] << 16);
-            vs[(d * 8 + ((kp >> 2) ^ vswz(d))) * 4 + (kp & 3)] = lo | hi;
-        }
-    }
+    for (int j = 0; j < 8; ++j) vsm[wave][tile_unit((lane >> 3) + 8 * j, lane & 7)] = vr[j];
 
     // S^T = K Q^T  (one 32-column block of heads)
     f32x16 sacc[2];
@@ -184,16 +163,16 @@ decode_split_kernel(DecParams p) {
         }
     lsum = sum_across_halves(lsum);
 
-    __syncthreads();  // V^T tiles written by every lane of each wave
+    __syncthreads();  // V tiles written by every lane of each wave
     f32x16 oacc[2];
 #pragma unroll
     for (int db = 0; db < 2; ++db) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[db][r] = 0.0f;
-        const int d = 32 * db + l32;
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
-            const bf16x8 a = as_bf16x8(vsm[wave][d * 8 + ((2 * kk + g) ^ vswz(d))]);
+            // V^T rows d = 32 db + l32, keys 16 kk + 8 g + 0..7
+            const bf16x8 a = tile_read_tr8(vsm[wave], 16 * kk + 8 * g, 32 * db + 16 * (l32 >> 4), l32 & 15);
             oacc[db] = mfma32(a, pb[kk], oacc[db]);
         }
     }
@@ -203,7 +182,7 @@ decode_split_kernel(DecParams p) {
         wm[wave][l32] = m;
         wl[wave][l32] = lsum;
     }
-    __syncthreads();  // all V^T reads done before the tiles are overwritten
+    __syncthreads();  // all V reads done before the tiles are overwritten
     float* ow = reinterpret_cast<float*>(vsm);  // 4 x 32 x 64 floats = 32 KB
     float msum = -INFINITY;
 #pragma unroll

@@ -17,8 +17,9 @@
 //   sharing) and the workgroup covers floor(256 / G) positions.
 //   Each wave owns 64 columns (two 32-column MFMA N-blocks).
 //   Key tiles of 64 rows are staged HBM -> LDS with 16-byte coalesced loads,
-//   double buffered: K row-major, V transposed (d-major) so that the P.V
-//   contraction over keys reads 8 consecutive keys per lane.
+//   double buffered, K and V both row-major (144-byte padded rows); the P.V
+//   contraction over keys reads V^T through transposing LDS reads
+//   (ds_read_b64_tr_b16), 8 consecutive keys per lane and MFMA slot group.
 //   Only tiles that intersect the causal/window band are visited; inside a
 //   wave, tiles fully outside its rows' band are skipped and tiles fully
 //   inside it skip the mask.
@@ -44,7 +45,6 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kCols = 256;        // columns per workgroup
 constexpr int kBk = 64;           // keys per LDS tile
-constexpr int kTileUnits = 512;   // 16-byte units per 64 x 64 bf16 tile
 
 struct FwdParams {
     const uint16_t* q;
@@ -60,10 +60,6 @@ struct FwdParams {
     float c;            // softmax scale * log2(e)
 };
 
-
-// V^T tile rows are indexed by d and swizzled like the K tile: a 16-lane
-// ds_read_b128 phase reads 16 consecutive d rows.
-__device__ __forceinline__ int vswz(int d) { return (d >> 1) & 7; }
 
 // Lazy rescaling bound: a tile's probabilities are exponentiated against the
 // running max m as long as every lane's tile sum stays below this bound
@@ -114,7 +110,7 @@ __device__ __forceinline__ void block_coords(const FwdParams& p, int bid, int& g
 
 __global__ void __launch_bounds__(kThreads, 2)
 fwd_kernel(FwdParams p) {
-    __shared__ uint4 smem[2][2][kTileUnits];  // [buffer][K | V^T][unit]
+    __shared__ uint4 smem[2][2][kTileUnits];  // [buffer][K | V][unit], both row-major
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -189,40 +185,27 @@ fwd_kernel(FwdParams p) {
     const size_t kv_row_stride = (size_t)p.Hkv * kHeadDim;
     const uint16_t* kbase = p.k + ((size_t)b * S * p.Hkv + kvh) * kHeadDim;
     const uint16_t* vbase = p.v + ((size_t)b * S * p.Hkv + kvh) * kHeadDim;
-    const int k_key0 = tid >> 3, k_unit = tid & 7;  // K: rows k_key0, k_key0 + 32
-    const int v_kp = tid & 31, v_dc = tid >> 5;      // V: rows 2kp, 2kp+1; d chunk
+    const int st_key = tid >> 3, st_unit = tid & 7;  // rows st_key, st_key + 32; 16-byte unit
     uint4 kreg[2], vreg[2];
 
     auto load_tile = [&](int t) {
         const int kt0 = t * kBk;
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-            const int key = kt0 + k_key0 + 32 * j;
-            kreg[j] = key < S ? ld16(kbase + key * kv_row_stride + 8 * k_unit) : make_uint4(0, 0, 0, 0);
-            const int vkey = kt0 + 2 * v_kp + j;
-            vreg[j] = vkey < S ? ld16(vbase + vkey * kv_row_stride + 8 * v_dc) : make_uint4(0, 0, 0, 0);
+            const int key = kt0 + st_key + 32 * j;
+            kreg[j] = make_uint4(0, 0, 0, 0);
+            vreg[j] = make_uint4(0, 0, 0, 0);
+            if (key < S) {
+                kreg[j] = ld16(kbase + key * kv_row_stride + 8 * st_unit);
+                vreg[j] = ld16(vbase + key * kv_row_stride + 8 * st_unit);
+            }
         }
     };
     auto store_tile = [&](int buf) {
-        uint4* ks = smem[buf][0];
-        uint32_t* vs = reinterpret_cast<uint32_t*>(smem[buf][1]);
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-            const int key = k_key0 + 32 * j;
-            ks[tile_unit(key, k_unit)] = kreg[j];
-        }
-        const uint32_t a[4] = {vreg[0].x, vreg[0].y, vreg[0].z, vreg[0].w};
-        const uint32_t c[4] = {vreg[1].x, vreg[1].y, vreg[1].z, vreg[1].w};
-        // lanes 32..63 (odd d chunk) walk the rows in the order s ^ 1 so the
-        // two half-waves of each store hit rows of opposite parity (disjoint banks)
-        const int flip = v_dc & 1;
-#pragma unroll
-        for (int s = 0; s < 8; ++s) {
-            const int e = s ^ flip;
-            const int d = 8 * v_dc + e;
-            const uint32_t lo = (e & 1) ? (a[s >> 1] >> 16) : (a[s >> 1] & 0xffffu);
-            const uint32_t hi = (e & 1) ? (c[s >> 1] & 0xffff0000u) : (c[s >> 1] << 16);
-            vs[(d * 8 + ((v_kp >> 2) ^ vswz(d))) * 4 + (v_kp & 3)] = lo | hi;
+            smem[buf][0][tile_unit(st_key + 32 * j, st_unit)] = kreg[j];
+            smem[buf][1][tile_unit(st_key + 32 * j, st_unit)] = vreg[j];
         }
     };
 
@@ -349,8 +332,8 @@ fwd_kernel(FwdParams p) {
             for (int kk = 0; kk < 4; ++kk) {
 #pragma unroll
                 for (int db = 0; db < 2; ++db) {
-                    const int d = 32 * db + l32;
-                    const bf16x8 a = as_bf16x8(vs[d * 8 + ((2 * kk + g) ^ vswz(d))]);
+                    // V^T rows d = 32 db + l32, keys 16 kk + 8 g + 0..7 (transposing read)
+                    const bf16x8 a = tile_read_tr8(vs, 16 * kk + 8 * g, 32 * db + 16 * (l32 >> 4), l32 & 15);
 #pragma unroll
                     for (int nb = 0; nb < 2; ++nb) oacc[db][nb] = mfma32(a, pb[kk][nb], oacc[db][nb]);
                 }

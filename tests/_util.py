@@ -1,5 +1,7 @@
 """Shared helpers of the test suite (comparison bars, device plumbing)."""
 
+import zlib
+
 import numpy as np
 import pytest
 import torch
@@ -43,3 +45,9 @@ def check_out_lse(out, lse, ref_out, ref_lse, what=""):
 def rel_l2(x, ref):
     x, ref = np.asarray(x, dtype=np.float64), np.asarray(ref, dtype=np.float64)
     return float(np.linalg.norm(x - ref) / max(np.linalg.norm(ref), 1e-300))
+
+
+def seed_of(*parts):
+    """Deterministic seed for a test case (Python's hash() of a str is salted
+    per process)."""
+    return zlib.crc32(repr(parts).encode()) % 100000

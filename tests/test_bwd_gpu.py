@@ -11,7 +11,7 @@ import attention_attn_fwd_amd as attn
 from attention_attn_fwd_amd import synth
 from oracle import ref_bwd
 
-from _util import GRAD_REL_L2, f64, need_gpu, rel_l2
+from _util import seed_of, GRAD_REL_L2, f64, need_gpu, rel_l2
 
 pytestmark = pytest.mark.gpu
 
@@ -46,8 +46,9 @@ def _oracle(case, dout, window, **kw):
     return ref_bwd(f64(case.q), f64(case.k), f64(case.v), f64(case.sinks), f64(dout), window, case.scale, **kw)
 
 
-SMALL = [  # B, S, Hq, Hkv
-    (1, 1, 8, 1), (1, 17, 8, 1), (2, 129, 8, 1), (1, 300, 8, 8), (1, 700, 8, 1), (2, 77, 16, 2),
+SMALL = [  # B, S, Hq, Hkv  (S = 1 over 4 batches: one key per head makes a single
+           # batch's relative L2 hinge on one possibly cancelling dS sum)
+    (4, 1, 8, 1), (1, 17, 8, 1), (2, 129, 8, 1), (1, 300, 8, 8), (1, 700, 8, 1), (2, 77, 16, 2),
     (1, 200, 6, 2), (1, 333, 1, 1), (1, 260, 4, 4),
 ]
 
@@ -57,7 +58,7 @@ SMALL = [  # B, S, Hq, Hkv
 def test_bwd_small_shapes(shape, window):
     dev = need_gpu()
     B, S, Hq, Hkv = shape
-    case = synth.make_prefill(B, S, Hq, Hkv, seed=hash((shape, window, "bwd")) % 10000)
+    case = synth.make_prefill(B, S, Hq, Hkv, seed=seed_of(shape, window, "bwd"))
     dout = synth.make_dout(tuple(case.q.shape), seed=S + window)
     print(f"bwd shape={shape} window={window}", flush=True)
     grads = _run(case, dout, window, dev)

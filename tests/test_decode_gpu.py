@@ -8,7 +8,7 @@ import attention_attn_fwd_amd as attn
 from attention_attn_fwd_amd import synth
 from oracle import ref_decode
 
-from _util import check_out_lse, f64, need_gpu
+from _util import seed_of, check_out_lse, f64, need_gpu
 
 pytestmark = pytest.mark.gpu
 

@@ -16,6 +16,7 @@ import json
 import math
 import os
 import operator
+import zlib
 
 import numpy as np
 import pytest
@@ -133,7 +134,7 @@ BRUTE_SHAPES = [  # B, S, Hq, Hkv, D
 @pytest.mark.parametrize("sink_kind", ["normal", "neg_inf", "large"])
 def test_matches_brute_force(shape, window, sink_kind):
     B, S, Hq, Hkv, D = shape
-    rng = np.random.default_rng(hash((shape, window, sink_kind)) % 2**32)
+    rng = np.random.default_rng(zlib.crc32(repr((shape, window, sink_kind)).encode()))
     q, k, v, sinks = _case(rng, B, S, Hq, Hkv, D, std=0.7)
     if sink_kind == "neg_inf":
         sinks[:] = -np.inf
