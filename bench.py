@@ -25,6 +25,36 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2516.6      # MI355X dense bf16 MFMA (256 CU x 2.4 GHz x 4096 FLOP/clk)
 D = 64
 WINDOWS = (128, 0)             # sliding layer, full-causal layer
+COPY_BYTES = 1 << 30           # calibration copy for the HBM byte counters
+ROOT = os.path.dirname(os.path.abspath(__file__))
+
+
+def source_digest():
+    """sha256 over the library sources; measured traffic is only reported
+    while it matches the digest recorded with the counters."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "attention_attn_fwd_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(key):
+    """HBM bytes per launch of `key` from profiles/traffic.json (FETCH_SIZE +
+    WRITE_SIZE, calibrated against a plain copy), or None if absent or taken
+    on different kernel sources."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_sha256") != source_digest():
+        return None
+    v = t.get("bytes_per_launch", {}).get(key)
+    return None if v is None else float(v)
 
 
 def pairs_per_head(S, W):
@@ -40,8 +70,11 @@ def parse():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["fwd", "bwd", "decode"], default=None,
-                    help="run only this part in a loop (for profiling); prints no JSON line")
+    ap.add_argument("--only", choices=["fwd", "bwd", "decode", "copy"], default=None,
+                    help="run only this part in a loop (for profiling); prints no JSON line.  'copy' "
+                         "copies 1 GiB once per step, to calibrate HBM byte counters")
+    ap.add_argument("--window", type=int, default=None, choices=list(WINDOWS),
+                    help="with --only: run that part for this layer's window only")
     ap.add_argument("--verbose", action="store_true")
     return ap.parse_args()
 
@@ -60,6 +93,15 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     log = (lambda *a: print(*a, file=sys.stderr, flush=True)) if args.verbose else (lambda *a: None)
+
+    if args.only == "copy":
+        src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(args.warmup + args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"done: copy of {COPY_BYTES} bytes x {args.warmup + args.steps}", flush=True)
+        return
 
     # ---- inputs (seeded, synthetic, gpt-oss shaped), resident in HBM
     case, dout_cpu = synth.config_inputs("c3_bwd_b4_s4096_h64x8")
@@ -102,8 +144,12 @@ def main():
 
     if args.only:
         fn = {"fwd": fwd, "bwd": bwd, "decode": decode}[args.only]
+        wins = WINDOWS if args.window is None else (args.window,)
+        if args.only == "bwd":
+            for w in wins:
+                fwd(w)  # the backward consumes this layer's forward out/lse
         for _ in range(args.warmup + args.steps):
-            for w in WINDOWS:
+            for w in wins:
                 fn(w)
         torch.cuda.synchronize()
         print(f"done: {args.only} x {args.warmup + args.steps} per layer", flush=True)
@@ -167,11 +213,26 @@ def main():
             "frac_of_roof": round(tf / roof_tf, 4)}
     log(json.dumps(parts, indent=1))
 
-    # dominant kernel: the single-launch forward of the full-causal layer
-    ms_f = part_ms[("fwd", 0)]
-    ach = flops[("fwd", 0)] / (ms_f * 1e-3) / 1e12
+    # Dominant unit of the step: the backward entry point of the full-causal
+    # layer (4 launches: pre, dkdv, dq, dsink; dkdv is the largest).  Events
+    # bracket the call on the stream its kernels run on; achieved uses the
+    # algorithmic 10*D FLOPs per visible pair.
+    ms_b = part_ms[("bwd", 0)]
+    ach = flops[("bwd", 0)] / (ms_b * 1e-3) / 1e12
+    tb = measured_traffic("bwd_full")
     roofline = {"bound": "mfma", "achieved": round(ach, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(ach / BF16_PEAK_TFLOPS, 4), "traffic": None, "kernel": "fwd_kernel (full causal)"}
+                "frac": round(ach / BF16_PEAK_TFLOPS, 4), "traffic": tb,
+                "kernel": "gptoss_attn_bwd, full-causal layer (bwd_pre + bwd_dkdv + bwd_dq + bwd_dsink)",
+                "ms_per_launch": round(ms_b, 4)}
+    ach_f = flops[("fwd", 0)] / (part_ms[("fwd", 0)] * 1e-3) / 1e12
+    roofline_fwd = {"bound": "mfma", "achieved": round(ach_f, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(ach_f / BF16_PEAK_TFLOPS, 4), "traffic": measured_traffic("fwd_full"),
+                    "kernel": "fwd_kernel, full-causal layer", "ms_per_launch": round(part_ms[("fwd", 0)], 4)}
+    ms_d = part_ms[("decode", 0)]
+    gbs_d = bytes_[("decode", 0)] / (ms_d * 1e-3) / 1e9
+    roofline_decode = {"bound": "hbm", "achieved": round(gbs_d, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                       "frac": round(gbs_d / HBM_PEAK_GBS, 4), "traffic": measured_traffic("decode_full"),
+                       "kernel": "gptoss_attn_decode, full layer (split + merge)", "ms_per_launch": round(ms_d, 4)}
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -189,6 +250,8 @@ def main():
                        for w in WINDOWS},
         "parts": parts,
         "roofline": roofline,
+        "roofline_fwd": roofline_fwd,
+        "roofline_decode": roofline_decode,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
@@ -196,8 +259,8 @@ def main():
 
 def cpu_baseline(case, dout_cpu):
     """The fp64 oracle timed on this host on a bounded sample of the same step:
-    forward + backward of KV group 0 (query heads 0..7) of batch 0 at the full
-    S = 4096, for both layers.  Reported in the metric's unit over that
+    forward + backward of KV groups 0..3 (query heads 0..31) of batch 0 at the
+    full S = 4096, for both layers.  Reported in the metric's unit over that
     sample's unmasked FLOPs."""
     from oracle import ref_bwd, ref_fwd
 
@@ -215,7 +278,7 @@ def cpu_baseline(case, dout_cpu):
     v = f64(case.v[:1])
     s = f64(case.sinks)
     do = f64(dout_cpu[:1])
-    heads = list(range(8))
+    heads = list(range(32))
     S = q.shape[1]
     t = time.perf_counter()
     fl = 0
@@ -225,7 +288,7 @@ def cpu_baseline(case, dout_cpu):
         fl += (4 + 10) * D * len(heads) * pairs_per_head(S, w)
     el = time.perf_counter() - t
     return {"value": round(fl / el / 1e12, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "sample": "fp64 oracle fwd+bwd of batch 0, query heads 0-7 (KV group 0), S=4096, both layers "
+            "sample": "fp64 oracle fwd+bwd of batch 0, query heads 0-31 (KV groups 0-3), S=4096, both layers "
                       f"({el:.1f} s); decode not included"}
 
 
