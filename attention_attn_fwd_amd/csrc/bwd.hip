@@ -35,7 +35,6 @@
 #include "common.h"
 #include "launch.h"
 
-#include <type_traits>
 
 namespace gptoss {
 namespace {
@@ -91,15 +90,26 @@ bwd_pre_kernel(BwdParams p, long long rows) {
     }
 }
 
-// dsink: one workgroup per head sums the rows' exp(sink - lse) r terms.
+// dsink: one workgroup per head sums the rows' exp(sink - lse) r terms
+// (contiguous per head; 16-byte loads, four independent partial sums).
 __global__ void __launch_bounds__(kThreads)
 bwd_dsink_kernel(BwdParams p) {
     __shared__ float red[kThreads / 64];
     const int h = blockIdx.x;
     const long long n = (long long)p.B * p.S;
-    float acc = 0.0f;
     const float* src = p.dsterm + (size_t)h * n;
-    for (long long i = threadIdx.x; i < n; i += kThreads) acc += src[i];
+    float a0 = 0.0f, a1 = 0.0f, a2 = 0.0f, a3 = 0.0f;
+    const long long n4 = ((size_t)h * n) % 4 == 0 ? n / 4 : 0;  // float4 part (rows start 16-byte aligned)
+    const float4* src4 = reinterpret_cast<const float4*>(src);
+    for (long long i = threadIdx.x; i < n4; i += kThreads) {
+        const float4 v = src4[i];
+        a0 += v.x;
+        a1 += v.y;
+        a2 += v.z;
+        a3 += v.w;
+    }
+    for (long long i = 4 * n4 + threadIdx.x; i < n; i += kThreads) a0 += src[i];
+    float acc = (a0 + a1) + (a2 + a3);
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = acc;
@@ -192,6 +202,15 @@ bwd_dkdv_kernel(BwdParams p, int n_kt) {
     uint4 rq[2], ro[2];
     float2 rld = make_float2(INFINITY, 0.0f);
     int rpos = 0x3fffffff;
+    // per-thread column offsets within a step (constant across steps when G divides 64)
+    int st_pos[2], st_head[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        st_pos[j] = (st_row + 32 * j) / G;
+        st_head[j] = (st_row + 32 * j) % G;
+    }
+    const int ld_pos = tid / G, ld_head = tid % G;
+    const int pos_per_step = kColsPerStep / G;
     auto load_step = [&](int st) {
         const int c0 = st * kColsPerStep;
 #pragma unroll
@@ -200,9 +219,9 @@ bwd_dkdv_kernel(BwdParams p, int n_kt) {
             rq[j] = make_uint4(0, 0, 0, 0);
             ro[j] = make_uint4(0, 0, 0, 0);
             if (c < n_cols) {
-                const int cq = g64 ? (st_row + 32 * j) : c;
-                const int pos = pos_lo + (g64 ? st * (kColsPerStep / G) + cq / G : cq / G);
-                const size_t off = (size_t)pos * pos_stride + (size_t)(cq % G) * kHeadDim;
+                const int pos = pos_lo + (g64 ? st * pos_per_step + st_pos[j] : c / G);
+                const int head = g64 ? st_head[j] : c % G;
+                const size_t off = (size_t)pos * pos_stride + (size_t)head * kHeadDim;
                 rq[j] = ld16(qcol_base + off);
                 ro[j] = ld16(ocol_base + off);
             }
@@ -212,9 +231,8 @@ bwd_dkdv_kernel(BwdParams p, int n_kt) {
             rld = make_float2(INFINITY, 0.0f);
             rpos = 0x3fffffff;
             if (c < n_cols) {
-                const int cq = g64 ? tid : c;
-                const int pos = pos_lo + (g64 ? st * (kColsPerStep / G) + cq / G : cq / G);
-                rld = ld_base[(size_t)pos * Hq + cq % G];
+                const int pos = pos_lo + (g64 ? st * pos_per_step + ld_pos : c / G);
+                rld = ld_base[(size_t)pos * Hq + (g64 ? ld_head : c % G)];
                 rpos = pos;
             }
         }
@@ -234,11 +252,11 @@ bwd_dkdv_kernel(BwdParams p, int n_kt) {
     };
 
     // One 32-column block: S = Q K^T and dP = dO V^T (one key per lane,
-    // register 8h + s = column 32 mb + 16 h + 8 g + s), P and dS, then
-    // dV^T += dO^T P and dK^T += Q^T dS over those 32 columns.
+    // register 8h + s = column 32 mb + 16 h + 8 g + s); on edge steps the
+    // invisible scores are set to -inf (so P = dS = 0); then P and dS, and
+    // dV^T += dO^T P, dK^T += Q^T dS over those 32 columns.
     auto block = [&](const uint4* tq, const uint4* to, const float4* tl, const float4* td, const int4* tp, int mb,
-                     auto masked) {
-        constexpr bool kMask = decltype(masked)::value;
+                     bool need_mask) {
         f32x16 sacc, dpacc;
 #pragma unroll
         for (int r = 0; r < 16; ++r) sacc[r] = dpacc[r] = 0.0f;
@@ -248,6 +266,17 @@ bwd_dkdv_kernel(BwdParams p, int n_kt) {
             sacc = mfma32(as_bf16x8(tq[tile_unit(arow, 2 * ks + g)]), kb[ks], sacc);
             dpacc = mfma32(as_bf16x8(to[tile_unit(arow, 2 * ks + g)]), vb[ks], dpacc);
         }
+        if (need_mask) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int q4 = (32 * mb + 16 * h + 8 * g) >> 2;
+                const int4 pa = tp[q4], pbp = tp[q4 + 1];
+                const int pv[8] = {pa.x, pa.y, pa.z, pa.w, pbp.x, pbp.y, pbp.z, pbp.w};
+#pragma unroll
+                for (int s = 0; s < 8; ++s)
+                    sacc[8 * h + s] = (unsigned)(pv[s] - my_key) < Weff ? sacc[8 * h + s] : -INFINITY;
+            }
+        }
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const int q4 = (32 * mb + 16 * h + 8 * g) >> 2;  // float4 index of the 8 columns
@@ -255,12 +284,6 @@ bwd_dkdv_kernel(BwdParams p, int n_kt) {
             const float4 da = td[q4], dbv = td[q4 + 1];
             const float lv[8] = {la.x, la.y, la.z, la.w, lb.x, lb.y, lb.z, lb.w};
             const float dv[8] = {da.x, da.y, da.z, da.w, dbv.x, dbv.y, dbv.z, dbv.w};
-            int pv[8];
-            if (kMask) {
-                const int4 pa = tp[q4], pbp = tp[q4 + 1];
-                pv[0] = pa.x; pv[1] = pa.y; pv[2] = pa.z; pv[3] = pa.w;
-                pv[4] = pbp.x; pv[5] = pbp.y; pv[6] = pbp.z; pv[7] = pbp.w;
-            }
             uint32_t wp[4], wd[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
@@ -268,10 +291,8 @@ bwd_dkdv_kernel(BwdParams p, int n_kt) {
 #pragma unroll
                 for (int e = 0; e < 2; ++e) {
                     const int s = 2 * j + e;
-                    float x = fast_exp2(fmaf(sacc[8 * h + s], p.c, -lv[s]));
-                    if (kMask) x = (unsigned)(pv[s] - my_key) < Weff ? x : 0.0f;
-                    pr[e] = x;
-                    ds[e] = x * (dpacc[8 * h + s] - dv[s]);
+                    pr[e] = fast_exp2(fmaf(sacc[8 * h + s], p.c, -lv[s]));
+                    ds[e] = pr[e] * (dpacc[8 * h + s] - dv[s]);
                 }
                 wp[j] = pack_bf16x2(pr[0], pr[1]);
                 wd[j] = pack_bf16x2(ds[0], ds[1]);
@@ -289,16 +310,21 @@ bwd_dkdv_kernel(BwdParams p, int n_kt) {
         }
     };
 
+    // Steps run from the last columns down: the workgroups of one KV group
+    // (dispatched together on one XCD) all start at the sequence end and move
+    // down in near lockstep, so each Q/dO tile comes from HBM once and from
+    // L2 for the others.
     if (n_steps > 0) {
-        load_step(0);
+        load_step(n_steps - 1);
         store_step(0);
     }
     __syncthreads();
 
-    for (int st = 0; st < n_steps; ++st) {
-        const int buf = st & 1;
-        const bool has_next = st + 1 < n_steps;
-        if (has_next) load_step(st + 1);
+    for (int it = 0; it < n_steps; ++it) {
+        const int st = n_steps - 1 - it;
+        const int buf = it & 1;
+        const bool has_next = st > 0;
+        if (has_next) load_step(st - 1);
 
         const int c0 = st * kColsPerStep;
         const int tp_min = pos_lo + c0 / G;
@@ -306,15 +332,9 @@ bwd_dkdv_kernel(BwdParams p, int n_kt) {
         const bool skip = !wave_active || tp_max < kw0 || (W > 0 && tp_min - kw1 >= W);
         if (!skip) {
             const bool need_mask = !(tp_min >= kw1 && (W == 0 || tp_max - kw0 < W));
-            if (need_mask) {
-                block(sQ[buf], sO[buf], sL[buf], sD[buf], sP[buf], 0, std::true_type{});
-                __builtin_amdgcn_sched_barrier(0);  // keep the two blocks' live ranges apart
-                block(sQ[buf], sO[buf], sL[buf], sD[buf], sP[buf], 1, std::true_type{});
-            } else {
-                block(sQ[buf], sO[buf], sL[buf], sD[buf], sP[buf], 0, std::false_type{});
-                __builtin_amdgcn_sched_barrier(0);  // keep the two blocks' live ranges apart
-                block(sQ[buf], sO[buf], sL[buf], sD[buf], sP[buf], 1, std::false_type{});
-            }
+            block(sQ[buf], sO[buf], sL[buf], sD[buf], sP[buf], 0, need_mask);
+            __builtin_amdgcn_sched_barrier(0);  // keep the two blocks' live ranges apart
+            block(sQ[buf], sO[buf], sL[buf], sD[buf], sP[buf], 1, need_mask);
         }
 
         if (has_next) store_step(buf ^ 1);
@@ -458,45 +478,47 @@ bwd_dq_kernel(BwdParams p, int n_qt, int pos_per_block) {
             const uint4* tk = sK[buf];
             const uint4* tv = sV[buf];
             // S^T = K Q^T and dP^T = V dO^T (one column per lane; register
-            // 8h + s of key block mb = key kt0 + 32 mb + 16 h + 8 g + s), then
-            // P, dS and this row's sum_j P dP
+            // 8h + s of key block mb = key kt0 + 32 mb + 16 h + 8 g + s); on edge
+            // tiles invisible scores become -inf (P = dS = 0); then P, dS and
+            // this row's sum_j P dP
             bf16x8 dsb[4];
-            auto keys = [&](auto masked) {
-                constexpr bool kMask = decltype(masked)::value;
-                const int dd = col_pos - kt0 - 8 * g;
+            const int dd = col_pos - kt0 - 8 * g;
 #pragma unroll
-                for (int mb = 0; mb < 2; ++mb) {
-                    f32x16 sacc, dpacc;
+            for (int mb = 0; mb < 2; ++mb) {
+                f32x16 sacc, dpacc;
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) sacc[r] = dpacc[r] = 0.0f;
-                    const int arow = 32 * mb + perm_row(l32);
+                for (int r = 0; r < 16; ++r) sacc[r] = dpacc[r] = 0.0f;
+                const int arow = 32 * mb + perm_row(l32);
 #pragma unroll
-                    for (int ks = 0; ks < 4; ++ks) {
-                        sacc = mfma32(as_bf16x8(tk[tile_unit(arow, 2 * ks + g)]), qf[ks], sacc);
-                        dpacc = mfma32(as_bf16x8(tv[tile_unit(arow, 2 * ks + g)]), of[ks], dpacc);
-                    }
+                for (int ks = 0; ks < 4; ++ks) {
+                    sacc = mfma32(as_bf16x8(tk[tile_unit(arow, 2 * ks + g)]), qf[ks], sacc);
+                    dpacc = mfma32(as_bf16x8(tv[tile_unit(arow, 2 * ks + g)]), of[ks], dpacc);
+                }
+                if (need_mask) {
 #pragma unroll
-                    for (int h = 0; h < 2; ++h) {
-                        uint32_t w[4];
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) {
-                            float ds[2];
-#pragma unroll
-                            for (int e = 0; e < 2; ++e) {
-                                const int r = 8 * h + 2 * j + e;
-                                float pr = fast_exp2(fmaf(sacc[r], p.c, -lse2));
-                                if (kMask) pr = (unsigned)(dd - (32 * mb + 16 * h + 2 * j + e)) < Weff ? pr : 0.0f;
-                                rsum = fmaf(pr, dpacc[r], rsum);
-                                ds[e] = pr * (dpacc[r] - dvec);
-                            }
-                            w[j] = pack_bf16x2(ds[0], ds[1]);
-                        }
-                        dsb[2 * mb + h] = __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
+                    for (int r = 0; r < 16; ++r) {
+                        const int cr = 32 * mb + 16 * (r >> 3) + (r & 7);
+                        sacc[r] = (unsigned)(dd - cr) < Weff ? sacc[r] : -INFINITY;
                     }
                 }
-            };
-            if (need_mask) keys(std::true_type{});
-            else keys(std::false_type{});
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    uint32_t w[4];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        float ds[2];
+#pragma unroll
+                        for (int e = 0; e < 2; ++e) {
+                            const int r = 8 * h + 2 * j + e;
+                            const float pr = fast_exp2(fmaf(sacc[r], p.c, -lse2));
+                            rsum = fmaf(pr, dpacc[r], rsum);
+                            ds[e] = pr * (dpacc[r] - dvec);
+                        }
+                        w[j] = pack_bf16x2(ds[0], ds[1]);
+                    }
+                    dsb[2 * mb + h] = __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
+                }
+            }
             // dQ^T += K^T dS^T over the 64 keys (16 per step)
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) {
@@ -534,10 +556,16 @@ bwd_dq_kernel(BwdParams p, int n_qt, int pos_per_block) {
 
 }  // namespace
 
+// Workspace: {lse * log2(e), Dvec} per row, then (256-byte aligned) one
+// dsink term per row.
+static size_t ld_region_bytes(int B, int S, int Hq) {
+    return ((size_t)B * S * Hq * sizeof(float2) + 255) / 256 * 256;
+}
+
 size_t bwd_workspace_bytes(int B, int S, int Hq, int Hkv, int window) {
     (void)Hkv;
     (void)window;
-    return (size_t)B * S * Hq * (sizeof(float2) + sizeof(float));
+    return ld_region_bytes(B, S, Hq) + (size_t)B * S * Hq * sizeof(float);
 }
 
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
@@ -554,7 +582,7 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
     p.dv = a.dv;
     p.dsinks = a.dsinks;
     p.ld = static_cast<float2*>(a.workspace);
-    p.dsterm = reinterpret_cast<float*>(p.ld + (size_t)a.B * a.S * a.Hq);
+    p.dsterm = reinterpret_cast<float*>(static_cast<char*>(a.workspace) + ld_region_bytes(a.B, a.S, a.Hq));
     p.B = a.B;
     p.S = a.S;
     p.Hq = a.Hq;
