@@ -71,8 +71,9 @@ def bwd_workspace_size(B, S, Hq, Hkv, D=64, window=0):
     return int(_lib.load().gptoss_attn_bwd_workspace_size(B, S, Hq, Hkv, D, int(window)))
 
 
-def bwd(q, k, v, sinks, out, lse, dout, window=0, scale=None, workspace=None):
-    """Backward of sum(dout * out).  Returns (dq, dk, dv bf16, dsinks fp32 [Hq])."""
+def bwd(q, k, v, sinks, out, lse, dout, window=0, scale=None, workspace=None, grads=None):
+    """Backward of sum(dout * out).  Returns (dq, dk, dv bf16, dsinks fp32 [Hq]),
+    written into `grads` = (dq, dk, dv, dsinks) when given."""
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (out, "out"), (dout, "dout")):
         _need(t, n, torch.bfloat16, 4)
     _need(sinks, "sinks", torch.float32, 1)
@@ -83,8 +84,18 @@ def bwd(q, k, v, sinks, out, lse, dout, window=0, scale=None, workspace=None):
             or lse.shape != (B, Hq, S) or sinks.shape != (Hq,)):
         raise ValueError("shape mismatch among backward inputs")
     scale = (1.0 / D ** 0.5) if scale is None else float(scale)
-    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    dsinks = torch.empty((Hq,), dtype=torch.float32, device=q.device)
+    if grads is None:
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        dsinks = torch.empty((Hq,), dtype=torch.float32, device=q.device)
+    else:
+        dq, dk, dv, dsinks = grads
+        for t, n, ref in ((dq, "dq", q), (dk, "dk", k), (dv, "dv", v)):
+            _need(t, n, torch.bfloat16, 4)
+            if t.shape != ref.shape:
+                raise ValueError(f"{n} must have shape {tuple(ref.shape)}")
+        _need(dsinks, "dsinks", torch.float32, 1)
+        if dsinks.shape != (Hq,):
+            raise ValueError(f"dsinks must have shape ({Hq},)")
     need = bwd_workspace_size(B, S, Hq, Hkv, D, window)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)

@@ -10,16 +10,20 @@
 //
 // The work is memory bound: every K/V byte is read once and serves all G
 // query heads of its KV head.
-//   split kernel : grid (split, KV head x head block, sequence).  A split is
-//     256 visible keys; each of the 4 waves takes 64 of them.  A wave reads
-//     its K rows straight into MFMA A-operand registers, stages its V rows
-//     in LDS (read back transposed), and computes S^T = K Q^T and O^T = V^T P^T with
-//     32x32x16 bf16 MFMAs (columns = the query heads of the group).  The 4
-//     waves merge through LDS and the workgroup writes one partial
-//     (unnormalised O, running max m in log2 units, sum l) per head.  A
-//     sequence that fits in one split is finished in place (sink folded in,
-//     out and lse written) and never touches the partial buffer.
-//   merge kernel : one wave per (sequence, head) with more than one split:
+//   split kernel : grid (chunk of visible keys, group of 4 KV heads x head
+//     block, sequence); chunks are only cut when too few (sequence, group)
+//     pairs would fill the chip.  Each wave owns one KV head, so the 4 waves of a
+//     workgroup stream adjacent 128-byte rows of the same tokens (512
+//     contiguous bytes per token for K and again for V).  A wave walks its
+//     chunk in 64-key tiles: K rows go straight into MFMA A-operand
+//     registers, V rows into a wave-private LDS tile (read back transposed),
+//     S^T = K Q^T and O^T = V^T P^T on 32x32x16 bf16 MFMAs with the G query
+//     heads as columns, an online softmax across tiles, and the next tile's
+//     loads in flight while the current one is computed.  Waves never
+//     synchronise.  A sequence that fits in one chunk is finished in place
+//     (sink folded in, out and lse written); otherwise the wave writes one
+//     partial (unnormalised O, running max m in log2 units, sum l) per head.
+//   merge kernel : one workgroup per (sequence, head) with more than one chunk:
 //     m = max(sink, m_s), l = 2^(sink - m) + sum l_s 2^(m_s - m),
 //     out = sum O_s 2^(m_s - m) / l, lse = ln2 (m + log2 l).  The sink enters
 //     here exactly once.
@@ -32,9 +36,12 @@ namespace gptoss {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kWaves = 4;
-constexpr int kSplitKeys = 256;   // visible keys per split (64 per wave)
+constexpr int kWaves = 4;         // KV heads per workgroup, one per wave
+constexpr int kTileKeys = 64;     // keys per wave step
 constexpr int kPartStride = 68;   // floats per partial: O[64], m, l, pad
+#ifndef GPTOSS_DECODE_PAR2_KEYS
+#define GPTOSS_DECODE_PAR2_KEYS 256   // chunks this long use two waves per KV head
+#endif
 
 struct DecParams {
     const uint16_t* q;
@@ -46,6 +53,7 @@ struct DecParams {
     float* lse;
     float* part;      // [N][Hq][n_splits][kPartStride]
     int Hq, Hkv, G, window, n_splits, n_hblk, max_seqlen;
+    int chunk_keys;   // visible keys per chunk (a multiple of 64)
     float c;          // scale * log2(e)
 };
 
@@ -55,60 +63,52 @@ __device__ __forceinline__ void seq_range(const DecParams& p, int n, int& base, 
     vis_lo = p.window > 0 ? max(0, L - p.window) : 0;
 }
 
-__global__ void __launch_bounds__(kThreads)
+// kPar waves per KV head: with kPar = 2 the two waves of a head take
+// alternate tiles of the chunk and are merged through LDS at the end.
+template <int kPar>
+__global__ void __launch_bounds__(kThreads * kPar, 2 / kPar)
 decode_split_kernel(DecParams p) {
-    // per wave: one row-major V tile (64 keys x 64 d, 144-byte rows); the
-    // space is reused for the cross-wave merge
-    __shared__ uint4 vsm[kWaves][kTileUnits];
-    __shared__ float wm[kWaves][32], wl[kWaves][32];
+    __shared__ uint4 ksm[kWaves * kPar][kTileUnits];  // one row-major K tile per wave
+    __shared__ uint4 vsm[kWaves * kPar][kTileUnits];  // one row-major V tile per wave
 
-    const int split = blockIdx.x;
-    const int kvh = blockIdx.y / p.n_hblk;
+    const int chunk = blockIdx.x;
+    const int kvg = blockIdx.y / p.n_hblk;
     const int hb = blockIdx.y % p.n_hblk;
     const int n = blockIdx.z;
     int base, L, vis_lo;
     seq_range(p, n, base, L, vis_lo);
     const int n_vis = L - vis_lo;
-    const int n_act = (n_vis + kSplitKeys - 1) / kSplitKeys;
-    if (split >= n_act) return;  // uniform over the workgroup
-
+    const int n_act = (n_vis + p.chunk_keys - 1) / p.chunk_keys;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int slot = wave % kWaves, par = wave / kWaves;
+    const int kvh = kvg * kWaves + slot;
+    if (n_act == 0) {
+        // empty sequence: only the sink is visible (out = 0, lse = sink)
+        if (chunk == 0 && par == 0 && kvh < p.Hkv && hb * 32 + (lane & 31) < p.G) {
+            const int hd = kvh * p.G + hb * 32 + (lane & 31);
+            uint16_t* orow = p.out + ((size_t)n * p.Hq + hd) * kHeadDim + 32 * (lane >> 5);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) st16(orow + 8 * i, make_uint4(0, 0, 0, 0));
+            if (lane < 32) p.lse[(size_t)n * p.Hq + hd] = p.sinks[hd];
+        }
+        return;
+    }
+    if (chunk >= n_act) return;  // uniform over the workgroup
+    const bool active = kvh < p.Hkv;  // idle waves still reach the merge barrier
     const int g = lane >> 5, l32 = lane & 31;
     const int G = p.G;
-    const int hcol = hb * 32 + l32;             // head within the group
+    const int hcol = hb * 32 + l32;  // head within the group
     const bool col_ok = hcol < G;
     const int head = kvh * G + hcol;
 
-    const int t0 = vis_lo + split * kSplitKeys + wave * 64;  // this wave's first key
-    const int t_end = min(t0 + 64, L);                       // exclusive
-    const bool wave_active = t0 < L;
+    const int c0 = vis_lo + chunk * p.chunk_keys;
+    const int c1 = min(c0 + p.chunk_keys, L);  // exclusive
+    const int n_tiles = (c1 - c0 + kTileKeys - 1) / kTileKeys;
 
     const size_t row_stride = (size_t)p.Hkv * kHeadDim;
     const uint16_t* kb = p.kc + ((size_t)base * p.Hkv + kvh) * kHeadDim;
     const uint16_t* vb = p.vc + ((size_t)base * p.Hkv + kvh) * kHeadDim;
 
-    // K A-operand rows (permuted as in the forward) and V rows for staging
-    bf16x8 ka[2][4];
-    uint4 vr[8];
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-        const int key = t0 + 32 * mb + perm_row(l32);
-        const bool ok = wave_active && key < t_end;
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            uint4 x = make_uint4(0, 0, 0, 0);
-            if (ok) x = ld16(kb + key * row_stride + 16 * ks + 8 * g);
-            ka[mb][ks] = as_bf16x8(x);
-        }
-    }
-    // V rows: lane loads 16-byte unit (lane % 8) of rows lane / 8 + 8 j
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const int key = t0 + (lane >> 3) + 8 * j;
-        uint4 x = make_uint4(0, 0, 0, 0);
-        if (wave_active && key < t_end) x = ld16(vb + key * row_stride + 8 * (lane & 7));
-        vr[j] = x;
-    }
     bf16x8 qf[4];
     {
         const uint16_t* qrow = p.q + ((size_t)n * p.Hq + head) * kHeadDim;
@@ -120,177 +120,234 @@ decode_split_kernel(DecParams p) {
         }
     }
 
-    // V into this wave's LDS tile (row-major; read transposed for P.V)
+    // tile loads: eight consecutive lanes read one whole 128-byte K or V row
+    // (lane loads unit lane % 8 of rows lane / 8 + 8 j), so every load
+    // instruction covers 8 full rows; the rows go through the wave's LDS
+    // tiles.  Rows past the chunk end re-read its last row: their scores are
+    // masked to -inf, so they add exactly 0 to l and to O.
+    uint4 kr[8], vr[8];
+    auto load_tile = [&](int t) {
+        const int t0 = c0 + t * kTileKeys;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) vsm[wave][tile_unit((lane >> 3) + 8 * j, lane & 7)] = vr[j];
-
-    // S^T = K Q^T  (one 32-column block of heads)
-    f32x16 sacc[2];
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sacc[mb][r] = 0.0f;
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) sacc[mb] = mfma32(ka[mb][ks], qf[ks], sacc[mb]);
-    }
-    // mask keys outside [t0, t_end)
-    float mx = -INFINITY;
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int key = t0 + 32 * mb + perm_row(acc_row(r, g));
-            sacc[mb][r] = key < t_end ? sacc[mb][r] : -INFINITY;
-            mx = fmaxf(mx, sacc[mb][r]);
+        for (int j = 0; j < 8; ++j) {
+            const size_t key = min(t0 + (lane >> 3) + 8 * j, c1 - 1);
+            kr[j] = ld16(kb + key * row_stride + 8 * (lane & 7));
+            vr[j] = ld16(vb + key * row_stride + 8 * (lane & 7));
         }
-    mx = max_across_halves(mx);
-    const float m = mx * p.c;                       // -inf only for an idle wave
-    const float m_use = m == -INFINITY ? 0.0f : m;
-    float lsum = 0.0f;
-    bf16x8 pb[4];
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            bf16x8 v8;
-#pragma unroll
-            for (int s = 0; s < 8; ++s) {
-                const float e = fast_exp2(fmaf(sacc[mb][8 * h + s], p.c, -m_use));
-                lsum += e;
-                v8[s] = (__bf16)e;
-            }
-            pb[2 * mb + h] = v8;
-        }
-    lsum = sum_across_halves(lsum);
+    };
 
-    __syncthreads();  // V tiles written by every lane of each wave
+    float m_run = -INFINITY, l_run = 0.0f;
     f32x16 oacc[2];
-#pragma unroll
-    for (int db = 0; db < 2; ++db) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[db][r] = 0.0f;
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-            // V^T rows d = 32 db + l32, keys 16 kk + 8 g + 0..7
-            const bf16x8 a = tile_read_tr8(vsm[wave], 16 * kk + 8 * g, 32 * db + 16 * (l32 >> 4), l32 & 15);
-            oacc[db] = mfma32(a, pb[kk], oacc[db]);
-        }
-    }
-
-    // ---- merge the 4 waves through LDS: O^T partials as [wave][col][d] fp32
-    if (g == 0) {
-        wm[wave][l32] = m;
-        wl[wave][l32] = lsum;
-    }
-    __syncthreads();  // all V reads done before the tiles are overwritten
-    float* ow = reinterpret_cast<float*>(vsm);  // 4 x 32 x 64 floats = 32 KB
-    float msum = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) msum = fmaxf(msum, wm[w][l32]);
-    const float mref = msum == -INFINITY ? 0.0f : msum;
-    const float myscale = m == -INFINITY ? 0.0f : fast_exp2(m - mref);
 #pragma unroll
     for (int db = 0; db < 2; ++db)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int d = 32 * db + acc_row(r, g);
-            ow[(wave * 32 + l32) * 64 + d] = oacc[db][r] * myscale;
+        for (int r = 0; r < 16; ++r) oacc[db][r] = 0.0f;
+
+    if (active && par < n_tiles) load_tile(par);
+    for (int t = par; active && t < n_tiles; t += kPar) {
+        // K and V tiles -> this wave's LDS tiles.  Only this wave touches
+        // them and a wave's LDS operations complete in order, so the previous
+        // tile's reads are done; the signal fences keep the compiler from
+        // moving LDS accesses across the hand-over.
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            ksm[wave][tile_unit((lane >> 3) + 8 * j, lane & 7)] = kr[j];
+            vsm[wave][tile_unit((lane >> 3) + 8 * j, lane & 7)] = vr[j];
         }
-    __syncthreads();
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        if (t + kPar < n_tiles) load_tile(t + kPar);  // in flight during this tile's compute
+        // S^T = K Q^T; A operand rows are keys in the forward's permuted
+        // order, K slots 8 g + 0..7 of step ks are d = 16 ks + 8 g + 0..7
+        f32x16 sacc[2];
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sacc[mb][r] = 0.0f;
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks)
+                sacc[mb] = mfma32(as_bf16x8(ksm[wave][tile_unit(32 * mb + perm_row(l32), 2 * ks + g)]), qf[ks],
+                                  sacc[mb]);
+        }
+        // keys at or beyond c1 are invisible: register r of block mb holds key
+        // t0 + 32 mb + 16 (r / 8) + 8 g + r % 8
+        const int rem = c1 - (c0 + t * kTileKeys) - 8 * g;
+        float mx = -INFINITY;
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int cr = 32 * mb + 16 * (r >> 3) + (r & 7);
+                sacc[mb][r] = cr < rem ? sacc[mb][r] : -INFINITY;
+                mx = fmaxf(mx, sacc[mb][r]);
+            }
+        mx = max_across_halves(mx);
+        const float m_new = fmaxf(m_run, mx * p.c);  // finite: every tile has a visible key
+        const float alpha = fast_exp2(m_run - m_new);  // m_run = -inf -> 0
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < 2; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+        m_run = m_new;
+        bf16x8 pb[4];
+        float la = 0.0f, lb = 0.0f;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            uint32_t w[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int r = 8 * (kk & 1) + 2 * j;
+                const float e0 = fast_exp2(fmaf(sacc[kk >> 1][r], p.c, -m_run));
+                const float e1 = fast_exp2(fmaf(sacc[kk >> 1][r + 1], p.c, -m_run));
+                la += e0;
+                lb += e1;
+                w[j] = pack_bf16x2(e0, e1);
+            }
+            pb[kk] = __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
+        }
+        l_run += la + lb;
+        // O^T += V^T P^T (V^T rows d = 32 db + l32, keys 16 kk + 8 g + 0..7)
+#pragma unroll
+        for (int db = 0; db < 2; ++db)
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk)
+                oacc[db] = mfma32(tile_read_tr8(vsm[wave], 16 * kk + 8 * g, 32 * db + 16 * (l32 >> 4), l32 & 15),
+                                  pb[kk], oacc[db]);
+    }
 
-    // 256 threads: column c = tid / 8, d chunk (8 floats) = tid % 8
-    const int c = tid >> 3, dch = tid & 7;
-    const int ghead = hb * 32 + c;
-    if (ghead >= G) return;
-    const int head_c = kvh * G + ghead;
-    float mtot = -INFINITY;
+    float l_tot = sum_across_halves(l_run);
+    if (kPar > 1) {
+        // merge the two waves of each head: wave par = 1 hands (m, l, O^T)
+        // over through its own LDS tile (its last transposing reads of that
+        // tile were issued before these writes, and a wave's LDS operations
+        // complete in order)
+        float* xfer = reinterpret_cast<float*>(vsm[wave]);
+        if (par == 1) {
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) mtot = fmaxf(mtot, wm[w][c]);
-    const float mref_c = mtot == -INFINITY ? 0.0f : mtot;
-    float ltot = 0.0f;
+            for (int db = 0; db < 2; ++db)
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w)
-        if (wm[w][c] != -INFINITY) ltot += wl[w][c] * fast_exp2(wm[w][c] - mref_c);
-    float o[8];
+                for (int r = 0; r < 16; ++r) xfer[(db * 16 + r) * 64 + lane] = oacc[db][r];
+            xfer[32 * 64 + lane] = m_run;
+            xfer[33 * 64 + lane] = l_tot;
+        }
+        __syncthreads();
+        if (par == 1 || !active) return;
+        const float* other = reinterpret_cast<const float*>(vsm[wave + kWaves]);
+        const float m1 = other[32 * 64 + lane], l1 = other[33 * 64 + lane];
+        const float mm = fmaxf(m_run, m1);
+        const float a0 = fast_exp2(m_run - mm), a1 = fast_exp2(m1 - mm);  // m1 = -inf -> 0
 #pragma unroll
-    for (int i = 0; i < 8; ++i) o[i] = 0.0f;
+        for (int db = 0; db < 2; ++db)
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w)
-#pragma unroll
-        for (int i = 0; i < 8; ++i) o[i] += ow[(w * 32 + c) * 64 + 8 * dch + i];
-
+            for (int r = 0; r < 16; ++r) oacc[db][r] = oacc[db][r] * a0 + other[(db * 16 + r) * 64 + lane] * a1;
+        l_tot = l_tot * a0 + l1 * a1;
+        m_run = mm;
+    }
+    if (!active || !col_ok) return;
     if (n_act == 1) {
         // finish in place: fold in the sink
-        const float sink = p.sinks[head_c];
+        const float sink = p.sinks[head];
         const float s2 = sink * kLog2e;
-        const float mf = fmaxf(s2, mtot);
-        const float a = fast_exp2(mtot - mf);  // mtot is finite: >= 1 visible key
-        const float lfin = (sink == -INFINITY ? 0.0f : fast_exp2(s2 - mf)) + ltot * a;
+        const float mf = fmaxf(s2, m_run);
+        const float a = fast_exp2(m_run - mf);
+        const float lfin = (sink == -INFINITY ? 0.0f : fast_exp2(s2 - mf)) + l_tot * a;
         const float inv = a / lfin;
-        uint4 w4;
-        w4.x = pack_bf16x2(o[0] * inv, o[1] * inv);
-        w4.y = pack_bf16x2(o[2] * inv, o[3] * inv);
-        w4.z = pack_bf16x2(o[4] * inv, o[5] * inv);
-        w4.w = pack_bf16x2(o[6] * inv, o[7] * inv);
-        st16(p.out + ((size_t)n * p.Hq + head_c) * kHeadDim + 8 * dch, w4);
-        if (dch == 0) p.lse[(size_t)n * p.Hq + head_c] = (mf + fast_log2(lfin)) * kLn2;
+        uint16_t* orow = p.out + ((size_t)n * p.Hq + head) * kHeadDim;
+#pragma unroll
+        for (int db = 0; db < 2; ++db)
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+                const int d0 = 32 * db + 8 * r4 + 4 * g;
+                uint2 w;
+                w.x = pack_bf16x2(oacc[db][4 * r4 + 0] * inv, oacc[db][4 * r4 + 1] * inv);
+                w.y = pack_bf16x2(oacc[db][4 * r4 + 2] * inv, oacc[db][4 * r4 + 3] * inv);
+                *reinterpret_cast<uint2*>(orow + d0) = w;
+            }
+        if (g == 0) p.lse[(size_t)n * p.Hq + head] = (mf + fast_log2(lfin)) * kLn2;
         return;
     }
-    float* dst = p.part + (((size_t)n * p.Hq + head_c) * p.n_splits + split) * kPartStride;
-    st16(dst + 8 * dch, *reinterpret_cast<uint4*>(&o[0]));
-    st16(dst + 8 * dch + 4, *reinterpret_cast<uint4*>(&o[4]));
-    if (dch == 0) {
-        dst[64] = mtot;
-        dst[65] = ltot;
+    float* dst = p.part + (((size_t)n * p.Hq + head) * p.n_splits + chunk) * kPartStride;
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+            const int d0 = 32 * db + 8 * r4 + 4 * g;
+            *reinterpret_cast<float4*>(dst + d0) =
+                make_float4(oacc[db][4 * r4 + 0], oacc[db][4 * r4 + 1], oacc[db][4 * r4 + 2], oacc[db][4 * r4 + 3]);
+        }
+    if (g == 0) {
+        dst[64] = m_run;
+        dst[65] = l_tot;
     }
 }
 
-// One wave per (sequence, head); lane = d.
+// One workgroup per (sequence, head) with more than one chunk.  The
+// block-wide maximum over the chunks' m (and the sink) comes first; then wave
+// w sums chunks w, w + 4, ... with lane = d, and wave 0 adds the four sums.
 __global__ void __launch_bounds__(256)
-decode_merge_kernel(DecParams p, int total) {
-    const int wid = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (wid >= total) return;
-    const int lane = threadIdx.x & 63;
-    const int n = wid / p.Hq, head = wid % p.Hq;
+decode_merge_kernel(DecParams p) {
+    __shared__ float red_o[4][64];
+    __shared__ float red_x[4];
+    const int head = blockIdx.x, n = blockIdx.y;
     int base, L, vis_lo;
     seq_range(p, n, base, L, vis_lo);
-    const int n_act = (L - vis_lo + kSplitKeys - 1) / kSplitKeys;
-    const float sink = p.sinks[head];
-    uint16_t* orow = p.out + ((size_t)n * p.Hq + head) * kHeadDim;
-    if (n_act == 1) return;  // finished by the split kernel
-    if (n_act == 0) {        // empty sequence: only the sink
-        orow[lane] = 0;
-        if (lane == 0) p.lse[(size_t)n * p.Hq + head] = sink;
-        return;
-    }
+    const int n_act = (L - vis_lo + p.chunk_keys - 1) / p.chunk_keys;
+    if (n_act <= 1) return;  // finished by the split kernel (uniform exit)
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const float* src = p.part + ((size_t)n * p.Hq + head) * p.n_splits * kPartStride;
-    float mtot = sink * kLog2e;
-    for (int s = 0; s < n_act; ++s) mtot = fmaxf(mtot, src[s * kPartStride + 64]);
-    float l = sink == -INFINITY ? 0.0f : fast_exp2(sink * kLog2e - mtot);
-    float o = 0.0f;
-    for (int s = 0; s < n_act; ++s) {
-        const float a = fast_exp2(src[s * kPartStride + 64] - mtot);
-        l += src[s * kPartStride + 65] * a;
-        o += src[s * kPartStride + lane] * a;
+    const float sink = p.sinks[head];
+    // maximum over the sink and every chunk's m (log2 units)
+    float mx = sink * kLog2e;
+    for (int s = tid; s < n_act; s += 256) mx = fmaxf(mx, src[s * kPartStride + 64]);
+    for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+    if (lane == 0) red_x[wave] = mx;
+    __syncthreads();
+    const float mtot = fmaxf(fmaxf(red_x[0], red_x[1]), fmaxf(red_x[2], red_x[3]));
+    __syncthreads();  // red_x is reused below
+    float o = 0.0f, l = 0.0f;
+#pragma unroll 4
+    for (int s = wave; s < n_act; s += 4) {
+        const float* c = src + s * kPartStride;
+        const float a = fast_exp2(c[64] - mtot);
+        o = fmaf(c[lane], a, o);
+        l = fmaf(c[65], a, l);
     }
-    const float r = o / l;
-    const __bf16 rb = (__bf16)r;
-    orow[lane] = __builtin_bit_cast(uint16_t, rb);
+    red_o[wave][lane] = o;
+    if (lane == 0) red_x[wave] = l;
+    __syncthreads();
+    if (wave != 0) return;
+    o = (red_o[0][lane] + red_o[1][lane]) + (red_o[2][lane] + red_o[3][lane]);
+    l = (red_x[0] + red_x[1]) + (red_x[2] + red_x[3]);
+    if (sink != -INFINITY) l += fast_exp2(sink * kLog2e - mtot);
+    const __bf16 rb = (__bf16)(o / l);
+    p.out[((size_t)n * p.Hq + head) * kHeadDim + lane] = __builtin_bit_cast(uint16_t, rb);
     if (lane == 0) p.lse[(size_t)n * p.Hq + head] = (mtot + fast_log2(l)) * kLn2;
 }
 
-int splits_for(int max_seqlen, int window) {
+// Chunking plan: about one workgroup per CU over the whole grid.  A sequence
+// is cut into chunks only when there are too few (sequence, KV-head group)
+// pairs to fill the chip; every chunk but the last per sequence costs a
+// partial write and read plus the merge launch, which on the 128 x 1024
+// workload cost more than they gain.
+struct ChunkPlan { int keys, n; };
+ChunkPlan chunk_plan(int N, int Hkv, int G, int max_seqlen, int window) {
     const int vis = window > 0 ? std::min(max_seqlen, window) : max_seqlen;
-    return std::max(1, (vis + kSplitKeys - 1) / kSplitKeys);
+    const long long groups = (long long)N * ((Hkv + kWaves - 1) / kWaves) * ((G + 31) / 32);
+    const long long want = std::max(1LL, (256 + groups - 1) / groups);
+    const int max_chunks = std::max(1, (vis + kTileKeys - 1) / kTileKeys);
+    const int n = (int)std::min<long long>(want, max_chunks);
+    int keys = (vis + n - 1) / n;
+    keys = std::max(kTileKeys, (keys + kTileKeys - 1) / kTileKeys * kTileKeys);
+    return ChunkPlan{keys, std::max(1, (vis + keys - 1) / keys)};
 }
 
 }  // namespace
 
 size_t decode_workspace_bytes(int N, int Hq, int Hkv, int max_seqlen, int window) {
-    (void)Hkv;
-    const int ns = splits_for(max_seqlen, window);
-    if (ns <= 1) return 0;
-    return (size_t)N * Hq * ns * kPartStride * sizeof(float);
+    const ChunkPlan cp = chunk_plan(N, Hkv, Hq / Hkv, max_seqlen, window);
+    if (cp.n <= 1) return 0;
+    return (size_t)N * Hq * cp.n * kPartStride * sizeof(float);
 }
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
@@ -308,15 +365,19 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
     p.G = a.Hq / a.Hkv;
     p.window = a.window;
     p.max_seqlen = a.max_seqlen;
-    p.n_splits = splits_for(a.max_seqlen, a.window);
+    const ChunkPlan cp = chunk_plan(a.N, a.Hkv, p.G, a.max_seqlen, a.window);
+    p.n_splits = cp.n;
+    p.chunk_keys = cp.keys;
     p.n_hblk = (p.G + 31) / 32;
     p.c = a.scale * kLog2e;
-    dim3 grid(p.n_splits, a.Hkv * p.n_hblk, a.N);
-    hipLaunchKernelGGL(decode_split_kernel, grid, dim3(kThreads), 0, stream, p);
+    dim3 grid(p.n_splits, ((a.Hkv + kWaves - 1) / kWaves) * p.n_hblk, a.N);
+    if (p.chunk_keys >= GPTOSS_DECODE_PAR2_KEYS)
+        hipLaunchKernelGGL(decode_split_kernel<2>, grid, dim3(kThreads * 2), 0, stream, p);
+    else
+        hipLaunchKernelGGL(decode_split_kernel<1>, grid, dim3(kThreads), 0, stream, p);
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    const int total = a.N * a.Hq;
-    hipLaunchKernelGGL(decode_merge_kernel, dim3((total + 3) / 4), dim3(256), 0, stream, p, total);
+    if (e != hipSuccess || p.n_splits == 1) return e;  // one chunk per sequence: nothing to merge
+    hipLaunchKernelGGL(decode_merge_kernel, dim3(a.Hq, a.N), dim3(256), 0, stream, p);
     return hipGetLastError();
 }
 

@@ -116,7 +116,7 @@ def test_bwd_rejects_bad_arguments(lib):
 
 
 def _dec(lib, **kw):
-    a = dict(q=P, kc=P, vc=P, cu=P, sinks=P, N=128, Hq=64, Hkv=8, D=64, max_seqlen=1024, window=0,
+    a = dict(q=P, kc=P, vc=P, cu=P, sinks=P, N=2, Hq=64, Hkv=8, D=64, max_seqlen=65536, window=0,
              scale=0.125, out=P, lse=P, ws=P, ws_bytes=None)
     a.update(kw)
     need = lib.gptoss_attn_decode_workspace_size(a["N"], a["Hq"], a["Hkv"], a["D"], a["max_seqlen"],
@@ -143,8 +143,10 @@ def test_decode_rejects_bad_arguments(lib, kw, frag):
 
 
 def test_workspace_size_queries(lib):
-    assert lib.gptoss_attn_decode_workspace_size(128, 64, 8, 64, 1024, 0) > 0
-    # a sliding layer fits one split per sequence: no partials
+    # a long single sequence is cut into chunks whose partials need a workspace
+    assert lib.gptoss_attn_decode_workspace_size(1, 64, 8, 64, 65536, 0) > 0
+    # 128 sequences of <= 1024 keys fill the chip one chunk each: no partials
+    assert lib.gptoss_attn_decode_workspace_size(128, 64, 8, 64, 1024, 0) == 0
     assert lib.gptoss_attn_decode_workspace_size(128, 64, 8, 64, 1024, 128) == 0
     assert lib.gptoss_attn_decode_workspace_size(128, 64, 8, 128, 1024, 0) == 0  # unsupported D
     assert lib.gptoss_attn_bwd_workspace_size(4, 4096, 64, 8, 64, 0) >= 0

@@ -107,6 +107,20 @@ def test_decode_matches_prefill_last_row():
         assert (lse_d[0] - lse_p[0, :, S - 1]).abs().max().item() <= 1e-3
 
 
+@pytest.mark.parametrize("window", [0, 128])
+@pytest.mark.parametrize("lengths", [[65536], [1024] * 31 + [700], [3000, 1, 64, 2049]],
+                         ids=["one_long", "n32", "mixed"])
+def test_decode_chunked(window, lengths):
+    """Few (sequence, KV group) pairs: sequences are cut into chunks, each
+    chunk walked by one or two waves per KV head, and merged afterwards."""
+    dev = need_gpu()
+    case = synth.make_decode(len(lengths), 64, 8, lengths=lengths, seed=seed_of(lengths, window))
+    print(f"decode chunked n={len(lengths)} max={max(lengths)} W={window}", flush=True)
+    out, lse = _run(case, window, dev)
+    ro, rl = _oracle(case, window)
+    check_out_lse(f64(out), f64(lse), ro, rl, f"chunked W={window}")
+
+
 def test_decode_is_deterministic():
     dev = need_gpu()
     case = synth.make_decode(32, 64, 8, max_len=1024, seed=13)
