@@ -15,15 +15,16 @@
 //     pairs would fill the chip.  Each wave owns one KV head, so the 4 waves of a
 //     workgroup stream adjacent 128-byte rows of the same tokens (512
 //     contiguous bytes per token for K and again for V).  A wave walks its
-//     chunk in 64-key tiles: K rows go straight into MFMA A-operand
-//     registers, V rows into a wave-private LDS tile (read back transposed),
-//     S^T = K Q^T and O^T = V^T P^T on 32x32x16 bf16 MFMAs with the G query
+//     chunk in 64-key tiles: whole K and V rows (8 lanes per 128-byte row)
+//     go through wave-private LDS tiles, K read back as MFMA A operands and V
+//     transposed, S^T = K Q^T and O^T = V^T P^T on 32x32x16 bf16 MFMAs with the G query
 //     heads as columns, an online softmax across tiles, and the next tile's
 //     loads in flight while the current one is computed.  Waves never
 //     synchronise.  A sequence that fits in one chunk is finished in place
 //     (sink folded in, out and lse written); otherwise the wave writes one
 //     partial (unnormalised O, running max m in log2 units, sum l) per head.
-//   merge kernel : one workgroup per (sequence, head) with more than one chunk:
+//   merge kernels (one wave per (sequence, head) when there are at most 16
+//     chunks, one workgroup per (sequence, head) otherwise):
 //     m = max(sink, m_s), l = 2^(sink - m) + sum l_s 2^(m_s - m),
 //     out = sum O_s 2^(m_s - m) / l, lse = ln2 (m + log2 l).  The sink enters
 //     here exactly once.
@@ -39,9 +40,10 @@ constexpr int kThreads = 256;
 constexpr int kWaves = 4;         // KV heads per workgroup, one per wave
 constexpr int kTileKeys = 64;     // keys per wave step
 constexpr int kPartStride = 68;   // floats per partial: O[64], m, l, pad
-#ifndef GPTOSS_DECODE_PAR2_KEYS
-#define GPTOSS_DECODE_PAR2_KEYS 256   // chunks this long use two waves per KV head
-#endif
+// Workgroups the chunking aims for: one per CU.  Cutting the 128 x 1024
+// workload finer (512 or more workgroups, merged afterwards) measured slower.
+constexpr long long kTargetWorkgroups = 256;
+
 
 struct DecParams {
     const uint16_t* q;
@@ -63,13 +65,14 @@ __device__ __forceinline__ void seq_range(const DecParams& p, int n, int& base, 
     vis_lo = p.window > 0 ? max(0, L - p.window) : 0;
 }
 
-// kPar waves per KV head: with kPar = 2 the two waves of a head take
-// alternate tiles of the chunk and are merged through LDS at the end.
-template <int kPar>
-__global__ void __launch_bounds__(kThreads * kPar, 2 / kPar)
+// The loads of tile t + 1 are issued as soon as tile t has been moved to
+// LDS.  (Keeping two to four tiles per wave in flight, at one wave per SIMD,
+// measured slower on the 128 x 1024 workload than one tile per wave at two
+// workgroups per CU, and so did two waves per KV head taking alternate tiles.)
+__global__ void __launch_bounds__(kThreads, 2)
 decode_split_kernel(DecParams p) {
-    __shared__ uint4 ksm[kWaves * kPar][kTileUnits];  // one row-major K tile per wave
-    __shared__ uint4 vsm[kWaves * kPar][kTileUnits];  // one row-major V tile per wave
+    __shared__ uint4 ksm[kWaves][kTileUnits];  // one row-major K tile per wave
+    __shared__ uint4 vsm[kWaves][kTileUnits];  // one row-major V tile per wave
 
     const int chunk = blockIdx.x;
     const int kvg = blockIdx.y / p.n_hblk;
@@ -80,11 +83,10 @@ decode_split_kernel(DecParams p) {
     const int n_vis = L - vis_lo;
     const int n_act = (n_vis + p.chunk_keys - 1) / p.chunk_keys;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int slot = wave % kWaves, par = wave / kWaves;
-    const int kvh = kvg * kWaves + slot;
+    const int kvh = kvg * kWaves + wave;
     if (n_act == 0) {
         // empty sequence: only the sink is visible (out = 0, lse = sink)
-        if (chunk == 0 && par == 0 && kvh < p.Hkv && hb * 32 + (lane & 31) < p.G) {
+        if (chunk == 0 && kvh < p.Hkv && hb * 32 + (lane & 31) < p.G) {
             const int hd = kvh * p.G + hb * 32 + (lane & 31);
             uint16_t* orow = p.out + ((size_t)n * p.Hq + hd) * kHeadDim + 32 * (lane >> 5);
 #pragma unroll
@@ -93,8 +95,8 @@ decode_split_kernel(DecParams p) {
         }
         return;
     }
-    if (chunk >= n_act) return;  // uniform over the workgroup
-    const bool active = kvh < p.Hkv;  // idle waves still reach the merge barrier
+    if (chunk >= n_act) return;
+    if (kvh >= p.Hkv) return;  // waves are independent: no barrier follows
     const int g = lane >> 5, l32 = lane & 31;
     const int G = p.G;
     const int hcol = hb * 32 + l32;  // head within the group
@@ -143,8 +145,8 @@ decode_split_kernel(DecParams p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[db][r] = 0.0f;
 
-    if (active && par < n_tiles) load_tile(par);
-    for (int t = par; active && t < n_tiles; t += kPar) {
+    if (n_tiles > 0) load_tile(0);
+    for (int t = 0; t < n_tiles; ++t) {
         // K and V tiles -> this wave's LDS tiles.  Only this wave touches
         // them and a wave's LDS operations complete in order, so the previous
         // tile's reads are done; the signal fences keep the compiler from
@@ -156,7 +158,7 @@ decode_split_kernel(DecParams p) {
             vsm[wave][tile_unit((lane >> 3) + 8 * j, lane & 7)] = vr[j];
         }
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
-        if (t + kPar < n_tiles) load_tile(t + kPar);  // in flight during this tile's compute
+        if (t + 1 < n_tiles) load_tile(t + 1);  // in flight during this tile's compute
         // S^T = K Q^T; A operand rows are keys in the forward's permuted
         // order, K slots 8 g + 0..7 of step ks are d = 16 ks + 8 g + 0..7
         f32x16 sacc[2];
@@ -216,35 +218,8 @@ decode_split_kernel(DecParams p) {
                                   pb[kk], oacc[db]);
     }
 
-    float l_tot = sum_across_halves(l_run);
-    if (kPar > 1) {
-        // merge the two waves of each head: wave par = 1 hands (m, l, O^T)
-        // over through its own LDS tile (its last transposing reads of that
-        // tile were issued before these writes, and a wave's LDS operations
-        // complete in order)
-        float* xfer = reinterpret_cast<float*>(vsm[wave]);
-        if (par == 1) {
-#pragma unroll
-            for (int db = 0; db < 2; ++db)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) xfer[(db * 16 + r) * 64 + lane] = oacc[db][r];
-            xfer[32 * 64 + lane] = m_run;
-            xfer[33 * 64 + lane] = l_tot;
-        }
-        __syncthreads();
-        if (par == 1 || !active) return;
-        const float* other = reinterpret_cast<const float*>(vsm[wave + kWaves]);
-        const float m1 = other[32 * 64 + lane], l1 = other[33 * 64 + lane];
-        const float mm = fmaxf(m_run, m1);
-        const float a0 = fast_exp2(m_run - mm), a1 = fast_exp2(m1 - mm);  // m1 = -inf -> 0
-#pragma unroll
-        for (int db = 0; db < 2; ++db)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) oacc[db][r] = oacc[db][r] * a0 + other[(db * 16 + r) * 64 + lane] * a1;
-        l_tot = l_tot * a0 + l1 * a1;
-        m_run = mm;
-    }
-    if (!active || !col_ok) return;
+    const float l_tot = sum_across_halves(l_run);
+    if (!col_ok) return;
     if (n_act == 1) {
         // finish in place: fold in the sink
         const float sink = p.sinks[head];
@@ -282,7 +257,48 @@ decode_split_kernel(DecParams p) {
     }
 }
 
-// One workgroup per (sequence, head) with more than one chunk.  The
+// Few chunks (at most kFewChunks): one wave per (sequence, head), four heads
+// per workgroup; lane = d, the chunks' partials are read in one unrolled pass.
+constexpr int kFewChunks = 16;
+__global__ void __launch_bounds__(256)
+decode_merge_few_kernel(DecParams p) {
+    const int n = blockIdx.y;
+    const int head = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (head >= p.Hq) return;
+    int base, L, vis_lo;
+    seq_range(p, n, base, L, vis_lo);
+    const int n_act = (L - vis_lo + p.chunk_keys - 1) / p.chunk_keys;
+    if (n_act <= 1) return;  // finished by the split kernel
+    const int lane = threadIdx.x & 63;
+    const float* src = p.part + ((size_t)n * p.Hq + head) * p.n_splits * kPartStride;
+    const float sink = p.sinks[head];
+    float ms[kFewChunks], ls[kFewChunks], os[kFewChunks];
+    float mtot = sink * kLog2e;
+#pragma unroll
+    for (int s = 0; s < kFewChunks; ++s) {
+        if (s < n_act) {
+            ms[s] = src[s * kPartStride + 64];
+            ls[s] = src[s * kPartStride + 65];
+            os[s] = src[s * kPartStride + lane];
+            mtot = fmaxf(mtot, ms[s]);
+        }
+    }
+    float l = sink == -INFINITY ? 0.0f : fast_exp2(sink * kLog2e - mtot);
+    float o = 0.0f;
+#pragma unroll
+    for (int s = 0; s < kFewChunks; ++s) {
+        if (s < n_act) {
+            const float a = fast_exp2(ms[s] - mtot);
+            l = fmaf(ls[s], a, l);
+            o = fmaf(os[s], a, o);
+        }
+    }
+    const __bf16 rb = (__bf16)(o / l);
+    p.out[((size_t)n * p.Hq + head) * kHeadDim + lane] = __builtin_bit_cast(uint16_t, rb);
+    if (lane == 0) p.lse[(size_t)n * p.Hq + head] = (mtot + fast_log2(l)) * kLn2;
+}
+
+// Many chunks: one workgroup per (sequence, head) with more than one chunk.  The
 // block-wide maximum over the chunks' m (and the sink) comes first; then wave
 // w sums chunks w, w + 4, ... with lane = d, and wave 0 adds the four sums.
 __global__ void __launch_bounds__(256)
@@ -334,7 +350,7 @@ struct ChunkPlan { int keys, n; };
 ChunkPlan chunk_plan(int N, int Hkv, int G, int max_seqlen, int window) {
     const int vis = window > 0 ? std::min(max_seqlen, window) : max_seqlen;
     const long long groups = (long long)N * ((Hkv + kWaves - 1) / kWaves) * ((G + 31) / 32);
-    const long long want = std::max(1LL, (256 + groups - 1) / groups);
+    const long long want = std::max(1LL, (kTargetWorkgroups + groups - 1) / groups);
     const int max_chunks = std::max(1, (vis + kTileKeys - 1) / kTileKeys);
     const int n = (int)std::min<long long>(want, max_chunks);
     int keys = (vis + n - 1) / n;
@@ -371,13 +387,13 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
     p.n_hblk = (p.G + 31) / 32;
     p.c = a.scale * kLog2e;
     dim3 grid(p.n_splits, ((a.Hkv + kWaves - 1) / kWaves) * p.n_hblk, a.N);
-    if (p.chunk_keys >= GPTOSS_DECODE_PAR2_KEYS)
-        hipLaunchKernelGGL(decode_split_kernel<2>, grid, dim3(kThreads * 2), 0, stream, p);
-    else
-        hipLaunchKernelGGL(decode_split_kernel<1>, grid, dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL(decode_split_kernel, grid, dim3(kThreads), 0, stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.n_splits == 1) return e;  // one chunk per sequence: nothing to merge
-    hipLaunchKernelGGL(decode_merge_kernel, dim3(a.Hq, a.N), dim3(256), 0, stream, p);
+    if (p.n_splits <= kFewChunks)
+        hipLaunchKernelGGL(decode_merge_few_kernel, dim3((a.Hq + 3) / 4, a.N), dim3(256), 0, stream, p);
+    else
+        hipLaunchKernelGGL(decode_merge_kernel, dim3(a.Hq, a.N), dim3(256), 0, stream, p);
     return hipGetLastError();
 }
 

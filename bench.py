@@ -30,6 +30,7 @@ BF16_PEAK_TFLOPS = 2516.6      # MI355X dense bf16 MFMA (256 CU x 2.4 GHz x 4096
 D = 64
 WINDOWS = (128, 0)             # sliding layer, full-causal layer
 COPY_BYTES = 1 << 30           # calibration copy for the HBM byte counters
+NSETS = 4                      # input/output buffer sets used in rotation
 ROOT = os.path.dirname(os.path.abspath(__file__))
 
 
@@ -107,56 +108,68 @@ def main():
         print(f"done: copy of {COPY_BYTES} bytes x {args.warmup + args.steps}", flush=True)
         return
 
-    # ---- inputs (seeded, synthetic, gpt-oss shaped), resident in HBM
+    # ---- inputs (seeded, synthetic, gpt-oss shaped), resident in HBM.
+    # NSETS copies of every input and output, used in rotation, so that
+    # consecutive launches never find their working set in the 256 MB
+    # last-level cache (MALL) that the previous launch filled.
     case, dout_cpu = synth.config_inputs("c3_bwd_b4_s4096_h64x8")
     B, S, Hq, _ = case.q.shape
     Hkv = case.k.shape[2]
-    q, k, v = case.q.to(dev), case.k.to(dev), case.v.to(dev)
     sinks = case.sinks.to(dev)
-    dout = dout_cpu.to(dev)
     dec = synth.config_inputs("c4_decode_n128_l1024_h64x8")
     N = dec.q.shape[0]
-    dq_, dk_, dv_ = dec.q.to(dev), dec.k_cache.to(dev), dec.v_cache.to(dev)
     dcu, dsinks_ = dec.cu_seqlens.to(dev), dec.sinks.to(dev)
     lengths = (dec.cu_seqlens[1:] - dec.cu_seqlens[:-1]).tolist()
     scale = case.scale
 
-    outs = {w: (torch.empty_like(q), torch.empty(B, Hq, S, device=dev)) for w in WINDOWS}
-    dec_out = {w: (torch.empty_like(dq_), torch.empty(N, Hq, device=dev)) for w in WINDOWS}
-    grads = {w: (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v),
-                 torch.empty(Hq, dtype=torch.float32, device=dev)) for w in WINDOWS}
+    sets = []
+    for _ in range(NSETS):
+        q, k, v, dout = case.q.to(dev), case.k.to(dev), case.v.to(dev), dout_cpu.to(dev)
+        sets.append(dict(
+            q=q, k=k, v=v, dout=dout,
+            outs={w: (torch.empty_like(q), torch.empty(B, Hq, S, device=dev)) for w in WINDOWS},
+            grads={w: (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v),
+                       torch.empty(Hq, dtype=torch.float32, device=dev)) for w in WINDOWS},
+            dq=dec.q.to(dev), dk=dec.k_cache.to(dev), dv=dec.v_cache.to(dev),
+            dec_out={w: (torch.empty_like(dec.q, device=dev), torch.empty(N, Hq, device=dev)) for w in WINDOWS}))
+    q, k = sets[0]["q"], sets[0]["k"]
     bws = torch.empty(attn.bwd_workspace_size(B, S, Hq, Hkv, D, 0), dtype=torch.uint8, device=dev)
     dws = torch.empty(max(1, attn.decode_workspace_size(N, Hq, Hkv, D, dec.max_seqlen, 0)),
                       dtype=torch.uint8, device=dev)
 
-    def fwd(w):
-        o, l = outs[w]
-        attn.fwd(q, k, v, sinks, w, scale, out=o, lse=l)
+    def fwd(w, i=0):
+        x = sets[i % NSETS]
+        o, l = x["outs"][w]
+        attn.fwd(x["q"], x["k"], x["v"], sinks, w, scale, out=o, lse=l)
 
-    def bwd(w):
-        o, l = outs[w]
-        attn.bwd(q, k, v, sinks, o, l, dout, w, scale, workspace=bws, grads=grads[w])
+    def bwd(w, i=0):
+        x = sets[i % NSETS]
+        o, l = x["outs"][w]
+        attn.bwd(x["q"], x["k"], x["v"], sinks, o, l, x["dout"], w, scale, workspace=bws, grads=x["grads"][w])
 
-    def decode(w):
-        o, l = dec_out[w]
-        attn.decode(dq_, dk_, dv_, dcu, dsinks_, dec.max_seqlen, w, dec.scale, out=o, lse=l, workspace=dws)
+    def decode(w, i=0):
+        x = sets[i % NSETS]
+        o, l = x["dec_out"][w]
+        attn.decode(x["dq"], x["dk"], x["dv"], dcu, dsinks_, dec.max_seqlen, w, dec.scale, out=o, lse=l,
+                    workspace=dws)
 
-    def step():
+    def step(i=0):
         for w in WINDOWS:
-            fwd(w)
-            bwd(w)
+            fwd(w, i)
+            bwd(w, i)
         for w in WINDOWS:
-            decode(w)
+            decode(w, i)
 
     if args.only:
         fn = {"fwd": fwd, "bwd": bwd, "decode": decode}[args.only]
         wins = WINDOWS if args.window is None else (args.window,)
         if args.only == "bwd":
+            for i in range(NSETS):
+                for w in wins:
+                    fwd(w, i)  # the backward consumes this layer's forward out/lse
+        for i in range(args.warmup + args.steps):
             for w in wins:
-                fwd(w)  # the backward consumes this layer's forward out/lse
-        for _ in range(args.warmup + args.steps):
-            for w in wins:
-                fn(w)
+                fn(w, i)
         torch.cuda.synchronize()
         print(f"done: {args.only} x {args.warmup + args.steps} per layer", flush=True)
         return
@@ -169,7 +182,7 @@ def main():
         flops[("fwd", w)] = 4 * D * pairs
         flops[("bwd", w)] = 10 * D * pairs
         # algorithmic bytes: every input read once, every output written once
-        bytes_[("fwd", w)] = 2 * (q.numel() + k.numel() + v.numel() + q.numel()) + 4 * B * Hq * S
+        bytes_[("fwd", w)] = 2 * (q.numel() + 2 * k.numel() + q.numel()) + 4 * B * Hq * S
         bytes_[("bwd", w)] = (2 * (4 * q.numel() + 2 * k.numel()) + 4 * B * Hq * S + 4 * Hq   # q,out,dout,dq + k,v
                               + 2 * 2 * k.numel() + 4 * Hq)                                  # dk, dv, sinks/dsinks
         vis = sum(min(L, w) if w else L for L in lengths)
@@ -191,25 +204,32 @@ def main():
         torch.cuda.synchronize()
         return t0.elapsed_time(t1) / n
 
-    # eager step (reported only): warm the library, then one timed pass
-    step()
-    ms_eager = timed(step, max(1, min(args.steps, 3)))
-    g_step = capture(step)
+    # eager step (reported only): warm the library on every buffer set, then
+    # one timed pass per set
+    for i in range(NSETS):
+        step(i)
+    it = iter(range(1 << 30))
+    ms_eager = timed(lambda: step(next(it)), NSETS)
+    g_steps = [capture(lambda: step(i)) for i in range(NSETS)]
 
-    # ---- warmup, then the timed region: exactly `steps` graph replays
-    for _ in range(args.warmup):
-        g_step.replay()
-    ms_per_step = timed(g_step.replay, args.steps)
+    # ---- warmup, then the timed region: exactly `steps` graph replays,
+    # rotating over the buffer sets
+    for i in range(args.warmup):
+        g_steps[i % NSETS].replay()
+    it = iter(range(1 << 30))
+    ms_per_step = timed(lambda: g_steps[next(it) % NSETS].replay(), args.steps)
     total_flops = sum(flops.values())
     value = total_flops / (ms_per_step * 1e-3) / 1e12
+    del g_steps
 
     # ---- per-part launch durations: a graph of `reps` back-to-back calls of
-    # one part, replayed three times; the median replay / reps
-    reps = 10
+    # one part (rotating over the buffer sets), replayed three times; the
+    # median replay / reps
+    reps = 4 * NSETS
     part_ms = {}
     for name, fn in (("fwd", fwd), ("bwd", bwd), ("decode", decode)):
         for w in WINDOWS:
-            g = capture(lambda: [fn(w) for _ in range(reps)])
+            g = capture(lambda: [fn(w, i) for i in range(reps)])
             g.replay()
             part_ms[(name, w)] = sorted(timed(g.replay, 1) for _ in range(3))[1] / reps
             del g
