@@ -130,8 +130,11 @@ __device__ __forceinline__ void dkdv_coords(const BwdParams& p, int n_kt, int bi
     const int n_groups = p.B * p.Hkv;
     if ((n_groups & 7) == 0) {
         const int xcd = bid & 7, slot = bid >> 3;
-        grp = xcd * (n_groups >> 3) + slot / n_kt;
-        kt = slot % n_kt;  // low key tiles (most queries) first
+        // tile-major within the XCD: the heaviest key tiles (lowest, seen by
+        // the most queries) of all the XCD's groups are dispatched first
+        const int gpx = n_groups >> 3;
+        grp = xcd * gpx + slot % gpx;
+        kt = slot / gpx;
     } else {
         grp = bid % n_groups;
         kt = bid / n_groups;
@@ -369,8 +372,9 @@ __device__ __forceinline__ void dq_coords(const BwdParams& p, int n_qt, int bid,
     const int n_groups = p.B * p.Hkv;
     if ((n_groups & 7) == 0) {
         const int xcd = bid & 7, slot = bid >> 3;
-        grp = xcd * (n_groups >> 3) + slot / n_qt;
-        qt = slot % n_qt;
+        const int gpx = n_groups >> 3;  // tile-major: heaviest tiles of all groups first
+        grp = xcd * gpx + slot % gpx;
+        qt = slot / gpx;
     } else {
         grp = bid % n_groups;
         qt = bid / n_groups;

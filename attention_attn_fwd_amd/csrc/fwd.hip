@@ -99,8 +99,9 @@ __device__ __forceinline__ void block_coords(const FwdParams& p, int bid, int& g
     const int nq = p.n_qtiles;
     if ((p.n_groups & 7) == 0) {
         const int xcd = bid & 7, slot = bid >> 3;
-        grp = xcd * (p.n_groups >> 3) + slot / nq;
-        qt = slot % nq;
+        const int gpx = p.n_groups >> 3;  // tile-major: heaviest tiles of all groups first
+        grp = xcd * gpx + slot % gpx;
+        qt = slot / gpx;
     } else {
         grp = bid % p.n_groups;
         qt = bid / p.n_groups;
