@@ -149,7 +149,7 @@ bwd_dkdv_kernel(BwdParams p, int n_kt) {
     __shared__ float4 sD[2][kColsPerStep / 4];  // Dvec per column
     __shared__ int4 sP[2][kColsPerStep / 4];    // position per column
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 5, l32 = lane & 31, i16 = lane & 15;
     int grp, kt;
     dkdv_coords(p, n_kt, blockIdx.x, grp, kt);
@@ -162,7 +162,12 @@ bwd_dkdv_kernel(BwdParams p, int n_kt) {
     const bool wave_active = kw0 < S;
     const int my_key = kw0 + l32;
 
-    // K and V rows of this lane's key as B operands (d = 16 ks + 8 g + 0..7)
+    // K and V rows of this lane's key as B operands (d = 16 ks + 8 g + 0..7).
+    // K is multiplied by c = scale * log2(e) once here (and rounded to bf16),
+    // so that S' = Q (c K)^T is the score in log2 units; with the
+    // accumulator started at -lse * log2(e), P = exp2(S') needs no further
+    // arithmetic.  (The rounding of c K perturbs P by ~2^-9 relative, far
+    // inside the gradients' tolerance; dK uses Q and dS, not K.)
     const size_t kv_stride = (size_t)p.Hkv * kHeadDim;
     bf16x8 kb[4], vb[4];
     {
@@ -174,7 +179,11 @@ bwd_dkdv_kernel(BwdParams p, int n_kt) {
                 x = ld16(p.k + off + 16 * ks + 8 * g);
                 y = ld16(p.v + off + 16 * ks + 8 * g);
             }
-            kb[ks] = as_bf16x8(x);
+            const uint32_t xw[4] = {x.x, x.y, x.z, x.w};
+            uint32_t kw[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) kw[i] = pack_bf16x2(bf16_lo(xw[i]) * p.c, bf16_hi(xw[i]) * p.c);
+            kb[ks] = as_bf16x8(make_uint4(kw[0], kw[1], kw[2], kw[3]));
             vb[ks] = as_bf16x8(y);
         }
     }
@@ -248,21 +257,32 @@ bwd_dkdv_kernel(BwdParams p, int n_kt) {
             sO[buf][tile_unit(row, st_unit)] = ro[j];
         }
         if (tid < kColsPerStep) {
-            reinterpret_cast<float*>(sL[buf])[tid] = rld.x;
-            reinterpret_cast<float*>(sD[buf])[tid] = rld.y;
+            // negated: they seed the S' and dP accumulators
+            reinterpret_cast<float*>(sL[buf])[tid] = -rld.x;
+            reinterpret_cast<float*>(sD[buf])[tid] = -rld.y;
             reinterpret_cast<int*>(sP[buf])[tid] = rpos;
         }
     };
 
-    // One 32-column block: S = Q K^T and dP = dO V^T (one key per lane,
-    // register 8h + s = column 32 mb + 16 h + 8 g + s); on edge steps the
-    // invisible scores are set to -inf (so P = dS = 0); then P and dS, and
-    // dV^T += dO^T P, dK^T += Q^T dS over those 32 columns.
+    // One 32-column block: S' - lse' = Q (c K)^T - lse * log2(e) and
+    // dP - Dvec = dO V^T - Dvec (one key per lane, register 8h + s = column
+    // 32 mb + 16 h + 8 g + s; the accumulators start at the staged -lse' and
+    // -Dvec); on edge steps the invisible scores are set to -inf (so P = dS =
+    // 0); then P = exp2(.), dS = P (dP - Dvec), and dV^T += dO^T P,
+    // dK^T += Q^T dS over those 32 columns.
     auto block = [&](const uint4* tq, const uint4* to, const float4* tl, const float4* td, const int4* tp, int mb,
                      bool need_mask) {
         f32x16 sacc, dpacc;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sacc[r] = dpacc[r] = 0.0f;
+        for (int h = 0; h < 2; ++h) {
+            const int q4 = (32 * mb + 16 * h + 8 * g) >> 2;  // float4 index of the 8 columns
+            const float4 la = tl[q4], lb = tl[q4 + 1];
+            const float4 da = td[q4], dbv = td[q4 + 1];
+            sacc[8 * h + 0] = la.x; sacc[8 * h + 1] = la.y; sacc[8 * h + 2] = la.z; sacc[8 * h + 3] = la.w;
+            sacc[8 * h + 4] = lb.x; sacc[8 * h + 5] = lb.y; sacc[8 * h + 6] = lb.z; sacc[8 * h + 7] = lb.w;
+            dpacc[8 * h + 0] = da.x; dpacc[8 * h + 1] = da.y; dpacc[8 * h + 2] = da.z; dpacc[8 * h + 3] = da.w;
+            dpacc[8 * h + 4] = dbv.x; dpacc[8 * h + 5] = dbv.y; dpacc[8 * h + 6] = dbv.z; dpacc[8 * h + 7] = dbv.w;
+        }
         const int arow = 32 * mb + perm_row(l32);
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
@@ -282,11 +302,6 @@ bwd_dkdv_kernel(BwdParams p, int n_kt) {
         }
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-            const int q4 = (32 * mb + 16 * h + 8 * g) >> 2;  // float4 index of the 8 columns
-            const float4 la = tl[q4], lb = tl[q4 + 1];
-            const float4 da = td[q4], dbv = td[q4 + 1];
-            const float lv[8] = {la.x, la.y, la.z, la.w, lb.x, lb.y, lb.z, lb.w};
-            const float dv[8] = {da.x, da.y, da.z, da.w, dbv.x, dbv.y, dbv.z, dbv.w};
             uint32_t wp[4], wd[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
@@ -294,8 +309,8 @@ bwd_dkdv_kernel(BwdParams p, int n_kt) {
 #pragma unroll
                 for (int e = 0; e < 2; ++e) {
                     const int s = 2 * j + e;
-                    pr[e] = fast_exp2(fmaf(sacc[8 * h + s], p.c, -lv[s]));
-                    ds[e] = pr[e] * (dpacc[8 * h + s] - dv[s]);
+                    pr[e] = fast_exp2(sacc[8 * h + s]);
+                    ds[e] = pr[e] * dpacc[8 * h + s];
                 }
                 wp[j] = pack_bf16x2(pr[0], pr[1]);
                 wd[j] = pack_bf16x2(ds[0], ds[1]);
@@ -387,7 +402,7 @@ bwd_dq_kernel(BwdParams p, int n_qt, int pos_per_block) {
     __shared__ uint4 sK[2][kTileUnits];
     __shared__ uint4 sV[2][kTileUnits];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 5, l32 = lane & 31, i16 = lane & 15;
     int grp, qt;
     dq_coords(p, n_qt, blockIdx.x, grp, qt);
