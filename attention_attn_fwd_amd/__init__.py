@@ -8,6 +8,11 @@ all computation runs in the library's HIP kernels.
     out, lse = fwd(q, k, v, sinks, window, scale)
     dq, dk, dv, dsinks = bwd(q, k, v, sinks, out, lse, dout, window, scale)
     out, lse = decode(q, k_cache, v_cache, cu_seqlens, sinks, max_seqlen, window, scale)
+    out, lse = decode_paged(q, k_pages, v_pages, block_table, seq_lens, sinks, max_seqlen, window, scale,
+                            ring_tokens)
+
+Training: attention_attn_fwd_amd.autograd.sink_attention (torch autograd over
+fwd/bwd).
 """
 
 import torch
@@ -15,7 +20,7 @@ import torch
 from . import _lib
 from ._lib import AttnError
 
-__all__ = ["fwd", "bwd", "decode", "bwd_workspace_size", "decode_workspace_size", "AttnError",
+__all__ = ["fwd", "bwd", "decode", "decode_paged", "bwd_workspace_size", "decode_workspace_size", "AttnError",
            "abi_version"]
 
 
@@ -139,5 +144,39 @@ def decode(q, k_cache, v_cache, cu_seqlens, sinks, max_seqlen, window=0, scale=N
                                 sinks.data_ptr(), N, Hq, Hkv, D, int(max_seqlen), int(window), scale,
                                 out.data_ptr(), lse.data_ptr(), workspace.data_ptr(), workspace.numel(),
                                 _stream(q.device))
+    _lib.check(st, lib)
+    return out, lse
+
+
+def decode_paged(q, k_pages, v_pages, block_table, seq_lens, sinks, max_seqlen, window=0, scale=None,
+                 ring_tokens=0, out=None, lse=None, workspace=None):
+    """Decode against a paged KV cache.  q [N,Hq,D]; pages [P, page_size, Hkv, D] bf16;
+    block_table int32 [N, pages_per_seq] and seq_lens int32 [N] on the device; ring_tokens = 0
+    for a linear cache, else the ring size of a sliding layer's cache.  Returns (out, lse)."""
+    _need(q, "q", torch.bfloat16, 3)
+    _need(k_pages, "k_pages", torch.bfloat16, 4)
+    _need(v_pages, "v_pages", torch.bfloat16, 4)
+    _need(block_table, "block_table", torch.int32, 2)
+    _need(seq_lens, "seq_lens", torch.int32, 1)
+    _need(sinks, "sinks", torch.float32, 1)
+    N, Hq, D = q.shape
+    _, page_size, Hkv, Dk = k_pages.shape
+    if (v_pages.shape != k_pages.shape or Dk != D or block_table.shape[0] != N or seq_lens.shape != (N,)
+            or sinks.shape != (Hq,)):
+        raise ValueError("shape mismatch among paged decode inputs")
+    scale = (1.0 / D ** 0.5) if scale is None else float(scale)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((N, Hq), dtype=torch.float32, device=q.device)
+    need = decode_workspace_size(N, Hq, Hkv, D, max_seqlen, window)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    lib = _lib.load()
+    st = lib.gptoss_attn_decode_paged(q.data_ptr(), k_pages.data_ptr(), v_pages.data_ptr(), block_table.data_ptr(),
+                                      seq_lens.data_ptr(), sinks.data_ptr(), N, Hq, Hkv, D, page_size,
+                                      block_table.shape[1], int(ring_tokens), int(max_seqlen), int(window), scale,
+                                      out.data_ptr(), lse.data_ptr(), workspace.data_ptr(), workspace.numel(),
+                                      _stream(q.device))
     _lib.check(st, lib)
     return out, lse

@@ -17,7 +17,7 @@ STATUS_NAMES = {0: "OK", 1: "INVALID_ARGUMENT", 2: "UNSUPPORTED", 3: "HIP"}
 EXPORTS = [
     "gptoss_attn_abi_version", "gptoss_attn_last_error", "gptoss_attn_fwd",
     "gptoss_attn_bwd_workspace_size", "gptoss_attn_bwd",
-    "gptoss_attn_decode_workspace_size", "gptoss_attn_decode",
+    "gptoss_attn_decode_workspace_size", "gptoss_attn_decode", "gptoss_attn_decode_paged",
 ]
 
 _lib = None
@@ -57,6 +57,9 @@ def load(path=None):
     lib.gptoss_attn_decode_workspace_size.argtypes = [c_int] * 6
     lib.gptoss_attn_decode.restype = c_int
     lib.gptoss_attn_decode.argtypes = [c_void_p] * 5 + [c_int] * 6 + [c_float] + [c_void_p] * 3 + \
+        [c_size_t, c_void_p]
+    lib.gptoss_attn_decode_paged.restype = c_int
+    lib.gptoss_attn_decode_paged.argtypes = [c_void_p] * 6 + [c_int] * 9 + [c_float] + [c_void_p] * 3 + \
         [c_size_t, c_void_p]
     if path == LIB_PATH:
         _lib = lib

@@ -214,6 +214,8 @@ gptoss_status gptoss_attn_decode(const void* q, const void* k_cache, const void*
     a.k_cache = static_cast<const uint16_t*>(k_cache);
     a.v_cache = static_cast<const uint16_t*>(v_cache);
     a.cu_seqlens = cu_seqlens;
+    a.block_table = nullptr;
+    a.seq_lens = nullptr;
     a.sinks = sinks;
     a.out = static_cast<uint16_t*>(out);
     a.lse = lse;
@@ -223,8 +225,86 @@ gptoss_status gptoss_attn_decode(const void* q, const void* k_cache, const void*
     a.Hkv = Hkv;
     a.max_seqlen = max_seqlen;
     a.window = window;
+    a.page_size = 0;
+    a.pages_per_seq = 0;
+    a.ring_tokens = 0;
     a.scale = softmax_scale;
     return launched(gptoss::launch_decode(a, static_cast<hipStream_t>(stream)), "decode");
+}
+
+static bool is_pow2(long long x) { return x > 0 && (x & (x - 1)) == 0; }
+
+gptoss_status gptoss_attn_decode_paged(const void* q, const void* k_pages, const void* v_pages,
+                                       const int* block_table, const int* seq_lens, const float* sinks, int N,
+                                       int Hq, int Hkv, int D, int page_size, int pages_per_seq, int ring_tokens,
+                                       int max_seqlen, int window, float softmax_scale, void* out, float* lse,
+                                       void* workspace, size_t workspace_bytes, void* stream) {
+    if (N < 0) return fail(GPTOSS_ERR_INVALID_ARGUMENT, "N (%d) must be >= 0", N);
+    if (max_seqlen < 1) return fail(GPTOSS_ERR_INVALID_ARGUMENT, "max_seqlen (%d) must be >= 1", max_seqlen);
+    gptoss_status st = check_common(Hq, Hkv, D, window, softmax_scale);
+    if (st != GPTOSS_OK) return st;
+    if (!is_pow2(page_size) || page_size > 65536)
+        return fail(GPTOSS_ERR_INVALID_ARGUMENT, "page_size (%d) must be a power of two in [1, 65536]", page_size);
+    if (pages_per_seq < 1) return fail(GPTOSS_ERR_INVALID_ARGUMENT, "pages_per_seq (%d) must be >= 1", pages_per_seq);
+    if (ring_tokens < 0) return fail(GPTOSS_ERR_INVALID_ARGUMENT, "ring_tokens (%d) must be >= 0", ring_tokens);
+    if (ring_tokens == 0) {
+        if ((long long)max_seqlen > (long long)pages_per_seq * page_size)
+            return fail(GPTOSS_ERR_INVALID_ARGUMENT,
+                        "linear cache: max_seqlen (%d) exceeds pages_per_seq * page_size (%lld)", max_seqlen,
+                        (long long)pages_per_seq * page_size);
+    } else {
+        if (window < 1 || window > ring_tokens)
+            return fail(GPTOSS_ERR_INVALID_ARGUMENT,
+                        "ring cache of %d tokens needs a window in [1, %d] (got %d)", ring_tokens, ring_tokens,
+                        window);
+        if (!is_pow2(ring_tokens) || ring_tokens % page_size != 0)
+            return fail(GPTOSS_ERR_INVALID_ARGUMENT,
+                        "ring_tokens (%d) must be a power of two and a multiple of page_size (%d)", ring_tokens,
+                        page_size);
+        if (ring_tokens / page_size > pages_per_seq)
+            return fail(GPTOSS_ERR_INVALID_ARGUMENT, "ring of %d tokens needs %d pages, pages_per_seq is %d",
+                        ring_tokens, ring_tokens / page_size, pages_per_seq);
+    }
+    if (N == 0) return ok();
+    if ((long long)N > 65535)
+        return fail(GPTOSS_ERR_INVALID_ARGUMENT, "N (%d) exceeds 65535 sequences per call", N);
+    if ((long long)N * pages_per_seq > 0x7fffffffLL)
+        return fail(GPTOSS_ERR_INVALID_ARGUMENT, "block table of %d x %d entries is too large", N, pages_per_seq);
+    CHECK_PTR(q, 16);
+    CHECK_PTR(k_pages, 16);
+    CHECK_PTR(v_pages, 16);
+    CHECK_PTR(block_table, 4);
+    CHECK_PTR(seq_lens, 4);
+    CHECK_PTR(sinks, 4);
+    CHECK_PTR(out, 16);
+    CHECK_PTR(lse, 4);
+    const size_t need = gptoss::decode_workspace_bytes(N, Hq, Hkv, max_seqlen, window);
+    if (workspace_bytes < need)
+        return fail(GPTOSS_ERR_INVALID_ARGUMENT, "workspace_bytes %zu < required %zu", workspace_bytes, need);
+    if (need > 0) CHECK_PTR(workspace, 256);
+    st = check_device();
+    if (st != GPTOSS_OK) return st;
+    gptoss::DecodeArgs a;
+    a.q = static_cast<const uint16_t*>(q);
+    a.k_cache = static_cast<const uint16_t*>(k_pages);
+    a.v_cache = static_cast<const uint16_t*>(v_pages);
+    a.cu_seqlens = nullptr;
+    a.block_table = block_table;
+    a.seq_lens = seq_lens;
+    a.sinks = sinks;
+    a.out = static_cast<uint16_t*>(out);
+    a.lse = lse;
+    a.workspace = workspace;
+    a.N = N;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.max_seqlen = max_seqlen;
+    a.window = window;
+    a.page_size = page_size;
+    a.pages_per_seq = pages_per_seq;
+    a.ring_tokens = ring_tokens;
+    a.scale = softmax_scale;
+    return launched(gptoss::launch_decode(a, static_cast<hipStream_t>(stream)), "paged decode");
 }
 
 }  // extern "C"

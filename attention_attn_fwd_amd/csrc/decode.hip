@@ -54,14 +54,22 @@ struct DecParams {
     uint16_t* out;
     float* lse;
     float* part;      // [N][Hq][n_splits][kPartStride]
+    const int* bt;    // paged cache: block table [N][pps]; nullptr for the contiguous cache
+    const int* lens;  // paged cache: L_n per sequence
+    int ps_shift, ps_mask, pps, ring_mask;  // page size = 1 << ps_shift; slot = position & ring_mask
     int Hq, Hkv, G, window, n_splits, n_hblk, max_seqlen;
     int chunk_keys;   // visible keys per chunk (a multiple of 64)
     float c;          // scale * log2(e)
 };
 
 __device__ __forceinline__ void seq_range(const DecParams& p, int n, int& base, int& L, int& vis_lo) {
-    base = p.cu[n];
-    L = min(p.cu[n + 1] - base, p.max_seqlen);
+    if (p.bt != nullptr) {
+        base = 0;
+        L = min(p.lens[n], p.max_seqlen);
+    } else {
+        base = p.cu[n];
+        L = min(p.cu[n + 1] - base, p.max_seqlen);
+    }
     vis_lo = p.window > 0 ? max(0, L - p.window) : 0;
 }
 
@@ -69,6 +77,10 @@ __device__ __forceinline__ void seq_range(const DecParams& p, int n, int& base, 
 // LDS.  (Keeping two to four tiles per wave in flight, at one wave per SIMD,
 // measured slower on the 128 x 1024 workload than one tile per wave at two
 // workgroups per CU, and so did two waves per KV head taking alternate tiles.)
+// kPaged: K/V rows are found through the block table (slot = position &
+// ring_mask, page = bt[n][slot >> ps_shift], row = slot & ps_mask); the page
+// indices of a tile are loaded one tile ahead of its K/V rows.
+template <bool kPaged>
 __global__ void __launch_bounds__(kThreads, 2)
 decode_split_kernel(DecParams p) {
     __shared__ uint4 ksm[kWaves][kTileUnits];  // one row-major K tile per wave
@@ -110,6 +122,7 @@ decode_split_kernel(DecParams p) {
     const size_t row_stride = (size_t)p.Hkv * kHeadDim;
     const uint16_t* kb = p.kc + ((size_t)base * p.Hkv + kvh) * kHeadDim;
     const uint16_t* vb = p.vc + ((size_t)base * p.Hkv + kvh) * kHeadDim;
+    const int* bt_row = kPaged ? p.bt + (size_t)n * p.pps : nullptr;
 
     bf16x8 qf[4];
     {
@@ -128,13 +141,20 @@ decode_split_kernel(DecParams p) {
     // tiles.  Rows past the chunk end re-read its last row: their scores are
     // masked to -inf, so they add exactly 0 to l and to O.
     uint4 kr[8], vr[8];
+    int pid[8];  // paged: page of each of this lane's 8 rows of the next tile to load
+    auto tile_key = [&](int t, int j) { return min(c0 + t * kTileKeys + (lane >> 3) + 8 * j, c1 - 1); };
+    auto load_pids = [&](int t) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) pid[j] = bt_row[(tile_key(t, j) & p.ring_mask) >> p.ps_shift];
+    };
     auto load_tile = [&](int t) {
-        const int t0 = c0 + t * kTileKeys;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            const size_t key = min(t0 + (lane >> 3) + 8 * j, c1 - 1);
-            kr[j] = ld16(kb + key * row_stride + 8 * (lane & 7));
-            vr[j] = ld16(vb + key * row_stride + 8 * (lane & 7));
+            const int key = tile_key(t, j);
+            size_t row = (size_t)key;
+            if (kPaged) row = ((size_t)pid[j] << p.ps_shift) + (size_t)(key & p.ring_mask & p.ps_mask);
+            kr[j] = ld16(kb + row * row_stride + 8 * (lane & 7));
+            vr[j] = ld16(vb + row * row_stride + 8 * (lane & 7));
         }
     };
 
@@ -145,7 +165,13 @@ decode_split_kernel(DecParams p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[db][r] = 0.0f;
 
-    if (n_tiles > 0) load_tile(0);
+    if (kPaged) {
+        load_pids(0);
+        load_tile(0);
+        if (n_tiles > 1) load_pids(1);
+    } else {
+        load_tile(0);  // n_tiles >= 1 here
+    }
     for (int t = 0; t < n_tiles; ++t) {
         // K and V tiles -> this wave's LDS tiles.  Only this wave touches
         // them and a wave's LDS operations complete in order, so the previous
@@ -158,7 +184,10 @@ decode_split_kernel(DecParams p) {
             vsm[wave][tile_unit((lane >> 3) + 8 * j, lane & 7)] = vr[j];
         }
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
-        if (t + 1 < n_tiles) load_tile(t + 1);  // in flight during this tile's compute
+        if (t + 1 < n_tiles) {  // in flight during this tile's compute
+            load_tile(t + 1);
+            if (kPaged && t + 2 < n_tiles) load_pids(t + 2);
+        }
         // S^T = K Q^T; A operand rows are keys in the forward's permuted
         // order, K slots 8 g + 0..7 of step ks are d = 16 ks + 8 g + 0..7
         f32x16 sacc[2];
@@ -386,8 +415,18 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
     p.chunk_keys = cp.keys;
     p.n_hblk = (p.G + 31) / 32;
     p.c = a.scale * kLog2e;
+    p.bt = a.block_table;
+    p.lens = a.seq_lens;
+    p.ps_shift = 0;
+    while (a.page_size > 0 && (1 << p.ps_shift) < a.page_size) ++p.ps_shift;
+    p.ps_mask = a.page_size > 0 ? a.page_size - 1 : 0;
+    p.pps = a.pages_per_seq;
+    p.ring_mask = a.ring_tokens > 0 ? a.ring_tokens - 1 : 0x7fffffff;
     dim3 grid(p.n_splits, ((a.Hkv + kWaves - 1) / kWaves) * p.n_hblk, a.N);
-    hipLaunchKernelGGL(decode_split_kernel, grid, dim3(kThreads), 0, stream, p);
+    if (p.bt != nullptr)
+        hipLaunchKernelGGL(decode_split_kernel<true>, grid, dim3(kThreads), 0, stream, p);
+    else
+        hipLaunchKernelGGL(decode_split_kernel<false>, grid, dim3(kThreads), 0, stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.n_splits == 1) return e;  // one chunk per sequence: nothing to merge
     if (p.n_splits <= kFewChunks)

@@ -38,14 +38,17 @@ struct BwdArgs {
 
 struct DecodeArgs {
     const uint16_t* q;
-    const uint16_t* k_cache;
-    const uint16_t* v_cache;
-    const int* cu_seqlens;
+    const uint16_t* k_cache;      // contiguous cache, or the K pages when paged
+    const uint16_t* v_cache;      // contiguous cache, or the V pages when paged
+    const int* cu_seqlens;        // contiguous cache only
+    const int* block_table;       // paged only: [N, pages_per_seq]
+    const int* seq_lens;          // paged only: [N]
     const float* sinks;
     uint16_t* out;
     float* lse;
     void* workspace;
     int N, Hq, Hkv, max_seqlen, window;
+    int page_size, pages_per_seq, ring_tokens;  // paged only (ring_tokens 0 = linear)
     float scale;
 };
 

@@ -19,8 +19,8 @@ from dataclasses import dataclass
 
 import torch
 
-__all__ = ["PrefillCase", "DecodeCase", "CONFIGS", "make_prefill", "make_dout",
-           "make_decode", "config_inputs"]
+__all__ = ["PrefillCase", "DecodeCase", "PagedDecodeCase", "CONFIGS", "make_prefill", "make_dout",
+           "make_decode", "make_paged_decode", "config_inputs"]
 
 SLIDING_WINDOW = 128
 
@@ -82,6 +82,50 @@ def make_decode(N, Hq, Hkv, D=64, max_len=1024, seed=0, lengths=None, std=1.0):
     sinks = torch.randn((Hq,), generator=gen, dtype=torch.float32)
     max_seqlen = max(1, int(lengths.max())) if N > 0 else 1
     return DecodeCase(q, kc, vc, cu.to(torch.int32), sinks, max_seqlen, 1.0 / D ** 0.5)
+
+
+@dataclass
+class PagedDecodeCase:
+    q: torch.Tensor            # bf16 [N, Hq, D]
+    k_pages: torch.Tensor      # bf16 [P, page_size, Hkv, D]
+    v_pages: torch.Tensor      # bf16 [P, page_size, Hkv, D]
+    block_table: torch.Tensor  # int32 [N, pages_per_seq]
+    seq_lens: torch.Tensor     # int32 [N]
+    sinks: torch.Tensor        # fp32 [Hq]
+    ring_tokens: int           # 0 = linear cache
+    max_seqlen: int
+    scale: float
+    full: DecodeCase           # the same sequences as one packed cache (every position kept)
+
+
+def make_paged_decode(N, Hq, Hkv, page_size, D=64, max_len=1024, seed=0, lengths=None, ring_tokens=0,
+                      spare_pages=3):
+    """A paged decode batch holding the sequences of make_decode(N, ..., seed):
+    each sequence's positions are written in order into its slots (slot t, or
+    t mod ring_tokens for a ring, so later positions overwrite earlier ones),
+    through a block table of randomly permuted page indices.  Slots never
+    written hold 1e4 (a misread would show)."""
+    full = make_decode(N, Hq, Hkv, D=D, max_len=max_len, seed=seed, lengths=lengths)
+    lens = (full.cu_seqlens[1:] - full.cu_seqlens[:-1]).tolist()
+    if ring_tokens:
+        pps = ring_tokens // page_size
+    else:
+        pps = max(1, (max(lens + [1]) + page_size - 1) // page_size)
+    n_pages = N * pps + spare_pages
+    gen = torch.Generator().manual_seed(seed + 7919)
+    perm = torch.randperm(n_pages, generator=gen)[: N * pps].to(torch.int32)
+    block_table = perm.reshape(N, pps).contiguous()
+    k_pages = torch.full((n_pages, page_size, Hkv, D), 1e4).to(torch.bfloat16)
+    v_pages = torch.full((n_pages, page_size, Hkv, D), 1e4).to(torch.bfloat16)
+    for n, L in enumerate(lens):
+        base = int(full.cu_seqlens[n])
+        for t in range(L):
+            slot = t % ring_tokens if ring_tokens else t
+            page = int(block_table[n, slot // page_size])
+            k_pages[page, slot % page_size] = full.k_cache[base + t]
+            v_pages[page, slot % page_size] = full.v_cache[base + t]
+    return PagedDecodeCase(full.q, k_pages, v_pages, block_table, torch.tensor(lens, dtype=torch.int32),
+                           full.sinks, ring_tokens, full.max_seqlen, full.scale, full)
 
 
 # The five workloads.  Each prefill config runs one sliding-window-128 layer

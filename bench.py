@@ -233,6 +233,23 @@ def main():
             g.replay()
             part_ms[(name, w)] = sorted(timed(g.replay, 1) for _ in range(3))[1] / reps
             del g
+    # training step of one full-causal layer through the autograd wrapper
+    # (forward + backward, the same kernels; timed eagerly, host marshalling
+    # included)
+    from attention_attn_fwd_amd.autograd import sink_attention
+    leaves = [[x[n].detach().requires_grad_(True) for n in ("q", "k", "v")] for x in sets]
+    sk_leaf = sinks.detach().requires_grad_(True)
+
+    def train(i):
+        qq, kk, vv = leaves[i % NSETS]
+        sink_attention(qq, kk, vv, sk_leaf, 0, scale).backward(sets[i % NSETS]["dout"])
+
+    for i in range(NSETS):
+        train(i)
+    it = iter(range(1 << 30))
+    ms_train = timed(lambda: train(next(it)), 2 * NSETS)
+    del leaves
+
     parts = {}
     for (name, w), ms in part_ms.items():
         tf = flops[(name, w)] / (ms * 1e-3) / 1e12
@@ -243,6 +260,32 @@ def main():
             "ms": round(ms, 4), "tflops": round(tf, 2), "gbs": round(gbs, 1),
             "bound": "mfma" if roof_tf >= BF16_PEAK_TFLOPS else "hbm",
             "frac_of_roof": round(tf / roof_tf, 4)}
+    # decode through a paged cache (pages of 16 tokens, the full layer) and
+    # through a ring cache of 128 slots (the sliding layer), same sequences
+    pg = synth.make_paged_decode(N, Hq, Hkv, 16, seed=1004)
+    rg = synth.make_paged_decode(N, Hq, Hkv, 16, seed=1004, ring_tokens=128)
+    pg_sets = [[t.to(dev) for t in (pg.k_pages, pg.v_pages)] for _ in range(NSETS)]
+    rg_sets = [[t.to(dev) for t in (rg.k_pages, rg.v_pages)] for _ in range(NSETS)]
+    pg_bt, rg_bt, lens_d = pg.block_table.to(dev), rg.block_table.to(dev), pg.seq_lens.to(dev)
+    for label, cs, bt, ring, w in (("decode_paged16_full", pg_sets, pg_bt, 0, 0),
+                                   ("decode_ring128_w128", rg_sets, rg_bt, 128, 128)):
+        def pfn(i, cs=cs, bt=bt, ring=ring, w=w):
+            x = sets[i % NSETS]
+            o, l = x["dec_out"][w]
+            kp, vp = cs[i % NSETS]
+            attn.decode_paged(x["dq"], kp, vp, bt, lens_d, dsinks_, dec.max_seqlen, w, dec.scale, ring_tokens=ring,
+                              out=o, lse=l, workspace=dws)
+        g = capture(lambda: [pfn(i) for i in range(reps)])
+        g.replay()
+        ms = sorted(timed(g.replay, 1) for _ in range(3))[1] / reps
+        del g
+        gbs = bytes_[("decode", w)] / (ms * 1e-3) / 1e9
+        parts[label] = {"ms": round(ms, 4), "gbs": round(gbs, 1), "bound": "hbm",
+                        "frac_of_roof": round(gbs / HBM_PEAK_GBS, 4)}
+    del pg_sets, rg_sets
+    tf_train = (flops[("fwd", 0)] + flops[("bwd", 0)]) / (ms_train * 1e-3) / 1e12
+    parts["autograd_train_full"] = {"ms": round(ms_train, 4), "tflops": round(tf_train, 2), "bound": "mfma",
+                                    "frac_of_roof": round(tf_train / BF16_PEAK_TFLOPS, 4)}
     log(json.dumps(parts, indent=1))
 
     # Dominant unit of the step: the backward entry point of the full-causal

@@ -134,6 +134,42 @@ gptoss_status gptoss_attn_decode(const void* q, const void* k_cache, const void*
                                  float softmax_scale, void* out, float* lse,
                                  void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Decode against a paged KV cache (HF blog "Tricks from OpenAI gpt-oss YOU
+ * can use with transformers", items "Continuous Batching & Paged Attention"
+ * and "Dynamic Sliding Window Layer & Cache": the cache lives in fixed-size
+ * pages named by a per-sequence block table, and a sliding layer need keep
+ * only its last W tokens).  Same operation and outputs as gptoss_attn_decode;
+ * only the addressing of K/V rows differs.
+ *   k_pages,
+ *   v_pages     bf16 [num_pages, page_size, Hkv, D]   read; page p holds
+ *               page_size token rows of Hkv heads.
+ *   block_table int32 [N, pages_per_seq], device: entry [n][i] is the page
+ *               holding slots i*page_size .. (i+1)*page_size-1 of sequence n.
+ *   seq_lens    int32 [N], device: L_n, tokens of sequence n so far (the new
+ *               token included); its query sits at position L_n - 1.
+ *   ring_tokens 0: slot of position t is t (linear cache; needs
+ *                  max_seqlen <= pages_per_seq * page_size).
+ *               R > 0: the cache of every sequence is a ring of R slots,
+ *                  position t in slot t mod R (positions t - R and before
+ *                  have been overwritten).  Needs window >= 1, window <= R,
+ *                  R a power of two, a multiple of page_size, and
+ *                  R / page_size <= pages_per_seq.
+ *   page_size   a power of two, 1 .. 65536.
+ *   workspace   gptoss_attn_decode_workspace_size(N, Hq, Hkv, D, max_seqlen,
+ *               window) bytes, 256-byte aligned; contents on entry ignored.
+ * Page indices in block_table and the seq_lens values are caller contracts
+ * (not checked); a sequence with L_n > max_seqlen sees its first max_seqlen
+ * positions only.
+ */
+gptoss_status gptoss_attn_decode_paged(const void* q, const void* k_pages, const void* v_pages,
+                                       const int* block_table, const int* seq_lens,
+                                       const float* sinks, int N, int Hq, int Hkv, int D,
+                                       int page_size, int pages_per_seq, int ring_tokens,
+                                       int max_seqlen, int window, float softmax_scale,
+                                       void* out, float* lse, void* workspace,
+                                       size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

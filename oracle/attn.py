@@ -60,7 +60,8 @@ the four invariants, and central finite differences for the backward.
 
 import numpy as np
 
-__all__ = ["allowed_mask", "ref_fwd", "ref_bwd", "ref_decode", "unmasked_pairs"]
+__all__ = ["allowed_mask", "ref_fwd", "ref_bwd", "ref_decode", "ref_decode_paged", "gather_paged",
+           "unmasked_pairs"]
 
 
 def allowed_mask(rows, keys, window):
@@ -196,3 +197,48 @@ def ref_decode(q, k_cache, v_cache, cu_seqlens, sinks, window, scale):
             out[n, h, :] = (P @ v_cache[base:base + L, c, :])[0]
             lse[n, h] = l[0]
     return out, lse
+
+
+def gather_paged(k_pages, v_pages, block_table, seq_lens, ring_tokens, window):
+    """The visible K/V rows of every sequence of a paged cache, in position
+    order, as a packed cache.
+
+    HF blog "Tricks from OpenAI gpt-oss YOU can use with transformers", items
+    "Continuous Batching & Paged Attention" (the cache lives in fixed-size
+    pages named by a per-sequence block table) and "Dynamic Sliding Window
+    Layer & Cache" (a sliding layer keeps only its last W tokens).  Position t
+    of sequence n sits in slot t (linear cache, ring_tokens = 0) or slot
+    t mod ring_tokens (ring), i.e. in page block_table[n][slot // page_size]
+    at row slot % page_size.  The visible positions are [L - W, L) (all L when
+    W = 0); in a ring, positions before L - ring_tokens have been overwritten,
+    so W <= ring_tokens is required.
+
+    k_pages, v_pages [P, page_size, Hkv, D]; block_table [N, pages_per_seq];
+    seq_lens [N].  Returns (k_cache, v_cache [T, Hkv, D], cu_seqlens [N + 1])
+    holding only the visible rows.
+    """
+    page_size = k_pages.shape[1]
+    if ring_tokens:
+        assert 1 <= window <= ring_tokens
+    ks, vs, cu = [], [], [0]
+    for n, L in enumerate(seq_lens):
+        L = int(L)
+        lo = max(0, L - window) if window > 0 else 0
+        for t in range(lo, L):
+            slot = t % ring_tokens if ring_tokens else t
+            page = int(block_table[n][slot // page_size])
+            ks.append(k_pages[page, slot % page_size])
+            vs.append(v_pages[page, slot % page_size])
+        cu.append(cu[-1] + (L - lo))
+    Hkv, D = k_pages.shape[2], k_pages.shape[3]
+    kc = np.array(ks).reshape(-1, Hkv, D) if ks else np.zeros((0, Hkv, D))
+    vc = np.array(vs).reshape(-1, Hkv, D) if vs else np.zeros((0, Hkv, D))
+    return kc, vc, np.array(cu)
+
+
+def ref_decode_paged(q, k_pages, v_pages, block_table, seq_lens, sinks, ring_tokens, window, scale):
+    """Decode against a paged cache: the query of sequence n (position L_n - 1)
+    over its visible rows read through the block table (gather_paged); the
+    attention itself is ref_decode on those rows (all of them visible)."""
+    kc, vc, cu = gather_paged(k_pages, v_pages, block_table, seq_lens, ring_tokens, window)
+    return ref_decode(q, kc, vc, cu, sinks, 0, scale)

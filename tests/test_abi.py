@@ -158,3 +158,47 @@ def test_error_message_cleared_on_success(lib):
     assert lib.gptoss_attn_last_error().decode() != ""
     assert _fwd(lib, B=0) == 0
     assert lib.gptoss_attn_last_error().decode() == ""
+
+
+def _paged(lib, **kw):
+    a = dict(q=P, kp=P, vp=P, bt=P, lens=P, sinks=P, N=2, Hq=64, Hkv=8, D=64, page_size=16, pps=64, ring=0,
+             max_seqlen=1024, window=0, scale=0.125, out=P, lse=P, ws=P, ws_bytes=None)
+    a.update(kw)
+    need = lib.gptoss_attn_decode_workspace_size(a["N"], a["Hq"], a["Hkv"], a["D"], a["max_seqlen"], a["window"])
+    wb = need if a["ws_bytes"] is None else a["ws_bytes"]
+    return lib.gptoss_attn_decode_paged(a["q"], a["kp"], a["vp"], a["bt"], a["lens"], a["sinks"], a["N"], a["Hq"],
+                                        a["Hkv"], a["D"], a["page_size"], a["pps"], a["ring"], a["max_seqlen"],
+                                        a["window"], a["scale"], a["out"], a["lse"], a["ws"], wb, None)
+
+
+@pytest.mark.parametrize("kw,frag", [
+    (dict(bt=None), "block_table is NULL"),
+    (dict(lens=None), "seq_lens is NULL"),
+    (dict(page_size=24), "power of two"),
+    (dict(page_size=0), "power of two"),
+    (dict(pps=0), "pages_per_seq"),
+    (dict(max_seqlen=1025), "linear cache"),
+    (dict(ring=128, window=0), "window"),
+    (dict(ring=128, window=129), "window"),
+    (dict(ring=96, window=64), "power of two"),
+    (dict(ring=8, window=8), "multiple of page_size"),
+    (dict(ring=2048, window=128), "pages"),
+    (dict(ring=-1), "ring_tokens"),
+    (dict(kp=P + 2), "aligned"),
+])
+def test_paged_decode_rejects_bad_arguments(lib, kw, frag):
+    assert _paged(lib, **kw) == 1
+    assert frag in lib.gptoss_attn_last_error().decode()
+
+
+def test_paged_decode_zero_sequences_is_a_noop(lib):
+    assert _paged(lib, N=0, q=None, kp=None, vp=None, bt=None, lens=None, out=None, lse=None, ws=None) == 0
+
+
+def test_autograd_wrapper_refuses_host_tensors():
+    import torch
+    from attention_attn_fwd_amd.autograd import sink_attention
+    q = torch.zeros(1, 4, 8, 64, dtype=torch.bfloat16)
+    k = torch.zeros(1, 4, 1, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="HIP device"):
+        sink_attention(q, k, k, torch.zeros(8), 0)
