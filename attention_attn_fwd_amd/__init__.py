@@ -10,6 +10,8 @@ all computation runs in the library's HIP kernels.
     out, lse = decode(q, k_cache, v_cache, cu_seqlens, sinks, max_seqlen, window, scale)
     out, lse = decode_paged(q, k_pages, v_pages, block_table, seq_lens, sinks, max_seqlen, window, scale,
                             ring_tokens)
+    out, lse = fwd_varlen(q, k, v, cu_seqlens, sinks, max_seqlen, window, scale)     # packed documents
+    dq, dk, dv, dsinks = bwd_varlen(q, k, v, cu_seqlens, sinks, out, lse, dout, max_seqlen, window, scale)
 
 Training: attention_attn_fwd_amd.autograd.sink_attention (torch autograd over
 fwd/bwd).
@@ -20,8 +22,8 @@ import torch
 from . import _lib
 from ._lib import AttnError
 
-__all__ = ["fwd", "bwd", "decode", "decode_paged", "bwd_workspace_size", "decode_workspace_size", "AttnError",
-           "abi_version"]
+__all__ = ["fwd", "bwd", "decode", "decode_paged", "fwd_varlen", "bwd_varlen", "bwd_workspace_size",
+           "bwd_varlen_workspace_size", "decode_workspace_size", "AttnError", "abi_version"]
 
 
 def _need(t, name, dtype, ndim):
@@ -180,3 +182,85 @@ def decode_paged(q, k_pages, v_pages, block_table, seq_lens, sinks, max_seqlen, 
                                       _stream(q.device))
     _lib.check(st, lib)
     return out, lse
+
+
+def fwd_varlen(q, k, v, cu_seqlens, sinks, max_seqlen, window=0, scale=None, out=None, lse=None):
+    """Prefill forward over documents packed along the token dimension.
+
+    q [T,Hq,D], k/v [T,Hkv,D] bf16; cu_seqlens int32 [N+1] on the device
+    (document b = rows cu_seqlens[b] .. cu_seqlens[b+1]-1, attention confined
+    to it); max_seqlen bounds every document length.  Returns
+    (out bf16 [T,Hq,D], lse fp32 [Hq,T]); rows outside every document are not
+    written.
+    """
+    _need(q, "q", torch.bfloat16, 3)
+    _need(k, "k", torch.bfloat16, 3)
+    _need(v, "v", torch.bfloat16, 3)
+    _need(cu_seqlens, "cu_seqlens", torch.int32, 1)
+    _need(sinks, "sinks", torch.float32, 1)
+    T, Hq, D = q.shape
+    Hkv = k.shape[1]
+    N = cu_seqlens.shape[0] - 1
+    if N < 0 or k.shape != (T, Hkv, D) or v.shape != k.shape or sinks.shape != (Hq,):
+        raise ValueError("shape mismatch among q, k, v, cu_seqlens, sinks")
+    scale = (1.0 / D ** 0.5) if scale is None else float(scale)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((Hq, T), dtype=torch.float32, device=q.device)
+    _need(out, "out", torch.bfloat16, 3)
+    _need(lse, "lse", torch.float32, 2)
+    if out.shape != q.shape or lse.shape != (Hq, T):
+        raise ValueError("out must be [T,Hq,D] and lse [Hq,T]")
+    lib = _lib.load()
+    st = lib.gptoss_attn_fwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), cu_seqlens.data_ptr(),
+                                    sinks.data_ptr(), N, T, Hq, Hkv, D, int(max_seqlen), int(window), scale,
+                                    out.data_ptr(), lse.data_ptr(), _stream(q.device))
+    _lib.check(st, lib)
+    return out, lse
+
+
+def bwd_varlen_workspace_size(T, Hq, Hkv, D=64):
+    return int(_lib.load().gptoss_attn_bwd_varlen_workspace_size(T, Hq, Hkv, D))
+
+
+def bwd_varlen(q, k, v, cu_seqlens, sinks, out, lse, dout, max_seqlen, window=0, scale=None, workspace=None,
+               grads=None):
+    """Backward of fwd_varlen for sum(dout * out).  Returns (dq, dk, dv bf16,
+    dsinks fp32 [Hq]), written into `grads` = (dq, dk, dv, dsinks) when given;
+    rows outside every document are not written."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (out, "out"), (dout, "dout")):
+        _need(t, n, torch.bfloat16, 3)
+    _need(cu_seqlens, "cu_seqlens", torch.int32, 1)
+    _need(sinks, "sinks", torch.float32, 1)
+    _need(lse, "lse", torch.float32, 2)
+    T, Hq, D = q.shape
+    Hkv = k.shape[1]
+    N = cu_seqlens.shape[0] - 1
+    if (N < 0 or k.shape != (T, Hkv, D) or v.shape != k.shape or out.shape != q.shape or dout.shape != q.shape
+            or lse.shape != (Hq, T) or sinks.shape != (Hq,)):
+        raise ValueError("shape mismatch among varlen backward inputs")
+    scale = (1.0 / D ** 0.5) if scale is None else float(scale)
+    if grads is None:
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        dsinks = torch.empty((Hq,), dtype=torch.float32, device=q.device)
+    else:
+        dq, dk, dv, dsinks = grads
+        for t, n, ref in ((dq, "dq", q), (dk, "dk", k), (dv, "dv", v)):
+            _need(t, n, torch.bfloat16, 3)
+            if t.shape != ref.shape:
+                raise ValueError(f"{n} must have shape {tuple(ref.shape)}")
+        _need(dsinks, "dsinks", torch.float32, 1)
+        if dsinks.shape != (Hq,):
+            raise ValueError(f"dsinks must have shape ({Hq},)")
+    need = bwd_varlen_workspace_size(T, Hq, Hkv, D)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    lib = _lib.load()
+    st = lib.gptoss_attn_bwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), cu_seqlens.data_ptr(),
+                                    sinks.data_ptr(), out.data_ptr(), lse.data_ptr(), dout.data_ptr(), N, T, Hq,
+                                    Hkv, D, int(max_seqlen), int(window), scale, dq.data_ptr(), dk.data_ptr(),
+                                    dv.data_ptr(), dsinks.data_ptr(), workspace.data_ptr(), workspace.numel(),
+                                    _stream(q.device))
+    _lib.check(st, lib)
+    return dq, dk, dv, dsinks

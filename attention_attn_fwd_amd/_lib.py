@@ -18,6 +18,7 @@ EXPORTS = [
     "gptoss_attn_abi_version", "gptoss_attn_last_error", "gptoss_attn_fwd",
     "gptoss_attn_bwd_workspace_size", "gptoss_attn_bwd",
     "gptoss_attn_decode_workspace_size", "gptoss_attn_decode", "gptoss_attn_decode_paged",
+    "gptoss_attn_fwd_varlen", "gptoss_attn_bwd_varlen_workspace_size", "gptoss_attn_bwd_varlen",
 ]
 
 _lib = None
@@ -60,6 +61,13 @@ def load(path=None):
         [c_size_t, c_void_p]
     lib.gptoss_attn_decode_paged.restype = c_int
     lib.gptoss_attn_decode_paged.argtypes = [c_void_p] * 6 + [c_int] * 9 + [c_float] + [c_void_p] * 3 + \
+        [c_size_t, c_void_p]
+    lib.gptoss_attn_fwd_varlen.restype = c_int
+    lib.gptoss_attn_fwd_varlen.argtypes = [c_void_p] * 5 + [c_int] * 7 + [c_float] + [c_void_p] * 3
+    lib.gptoss_attn_bwd_varlen_workspace_size.restype = c_size_t
+    lib.gptoss_attn_bwd_varlen_workspace_size.argtypes = [c_int] * 4
+    lib.gptoss_attn_bwd_varlen.restype = c_int
+    lib.gptoss_attn_bwd_varlen.argtypes = [c_void_p] * 8 + [c_int] * 7 + [c_float] + [c_void_p] * 5 + \
         [c_size_t, c_void_p]
     if path == LIB_PATH:
         _lib = lib

@@ -117,8 +117,10 @@ gptoss_status gptoss_attn_fwd(const void* q, const void* k, const void* v, const
     a.sinks = sinks;
     a.out = static_cast<uint16_t*>(out);
     a.lse = lse;
+    a.cu = nullptr;
     a.B = B;
     a.S = S;
+    a.T = B * S;
     a.Hq = Hq;
     a.Hkv = Hkv;
     a.window = window;
@@ -128,7 +130,7 @@ gptoss_status gptoss_attn_fwd(const void* q, const void* k, const void* v, const
 
 size_t gptoss_attn_bwd_workspace_size(int B, int S, int Hq, int Hkv, int D, int window) {
     if (B <= 0 || S <= 0 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || D != 64 || window < 0) return 0;
-    return gptoss::bwd_workspace_bytes(B, S, Hq, Hkv, window);
+    return gptoss::bwd_workspace_bytes((long long)B * S, Hq);
 }
 
 gptoss_status gptoss_attn_bwd(const void* q, const void* k, const void* v, const float* sinks, const void* out,
@@ -152,7 +154,7 @@ gptoss_status gptoss_attn_bwd(const void* q, const void* k, const void* v, const
     CHECK_PTR(dk, 16);
     CHECK_PTR(dv, 16);
     CHECK_PTR(dsinks, 4);
-    const size_t need = gptoss::bwd_workspace_bytes(B, S, Hq, Hkv, window);
+    const size_t need = gptoss::bwd_workspace_bytes((long long)B * S, Hq);
     if (workspace_bytes < need)
         return fail(GPTOSS_ERR_INVALID_ARGUMENT, "workspace_bytes %zu < required %zu", workspace_bytes, need);
     if (need > 0) CHECK_PTR(workspace, 256);
@@ -171,13 +173,115 @@ gptoss_status gptoss_attn_bwd(const void* q, const void* k, const void* v, const
     a.dv = static_cast<uint16_t*>(dv);
     a.dsinks = dsinks;
     a.workspace = workspace;
+    a.cu = nullptr;
     a.B = B;
     a.S = S;
+    a.T = B * S;
     a.Hq = Hq;
     a.Hkv = Hkv;
     a.window = window;
     a.scale = softmax_scale;
     return launched(gptoss::launch_bwd(a, static_cast<hipStream_t>(stream)), "backward");
+}
+
+// Packed variable-length batches: shape checks shared by the two entry points.
+static gptoss_status check_varlen(int N, int T, int max_seqlen) {
+    if (N < 0 || T < 0) return fail(GPTOSS_ERR_INVALID_ARGUMENT, "N (%d) and T (%d) must be >= 0", N, T);
+    if (max_seqlen < 1) return fail(GPTOSS_ERR_INVALID_ARGUMENT, "max_seqlen (%d) must be >= 1", max_seqlen);
+    if (N > 65535) return fail(GPTOSS_ERR_INVALID_ARGUMENT, "N (%d) exceeds 65535 documents per call", N);
+    return GPTOSS_OK;
+}
+
+gptoss_status gptoss_attn_fwd_varlen(const void* q, const void* k, const void* v, const int* cu_seqlens,
+                                     const float* sinks, int N, int T, int Hq, int Hkv, int D, int max_seqlen,
+                                     int window, float softmax_scale, void* out, float* lse, void* stream) {
+    gptoss_status st = check_varlen(N, T, max_seqlen);
+    if (st != GPTOSS_OK) return st;
+    st = check_common(Hq, Hkv, D, window, softmax_scale);
+    if (st != GPTOSS_OK) return st;
+    if (N == 0 || T == 0) return ok();
+    CHECK_PTR(q, 16);
+    CHECK_PTR(k, 16);
+    CHECK_PTR(v, 16);
+    CHECK_PTR(cu_seqlens, 4);
+    CHECK_PTR(sinks, 4);
+    CHECK_PTR(out, 16);
+    CHECK_PTR(lse, 4);
+    st = check_device();
+    if (st != GPTOSS_OK) return st;
+    gptoss::FwdArgs a;
+    a.q = static_cast<const uint16_t*>(q);
+    a.k = static_cast<const uint16_t*>(k);
+    a.v = static_cast<const uint16_t*>(v);
+    a.sinks = sinks;
+    a.out = static_cast<uint16_t*>(out);
+    a.lse = lse;
+    a.cu = cu_seqlens;
+    a.B = N;
+    a.S = max_seqlen;
+    a.T = T;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.window = window;
+    a.scale = softmax_scale;
+    return launched(gptoss::launch_fwd(a, static_cast<hipStream_t>(stream)), "varlen forward");
+}
+
+size_t gptoss_attn_bwd_varlen_workspace_size(int T, int Hq, int Hkv, int D) {
+    if (T <= 0 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || D != 64) return 0;
+    return gptoss::bwd_workspace_bytes(T, Hq);
+}
+
+gptoss_status gptoss_attn_bwd_varlen(const void* q, const void* k, const void* v, const int* cu_seqlens,
+                                     const float* sinks, const void* out, const float* lse, const void* dout, int N,
+                                     int T, int Hq, int Hkv, int D, int max_seqlen, int window, float softmax_scale,
+                                     void* dq, void* dk, void* dv, float* dsinks, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
+    gptoss_status st = check_varlen(N, T, max_seqlen);
+    if (st != GPTOSS_OK) return st;
+    st = check_common(Hq, Hkv, D, window, softmax_scale);
+    if (st != GPTOSS_OK) return st;
+    if (N == 0 || T == 0) return ok();
+    CHECK_PTR(q, 16);
+    CHECK_PTR(k, 16);
+    CHECK_PTR(v, 16);
+    CHECK_PTR(cu_seqlens, 4);
+    CHECK_PTR(sinks, 4);
+    CHECK_PTR(out, 16);
+    CHECK_PTR(lse, 4);
+    CHECK_PTR(dout, 16);
+    CHECK_PTR(dq, 16);
+    CHECK_PTR(dk, 16);
+    CHECK_PTR(dv, 16);
+    CHECK_PTR(dsinks, 4);
+    const size_t need = gptoss::bwd_workspace_bytes(T, Hq);
+    if (workspace_bytes < need)
+        return fail(GPTOSS_ERR_INVALID_ARGUMENT, "workspace_bytes %zu < required %zu", workspace_bytes, need);
+    CHECK_PTR(workspace, 256);
+    st = check_device();
+    if (st != GPTOSS_OK) return st;
+    gptoss::BwdArgs a;
+    a.q = static_cast<const uint16_t*>(q);
+    a.k = static_cast<const uint16_t*>(k);
+    a.v = static_cast<const uint16_t*>(v);
+    a.sinks = sinks;
+    a.out = static_cast<const uint16_t*>(out);
+    a.lse = lse;
+    a.dout = static_cast<const uint16_t*>(dout);
+    a.dq = static_cast<uint16_t*>(dq);
+    a.dk = static_cast<uint16_t*>(dk);
+    a.dv = static_cast<uint16_t*>(dv);
+    a.dsinks = dsinks;
+    a.workspace = workspace;
+    a.cu = cu_seqlens;
+    a.B = N;
+    a.S = max_seqlen;
+    a.T = T;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.window = window;
+    a.scale = softmax_scale;
+    return launched(gptoss::launch_bwd(a, static_cast<hipStream_t>(stream)), "varlen backward");
 }
 
 size_t gptoss_attn_decode_workspace_size(int N, int Hq, int Hkv, int D, int max_seqlen, int window) {

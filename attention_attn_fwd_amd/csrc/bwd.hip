@@ -26,7 +26,7 @@
 //            put one column per lane, which is the operand layout of
 //            dQ^T += K^T dS^T (K^T through transposing LDS reads).
 //   dsink  : one workgroup per head reduces the per-row terms the dq kernel
-//            left in the workspace ([head][batch][position], contiguous).
+//            left in the workspace ([head][token row], contiguous).
 // P and dP are recomputed in both the key-outer and query-outer kernels.
 // dsink does not use Dvec = <dout, out>, whose bf16 `out` carries rounding
 // that a cancelling sum over all rows would amplify: the dq kernel forms
@@ -53,9 +53,11 @@ struct BwdParams {
     uint16_t* dk;
     uint16_t* dv;
     float* dsinks;
-    float2* ld;      // [B][S][Hq] {lse * log2(e), Dvec}
-    float* dsterm;   // [Hq][B][S] exp(sink - lse) * sum_j P dP per row
-    int B, S, Hq, Hkv, G, window;
+    float2* ld;      // [T][Hq] {lse * log2(e), Dvec} per token row and head
+    float* dsterm;   // [Hq][T] exp(sink - lse) * sum_j P dP per row
+    const int* cu;   // packed documents: sequence b = rows cu[b] .. cu[b+1]-1; nullptr = dense batch
+    int B, S, Hq, Hkv, G, window;  // S = sequence length (dense) or the longest document (packed)
+    int T;           // total token rows (B * S when dense)
     float scale;
     float c;  // scale * log2(e)
 };
@@ -82,11 +84,18 @@ bwd_pre_kernel(BwdParams p, long long rows) {
     acc += __shfl_xor(acc, 4);
     if (row < rows && chunk == 0) {
         const int h = (int)(row % p.Hq);
-        const long long bs = row / p.Hq;
-        const int pos = (int)(bs % p.S);
-        const int b = (int)(bs / p.S);
-        const float l = p.lse[((size_t)b * p.Hq + h) * p.S + pos];
-        p.ld[row] = make_float2(l * kLog2e, acc);
+        const int tok = (int)(row / p.Hq);
+        size_t li;
+        if (p.cu == nullptr) {
+            const int b = tok / p.S, pos = tok % p.S;
+            li = ((size_t)b * p.Hq + h) * p.S + pos;
+        } else {
+            li = (size_t)h * p.T + tok;
+            // rows outside every document keep a zero dsink term (the dq
+            // kernel overwrites the rows it covers)
+            p.dsterm[li] = 0.0f;
+        }
+        p.ld[row] = make_float2(p.lse[li] * kLog2e, acc);
     }
 }
 
@@ -96,7 +105,7 @@ __global__ void __launch_bounds__(kThreads)
 bwd_dsink_kernel(BwdParams p) {
     __shared__ float red[kThreads / 64];
     const int h = blockIdx.x;
-    const long long n = (long long)p.B * p.S;
+    const long long n = p.T;
     const float* src = p.dsterm + (size_t)h * n;
     float a0 = 0.0f, a1 = 0.0f, a2 = 0.0f, a3 = 0.0f;
     const long long n4 = ((size_t)h * n) % 4 == 0 ? n / 4 : 0;  // float4 part (rows start 16-byte aligned)
@@ -131,7 +140,10 @@ __device__ __forceinline__ void dkdv_coords(const BwdParams& p, int n_kt, int bi
     if ((n_groups & 7) == 0) {
         const int xcd = bid & 7, slot = bid >> 3;
         // tile-major within the XCD: the heaviest key tiles (lowest, seen by
-        // the most queries) of all the XCD's groups are dispatched first
+        // the most queries) of all the XCD's groups are dispatched first.
+        // Groups are KV-head-major, so with 8 KV heads each XCD takes one KV
+        // head of every sequence: equal work per XCD even when packed
+        // documents differ in length.
         const int gpx = n_groups >> 3;
         grp = xcd * gpx + slot % gpx;
         kt = slot / gpx;
@@ -153,10 +165,12 @@ bwd_dkdv_kernel(BwdParams p, int n_kt) {
     const int g = lane >> 5, l32 = lane & 31, i16 = lane & 15;
     int grp, kt;
     dkdv_coords(p, n_kt, blockIdx.x, grp, kt);
-    const int b = grp / p.Hkv, kvh = grp % p.Hkv;
-    const int S = p.S, W = p.window, G = p.G, Hq = p.Hq;
+    const int kvh = grp / p.B, b = grp % p.B;  // KV-head-major groups
+    const SeqRows sr = seq_rows(p.cu, p.S, p.Hq, p.T, b);
+    const int S = sr.len, W = p.window, G = p.G, Hq = p.Hq;
     const unsigned Weff = W > 0 ? (unsigned)W : 0x7fffffffu;
     const int k0 = kt * kKeysPerBlock;
+    if (k0 >= S) return;  // a document shorter than the longest one
     const int kw0 = k0 + 32 * wave;          // this wave's keys kw0 .. kw0+31
     const int kw1 = min(kw0 + 31, S - 1);
     const bool wave_active = kw0 < S;
@@ -171,7 +185,7 @@ bwd_dkdv_kernel(BwdParams p, int n_kt) {
     const size_t kv_stride = (size_t)p.Hkv * kHeadDim;
     bf16x8 kb[4], vb[4];
     {
-        const size_t off = ((size_t)b * S + my_key) * kv_stride + (size_t)kvh * kHeadDim;
+        const size_t off = ((size_t)sr.row0 + my_key) * kv_stride + (size_t)kvh * kHeadDim;
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
             uint4 x = make_uint4(0, 0, 0, 0), y = make_uint4(0, 0, 0, 0);
@@ -208,9 +222,9 @@ bwd_dkdv_kernel(BwdParams p, int n_kt) {
     const int st_row = tid >> 3, st_unit = tid & 7;
     const bool g64 = (kColsPerStep % G) == 0;
     const size_t pos_stride = (size_t)Hq * kHeadDim;  // elements per position
-    const uint16_t* qcol_base = p.q + (((size_t)b * S) * Hq + (size_t)kvh * G) * kHeadDim + 8 * st_unit;
-    const uint16_t* ocol_base = p.dout + (((size_t)b * S) * Hq + (size_t)kvh * G) * kHeadDim + 8 * st_unit;
-    const float2* ld_base = p.ld + ((size_t)b * S) * Hq + (size_t)kvh * G;
+    const uint16_t* qcol_base = p.q + ((size_t)sr.row0 * Hq + (size_t)kvh * G) * kHeadDim + 8 * st_unit;
+    const uint16_t* ocol_base = p.dout + ((size_t)sr.row0 * Hq + (size_t)kvh * G) * kHeadDim + 8 * st_unit;
+    const float2* ld_base = p.ld + (size_t)sr.row0 * Hq + (size_t)kvh * G;
     uint4 rq[2], ro[2];
     float2 rld = make_float2(INFINITY, 0.0f);
     int rpos = 0x3fffffff;
@@ -361,7 +375,7 @@ bwd_dkdv_kernel(BwdParams p, int n_kt) {
 
     // epilogue: lane = key, registers = d rows (acc_row); 4 contiguous d per store
     if (my_key < S) {
-        const size_t off = ((size_t)b * S + my_key) * kv_stride + (size_t)kvh * kHeadDim;
+        const size_t off = ((size_t)sr.row0 + my_key) * kv_stride + (size_t)kvh * kHeadDim;
 #pragma unroll
         for (int db = 0; db < 2; ++db)
 #pragma unroll
@@ -406,10 +420,12 @@ bwd_dq_kernel(BwdParams p, int n_qt, int pos_per_block) {
     const int g = lane >> 5, l32 = lane & 31, i16 = lane & 15;
     int grp, qt;
     dq_coords(p, n_qt, blockIdx.x, grp, qt);
-    const int b = grp / p.Hkv, kvh = grp % p.Hkv;
-    const int S = p.S, W = p.window, G = p.G, Hq = p.Hq;
+    const int kvh = grp / p.B, b = grp % p.B;  // KV-head-major groups
+    const SeqRows sr = seq_rows(p.cu, p.S, p.Hq, p.T, b);
+    const int S = sr.len, W = p.window, G = p.G, Hq = p.Hq;
     const unsigned Weff = W > 0 ? (unsigned)W : 0x7fffffffu;
     const int p0 = qt * pos_per_block;
+    if (p0 >= S) return;  // a document shorter than the longest one
     const int used_cols = pos_per_block * G;
     const int P1 = min(p0 + pos_per_block, S) - 1;
 
@@ -425,7 +441,7 @@ bwd_dq_kernel(BwdParams p, int n_qt, int pos_per_block) {
     bf16x8 qf[4], of[4];
     float lse2 = INFINITY, dvec = 0.0f, rsum = 0.0f;
     {
-        const size_t off = (((size_t)b * S + col_pos) * Hq + col_head) * kHeadDim;
+        const size_t off = (((size_t)sr.row0 + col_pos) * Hq + col_head) * kHeadDim;
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
             uint4 x = make_uint4(0, 0, 0, 0), y = make_uint4(0, 0, 0, 0);
@@ -437,7 +453,7 @@ bwd_dq_kernel(BwdParams p, int n_qt, int pos_per_block) {
             of[ks] = as_bf16x8(y);
         }
         if (col_ok) {
-            const float2 v = p.ld[((size_t)b * S + col_pos) * Hq + col_head];
+            const float2 v = p.ld[((size_t)sr.row0 + col_pos) * Hq + col_head];
             lse2 = v.x;
             dvec = v.y;
         }
@@ -454,8 +470,8 @@ bwd_dq_kernel(BwdParams p, int n_qt, int pos_per_block) {
     const int t_end = P1 / kBk;
 
     const size_t kv_stride = (size_t)p.Hkv * kHeadDim;
-    const uint16_t* kbase = p.k + ((size_t)b * S * p.Hkv + kvh) * kHeadDim;
-    const uint16_t* vbase = p.v + ((size_t)b * S * p.Hkv + kvh) * kHeadDim;
+    const uint16_t* kbase = p.k + ((size_t)sr.row0 * p.Hkv + kvh) * kHeadDim;
+    const uint16_t* vbase = p.v + ((size_t)sr.row0 * p.Hkv + kvh) * kHeadDim;
     const int st_row = tid >> 3, st_unit = tid & 7;
     uint4 rk[2], rv[2];
     auto load_tile = [&](int t) {
@@ -466,8 +482,8 @@ bwd_dq_kernel(BwdParams p, int n_qt, int pos_per_block) {
             rk[j] = make_uint4(0, 0, 0, 0);
             rv[j] = make_uint4(0, 0, 0, 0);
             if (key < S) {
-                rk[j] = ld16(kbase + key * kv_stride + 8 * st_unit);
-                rv[j] = ld16(vbase + key * kv_stride + 8 * st_unit);
+                rk[j] = ld16(kbase + row_off(key, (uint32_t)kv_stride) + 8 * st_unit);
+                rv[j] = ld16(vbase + row_off(key, (uint32_t)kv_stride) + 8 * st_unit);
             }
         }
     };
@@ -557,9 +573,9 @@ bwd_dq_kernel(BwdParams p, int n_qt, int pos_per_block) {
         if (g == 0) {
             // this row's dsink term; the row's own Q/dO/lse were read above
             const float s2 = p.sinks[col_head] * kLog2e;
-            p.dsterm[((size_t)col_head * p.B + b) * S + col_pos] = fast_exp2(s2 - lse2) * rsum;
+            p.dsterm[(size_t)col_head * p.T + sr.row0 + col_pos] = fast_exp2(s2 - lse2) * rsum;
         }
-        uint16_t* row = p.dq + (((size_t)b * S + col_pos) * Hq + col_head) * kHeadDim;
+        uint16_t* row = p.dq + (((size_t)sr.row0 + col_pos) * Hq + col_head) * kHeadDim;
 #pragma unroll
         for (int db = 0; db < 2; ++db)
 #pragma unroll
@@ -577,14 +593,12 @@ bwd_dq_kernel(BwdParams p, int n_qt, int pos_per_block) {
 
 // Workspace: {lse * log2(e), Dvec} per row, then (256-byte aligned) one
 // dsink term per row.
-static size_t ld_region_bytes(int B, int S, int Hq) {
-    return ((size_t)B * S * Hq * sizeof(float2) + 255) / 256 * 256;
+static size_t ld_region_bytes(long long total_rows, int Hq) {
+    return ((size_t)total_rows * Hq * sizeof(float2) + 255) / 256 * 256;
 }
 
-size_t bwd_workspace_bytes(int B, int S, int Hq, int Hkv, int window) {
-    (void)Hkv;
-    (void)window;
-    return ld_region_bytes(B, S, Hq) + (size_t)B * S * Hq * sizeof(float);
+size_t bwd_workspace_bytes(long long total_rows, int Hq) {
+    return ld_region_bytes(total_rows, Hq) + (size_t)total_rows * Hq * sizeof(float);
 }
 
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
@@ -601,9 +615,11 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
     p.dv = a.dv;
     p.dsinks = a.dsinks;
     p.ld = static_cast<float2*>(a.workspace);
-    p.dsterm = reinterpret_cast<float*>(static_cast<char*>(a.workspace) + ld_region_bytes(a.B, a.S, a.Hq));
+    p.dsterm = reinterpret_cast<float*>(static_cast<char*>(a.workspace) + ld_region_bytes(a.T, a.Hq));
+    p.cu = a.cu;
     p.B = a.B;
     p.S = a.S;
+    p.T = a.T;
     p.Hq = a.Hq;
     p.Hkv = a.Hkv;
     p.G = a.Hq / a.Hkv;
@@ -611,15 +627,17 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
     p.scale = a.scale;
     p.c = a.scale * kLog2e;
 
-    const long long rows = (long long)a.B * a.S * a.Hq;
+    const long long rows = (long long)a.T * a.Hq;
+    const int n_kt = (a.S + kKeysPerBlock - 1) / kKeysPerBlock;
+    const int ppb = kDqCols / p.G >= 1 ? kDqCols / p.G : 1;
+    const int n_qt = (a.S + ppb - 1) / ppb;
+    if ((rows + 31) / 32 > 0x7fffffffLL || (long long)n_qt * a.B * a.Hkv > 0x7fffffffLL)
+        return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL(bwd_pre_kernel, dim3((unsigned)((rows + 31) / 32)), dim3(kThreads), 0, stream, p, rows);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int n_kt = (a.S + kKeysPerBlock - 1) / kKeysPerBlock;
     hipLaunchKernelGGL(bwd_dkdv_kernel, dim3((unsigned)(n_kt * a.B * a.Hkv)), dim3(kThreads), 0, stream, p, n_kt);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    const int ppb = kDqCols / p.G >= 1 ? kDqCols / p.G : 1;
-    const int n_qt = (a.S + ppb - 1) / ppb;
     hipLaunchKernelGGL(bwd_dq_kernel, dim3((unsigned)(n_qt * a.B * a.Hkv)), dim3(kThreads), 0, stream, p, n_qt, ppb);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(bwd_dsink_kernel, dim3(a.Hq), dim3(kThreads), 0, stream, p);

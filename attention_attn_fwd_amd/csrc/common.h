@@ -121,4 +121,36 @@ __device__ __forceinline__ bf16x8 tile_read_tr8(const uint4* tile, int r0, int c
     return __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
 }
 
+// Element offset of row `row` (>= 0) of a tensor with `stride` elements per
+// row, as one 32 x 32 -> 64-bit multiply (v_mad_u64_u32).  (A 64-bit stride
+// makes the compiler add a high-half product whose don't-care addend
+// register can alias a load still in flight, which costs a full wait.)
+__device__ __forceinline__ size_t row_off(int row, uint32_t stride) { return (size_t)(uint32_t)row * stride; }
+
+// Rows of sequence b in a [token, head, d] tensor.  A dense batch
+// (cu == nullptr) puts sequence b at rows b * S .. b * S + S - 1; a packed
+// batch of variable-length documents puts it at rows cu[b] .. cu[b + 1] - 1,
+// with the length capped at S (the longest document the grid covers).
+// lse is [B][H][S] for a dense batch and [H][total rows] for a packed one:
+// entry (b, h, pos) sits at lse_base + h * lse_hstride + pos.
+struct SeqRows {
+    int row0, len;
+    size_t lse_base, lse_hstride;
+};
+__device__ __forceinline__ SeqRows seq_rows(const int* cu, int S, int H, int total_rows, int b) {
+    SeqRows r;
+    if (cu == nullptr) {
+        r.row0 = b * S;
+        r.len = S;
+        r.lse_base = (size_t)b * H * S;
+        r.lse_hstride = (size_t)S;
+    } else {
+        r.row0 = cu[b];
+        r.len = min(cu[b + 1] - r.row0, S);
+        r.lse_base = (size_t)r.row0;
+        r.lse_hstride = (size_t)total_rows;
+    }
+    return r;
+}
+
 }  // namespace gptoss

@@ -53,10 +53,13 @@ struct FwdParams {
     const float* sinks;
     uint16_t* out;
     float* lse;
-    int S, Hq, Hkv, G, window;
+    const int* cu;      // packed documents: sequence b = rows cu[b] .. cu[b+1]-1; nullptr = dense batch
+    int S, Hq, Hkv, G, window;  // S = sequence length (dense) or the longest document (packed)
+    int T;              // total token rows (B * S when dense)
     int pos_per_block;  // positions per workgroup = floor(256 / G)
     int n_qtiles;       // ceil(S / pos_per_block)
     int n_groups;       // B * Hkv
+    int B;              // sequences (dense batch or packed documents)
     float c;            // softmax scale * log2(e)
 };
 
@@ -93,8 +96,11 @@ __device__ __forceinline__ float exp_pack(const f32x16& s0, const f32x16& s1, fl
 
 // Workgroup -> (KV group, query tile).  Workgroups are dispatched round-robin
 // over the 8 XCDs, so when the groups split evenly each XCD walks its own
-// groups and their K/V stay in that XCD's L2.  Query tiles run heaviest
-// (latest positions, most keys) first.
+// groups and their K/V stay in that XCD's L2.  Groups are numbered
+// KV-head-major (group = kv_head * B + sequence), so with 8 KV heads each
+// XCD takes one KV head of every sequence, which keeps the XCDs' work equal
+// when packed documents differ in length.  Query tiles run heaviest (latest
+// positions, most keys) first.
 __device__ __forceinline__ void block_coords(const FwdParams& p, int bid, int& grp, int& qt) {
     const int nq = p.n_qtiles;
     if ((p.n_groups & 7) == 0) {
@@ -121,13 +127,14 @@ fwd_kernel(FwdParams p) {
 
     int grp, qt;
     block_coords(p, blockIdx.x, grp, qt);
-    const int b = grp / p.Hkv;
-    const int kvh = grp % p.Hkv;
+    const int kvh = grp / p.B, b = grp % p.B;  // KV-head-major groups
     const int G = p.G;
-    const int S = p.S;
+    const SeqRows sr = seq_rows(p.cu, p.S, p.Hq, p.T, b);
+    const int S = sr.len;  // positions of this sequence
     const int W = p.window;
     const unsigned Weff = W > 0 ? (unsigned)W : 0x7fffffffu;
     const int p0 = qt * p.pos_per_block;
+    if (p0 >= S) return;  // a document shorter than the longest one
     const int used_cols = p.pos_per_block * G;
     const int P1 = min(p0 + p.pos_per_block, S) - 1;
 
@@ -151,7 +158,7 @@ fwd_kernel(FwdParams p) {
     bf16x8 qf[2][4];
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
-        const uint16_t* qrow = p.q + ((size_t)(b * S + col_pos[nb]) * p.Hq + col_head[nb]) * kHeadDim;
+        const uint16_t* qrow = p.q + ((size_t)(sr.row0 + col_pos[nb]) * p.Hq + col_head[nb]) * kHeadDim;
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
             uint4 x = make_uint4(0, 0, 0, 0);
@@ -183,9 +190,9 @@ fwd_kernel(FwdParams p) {
     const int t_end = P1 / kBk;  // inclusive
 
     // global -> register staging of one K/V tile
-    const size_t kv_row_stride = (size_t)p.Hkv * kHeadDim;
-    const uint16_t* kbase = p.k + ((size_t)b * S * p.Hkv + kvh) * kHeadDim;
-    const uint16_t* vbase = p.v + ((size_t)b * S * p.Hkv + kvh) * kHeadDim;
+    const uint32_t kv_row_stride = (uint32_t)p.Hkv * kHeadDim;
+    const uint16_t* kbase = p.k + ((size_t)sr.row0 * p.Hkv + kvh) * kHeadDim;
+    const uint16_t* vbase = p.v + ((size_t)sr.row0 * p.Hkv + kvh) * kHeadDim;
     const int st_key = tid >> 3, st_unit = tid & 7;  // rows st_key, st_key + 32; 16-byte unit
     uint4 kreg[2], vreg[2];
 
@@ -197,8 +204,8 @@ fwd_kernel(FwdParams p) {
             kreg[j] = make_uint4(0, 0, 0, 0);
             vreg[j] = make_uint4(0, 0, 0, 0);
             if (key < S) {
-                kreg[j] = ld16(kbase + key * kv_row_stride + 8 * st_unit);
-                vreg[j] = ld16(vbase + key * kv_row_stride + 8 * st_unit);
+                kreg[j] = ld16(kbase + row_off(key, kv_row_stride) + 8 * st_unit);
+                vreg[j] = ld16(vbase + row_off(key, kv_row_stride) + 8 * st_unit);
             }
         }
     };
@@ -351,7 +358,7 @@ fwd_kernel(FwdParams p) {
         const float l_tot = sum_across_halves(l_run[nb]);
         if (!col_ok[nb]) continue;
         const float inv = 1.0f / l_tot;
-        uint16_t* orow = p.out + ((size_t)(b * S + col_pos[nb]) * p.Hq + col_head[nb]) * kHeadDim;
+        uint16_t* orow = p.out + ((size_t)(sr.row0 + col_pos[nb]) * p.Hq + col_head[nb]) * kHeadDim;
 #pragma unroll
         for (int db = 0; db < 2; ++db)
 #pragma unroll
@@ -363,7 +370,7 @@ fwd_kernel(FwdParams p) {
                 *reinterpret_cast<uint2*>(orow + d0) = w;
             }
         if (g == 0)
-            p.lse[((size_t)b * p.Hq + col_head[nb]) * S + col_pos[nb]] = (m_run[nb] + fast_log2(l_tot)) * kLn2;
+            p.lse[sr.lse_base + col_head[nb] * sr.lse_hstride + col_pos[nb]] = (m_run[nb] + fast_log2(l_tot)) * kLn2;
     }
 }
 
@@ -377,7 +384,9 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {
     p.sinks = a.sinks;
     p.out = a.out;
     p.lse = a.lse;
+    p.cu = a.cu;
     p.S = a.S;
+    p.T = a.T;
     p.Hq = a.Hq;
     p.Hkv = a.Hkv;
     p.G = a.Hq / a.Hkv;
@@ -385,8 +394,10 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {
     p.pos_per_block = kCols / p.G;
     p.n_qtiles = (a.S + p.pos_per_block - 1) / p.pos_per_block;
     p.n_groups = a.B * a.Hkv;
+    p.B = a.B;
     p.c = a.scale * kLog2e;
     const long long blocks = (long long)p.n_groups * p.n_qtiles;
+    if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL(fwd_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream, p);
     return hipGetLastError();
 }

@@ -15,7 +15,9 @@ struct FwdArgs {
     const float* sinks;
     uint16_t* out;
     float* lse;
-    int B, S, Hq, Hkv, window;
+    const int* cu;  // packed documents (sequence b = rows cu[b] .. cu[b+1]-1), nullptr = dense [B, S]
+    int B, S, Hq, Hkv, window;  // packed: B = documents, S = longest document
+    int T;                      // total token rows (B * S when dense)
     float scale;
 };
 
@@ -32,7 +34,9 @@ struct BwdArgs {
     uint16_t* dv;
     float* dsinks;
     void* workspace;
+    const int* cu;  // as in FwdArgs
     int B, S, Hq, Hkv, window;
+    int T;
     float scale;
 };
 
@@ -54,7 +58,7 @@ struct DecodeArgs {
 
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
 
-size_t bwd_workspace_bytes(int B, int S, int Hq, int Hkv, int window);
+size_t bwd_workspace_bytes(long long total_rows, int Hq);
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream);
 
 size_t decode_workspace_bytes(int N, int Hq, int Hkv, int max_seqlen, int window);

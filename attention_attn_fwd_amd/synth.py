@@ -19,8 +19,9 @@ from dataclasses import dataclass
 
 import torch
 
-__all__ = ["PrefillCase", "DecodeCase", "PagedDecodeCase", "CONFIGS", "make_prefill", "make_dout",
-           "make_decode", "make_paged_decode", "config_inputs"]
+__all__ = ["PrefillCase", "DecodeCase", "PagedDecodeCase", "VarlenCase", "CONFIGS", "make_prefill", "make_dout",
+           "make_decode", "make_paged_decode", "make_varlen", "draw_doc_lengths", "config_inputs", "VARLEN_WORKLOAD",
+           "varlen_workload"]
 
 SLIDING_WINDOW = 128
 
@@ -128,6 +129,54 @@ def make_paged_decode(N, Hq, Hkv, page_size, D=64, max_len=1024, seed=0, lengths
                            full.sinks, ring_tokens, full.max_seqlen, full.scale, full)
 
 
+@dataclass
+class VarlenCase:
+    q: torch.Tensor           # bf16 [T, Hq, D]
+    k: torch.Tensor           # bf16 [T, Hkv, D]
+    v: torch.Tensor           # bf16 [T, Hkv, D]
+    cu_seqlens: torch.Tensor  # int32 [N + 1]; document b = rows cu[b] .. cu[b+1]-1
+    sinks: torch.Tensor       # fp32 [Hq]
+    max_seqlen: int
+    scale: float
+
+
+def draw_doc_lengths(total, max_len, gen):
+    """Document lengths ~ U{1..max_len} drawn until they cover `total` tokens;
+    the last one is cut so that the lengths sum to `total` exactly."""
+    lengths, left = [], total
+    while left > 0:
+        L = int(torch.randint(1, max_len + 1, (1,), generator=gen))
+        lengths.append(min(L, left))
+        left -= lengths[-1]
+    return lengths
+
+
+def make_varlen(Hq, Hkv, D=64, lengths=None, total=None, max_len=None, std=1.0, seed=0, lead=0, tail=0,
+                scale=None):
+    """Documents packed back to back along the token dimension.
+
+    Lengths are given explicitly or drawn by draw_doc_lengths(total, max_len).
+    `lead` / `tail` rows before the first and after the last document belong
+    to no document (their values are drawn like the rest).  Draw order:
+    (lengths), q, k, v, sinks.
+    """
+    gen = torch.Generator().manual_seed(seed)
+    if lengths is None:
+        lengths = draw_doc_lengths(total, max_len, gen)
+    lengths = [int(x) for x in lengths]
+    cu = [lead]
+    for L in lengths:
+        cu.append(cu[-1] + L)
+    T = cu[-1] + tail
+    q = _normal_bf16(gen, (T, Hq, D), std)
+    k = _normal_bf16(gen, (T, Hkv, D), std)
+    v = _normal_bf16(gen, (T, Hkv, D), std)
+    sinks = torch.randn((Hq,), generator=gen, dtype=torch.float32)
+    max_seqlen = max([1] + lengths)
+    return VarlenCase(q, k, v, torch.tensor(cu, dtype=torch.int32), sinks, max_seqlen,
+                      (1.0 / D ** 0.5) if scale is None else scale)
+
+
 # The five workloads.  Each prefill config runs one sliding-window-128 layer
 # and one full-causal layer (window 0) over the same tensors.
 CONFIGS = {
@@ -139,6 +188,21 @@ CONFIGS = {
     "c4_decode_n128_l1024_h64x8": dict(kind="decode", N=128, Hq=64, Hkv=8, max_len=1024,
                                        seed=1004),
 }
+
+
+# Packed-document prefill: the token count and heads of the B=4, S=4096
+# workload, cut into documents of U{1..4096} tokens (the pages give no
+# document-length mix; this is the plainest one that spans short and
+# full-length documents).
+VARLEN_WORKLOAD = dict(name="varlen_t16384_docs_u1_4096_h64x8", total=16384, max_len=4096, Hq=64, Hkv=8,
+                       seed=1005, dout_seed=1006)
+
+
+def varlen_workload():
+    """(VarlenCase, dout) of the packed-document workload (CPU tensors)."""
+    w = VARLEN_WORKLOAD
+    case = make_varlen(w["Hq"], w["Hkv"], total=w["total"], max_len=w["max_len"], seed=w["seed"], scale=0.125)
+    return case, make_dout(tuple(case.q.shape), w["dout_seed"])
 
 
 def config_inputs(name):

@@ -16,7 +16,11 @@ reported beside it as `ms_per_step_eager`.
 value = unmasked FLOPs of the step (forward 4*D, backward 10*D per visible
 (batch, query head, query, key) pair; decode 4*D per visible key and head)
 divided by the step time, in TFLOP/s.  Per-part figures (TFLOP/s, GB/s and
-the fraction of the bounding roof) are printed in `parts`.
+the fraction of the bounding roof) are printed in `parts`; `parts` also times
+paths outside the step: decode through a paged and a ring cache, a training
+step through the autograd wrapper, and prefill of packed documents (16384
+tokens in documents of U{1..4096} tokens, same heads; FLOPs over the pairs
+visible inside each document).
 """
 
 import argparse
@@ -75,7 +79,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["fwd", "bwd", "decode", "copy"], default=None,
+    ap.add_argument("--only", choices=["fwd", "bwd", "decode", "varlen_fwd", "varlen_bwd", "copy"], default=None,
                     help="run only this part in a loop (for profiling); prints no JSON line.  'copy' "
                          "copies 1 GiB once per step, to calibrate HBM byte counters")
     ap.add_argument("--window", type=int, default=None, choices=list(WINDOWS),
@@ -160,13 +164,40 @@ def main():
         for w in WINDOWS:
             decode(w, i)
 
+    # packed documents: 16384 tokens in documents of U{1..4096} tokens, same heads
+    vcase, vdout_cpu = synth.varlen_workload()
+    vT = vcase.q.shape[0]
+    vcu = vcase.cu_seqlens.to(dev)
+    vlens = (vcase.cu_seqlens[1:] - vcase.cu_seqlens[:-1]).tolist()
+    vsets = []
+    for _ in range(NSETS if not args.only or args.only.startswith("varlen") else 0):
+        vq, vk, vv = vcase.q.to(dev), vcase.k.to(dev), vcase.v.to(dev)
+        vsets.append(dict(q=vq, k=vk, v=vv, dout=vdout_cpu.to(dev),
+                          outs={w: (torch.empty_like(vq), torch.empty(Hq, vT, device=dev)) for w in WINDOWS},
+                          grads={w: (torch.empty_like(vq), torch.empty_like(vk), torch.empty_like(vv),
+                                     torch.empty(Hq, dtype=torch.float32, device=dev)) for w in WINDOWS}))
+    vws = torch.empty(attn.bwd_varlen_workspace_size(vT, Hq, Hkv, D), dtype=torch.uint8, device=dev)
+
+    def varlen_fwd(w, i=0):
+        x = vsets[i % NSETS]
+        o, l = x["outs"][w]
+        attn.fwd_varlen(x["q"], x["k"], x["v"], vcu, sinks, vcase.max_seqlen, w, vcase.scale, out=o, lse=l)
+
+    def varlen_bwd(w, i=0):
+        x = vsets[i % NSETS]
+        o, l = x["outs"][w]
+        attn.bwd_varlen(x["q"], x["k"], x["v"], vcu, sinks, o, l, x["dout"], vcase.max_seqlen, w, vcase.scale,
+                        workspace=vws, grads=x["grads"][w])
+
     if args.only:
-        fn = {"fwd": fwd, "bwd": bwd, "decode": decode}[args.only]
+        fn = {"fwd": fwd, "bwd": bwd, "decode": decode, "varlen_fwd": varlen_fwd,
+              "varlen_bwd": varlen_bwd}[args.only]
         wins = WINDOWS if args.window is None else (args.window,)
-        if args.only == "bwd":
+        if args.only in ("bwd", "varlen_bwd"):
+            first = fwd if args.only == "bwd" else varlen_fwd
             for i in range(NSETS):
                 for w in wins:
-                    fwd(w, i)  # the backward consumes this layer's forward out/lse
+                    first(w, i)  # the backward consumes this layer's forward out/lse
         for i in range(args.warmup + args.steps):
             for w in wins:
                 fn(w, i)
@@ -189,6 +220,12 @@ def main():
         flops[("decode", w)] = 4 * D * Hq * vis
         bytes_[("decode", w)] = (2 * 2 * vis * Hkv * D + 2 * 2 * N * Hq * D + 4 * N * Hq + 4 * Hq
                                  + 4 * (N + 1))
+        vpairs = Hq * sum(pairs_per_head(L, w) for L in vlens)
+        flops[("varlen_fwd", w)] = 4 * D * vpairs
+        flops[("varlen_bwd", w)] = 10 * D * vpairs
+        vq_el, vk_el = vT * Hq * D, vT * Hkv * D
+        bytes_[("varlen_fwd", w)] = 2 * (2 * vq_el + 2 * vk_el) + 4 * Hq * vT + 4 * len(vlens)
+        bytes_[("varlen_bwd", w)] = 2 * (4 * vq_el + 4 * vk_el) + 4 * Hq * vT + 8 * Hq + 4 * len(vlens)
 
     stream = torch.cuda.current_stream(dev)
 
@@ -218,7 +255,7 @@ def main():
         g_steps[i % NSETS].replay()
     it = iter(range(1 << 30))
     ms_per_step = timed(lambda: g_steps[next(it) % NSETS].replay(), args.steps)
-    total_flops = sum(flops.values())
+    total_flops = sum(f for (name, _), f in flops.items() if not name.startswith("varlen"))
     value = total_flops / (ms_per_step * 1e-3) / 1e12
     del g_steps
 
@@ -283,6 +320,26 @@ def main():
         parts[label] = {"ms": round(ms, 4), "gbs": round(gbs, 1), "bound": "hbm",
                         "frac_of_roof": round(gbs / HBM_PEAK_GBS, 4)}
     del pg_sets, rg_sets
+    # packed-document prefill (not part of the step): forward and backward
+    # per layer, each timed like the parts above
+    for w in WINDOWS:
+        for i in range(NSETS):
+            varlen_fwd(w, i)
+    for name, fn in (("varlen_fwd", varlen_fwd), ("varlen_bwd", varlen_bwd)):
+        for w in WINDOWS:
+            g = capture(lambda: [fn(w, i) for i in range(reps)])
+            g.replay()
+            ms = sorted(timed(g.replay, 1) for _ in range(3))[1] / reps
+            del g
+            tf = flops[(name, w)] / (ms * 1e-3) / 1e12
+            gbs = bytes_[(name, w)] / (ms * 1e-3) / 1e9
+            ai = flops[(name, w)] / bytes_[(name, w)]
+            roof_tf = min(BF16_PEAK_TFLOPS, ai * HBM_PEAK_GBS / 1e3)
+            parts[f"{name}_{'full' if w == 0 else 'w%d' % w}"] = {
+                "ms": round(ms, 4), "tflops": round(tf, 2), "gbs": round(gbs, 1),
+                "bound": "mfma" if roof_tf >= BF16_PEAK_TFLOPS else "hbm",
+                "frac_of_roof": round(tf / roof_tf, 4)}
+    del vsets
     tf_train = (flops[("fwd", 0)] + flops[("bwd", 0)]) / (ms_train * 1e-3) / 1e12
     parts["autograd_train_full"] = {"ms": round(ms_train, 4), "tflops": round(tf_train, 2), "bound": "mfma",
                                     "frac_of_roof": round(tf_train / BF16_PEAK_TFLOPS, 4)}

@@ -40,8 +40,8 @@
  *     accumulated into.  Calls on different streams must not share outputs or
  *     workspace.
  *   - Argument errors are detected on the host before any HIP call and
- *     nothing is written.  A zero-sized problem (B == 0, S == 0 or N == 0)
- *     returns GPTOSS_OK without touching memory.  Contents of device buffers
+ *     nothing is written.  A zero-sized problem (B == 0, S == 0, N == 0 or
+ *     T == 0) returns GPTOSS_OK without touching memory.  Contents of device buffers
  *     (NaN/Inf in inputs, cu_seqlens values) are caller contracts and are not
  *     checked.
  *   - gptoss_attn_last_error() returns the message of this thread's last
@@ -169,6 +169,55 @@ gptoss_status gptoss_attn_decode_paged(const void* q, const void* k_pages, const
                                        int max_seqlen, int window, float softmax_scale,
                                        void* out, float* lse, void* workspace,
                                        size_t workspace_bytes, void* stream);
+
+/*
+ * Packed variable-length prefill (documents packed back to back in one token
+ * dimension, attention confined to each document).  Megatron-LM issue
+ * "gpt-oss implementation", discussion thread: a user asks for attention
+ * computed within each document of a packed sequence rather than over the
+ * whole sequence (intra-document masking); the pages give no answer.  The
+ * reading used here: document b is rows cu_seqlens[b] .. cu_seqlens[b+1]-1,
+ * its positions restart at 0, and the definition above (sink, causal and
+ * window visibility) applies inside each document on its own; rows of other
+ * documents are never visible.
+ *   q, out          bf16 [T, Hq, D]      (q read, out written)
+ *   k, v            bf16 [T, Hkv, D]     read
+ *   cu_seqlens      int32 [N + 1], device, non-decreasing, 0 <= cu[0],
+ *                   cu[N] <= T.  Rows outside every document are neither
+ *                   read as keys nor written.
+ *   max_seqlen      host-side upper bound of every document length (>= 1); it
+ *                   sizes the grid without reading device memory.  A longer
+ *                   document is a caller error: only its first max_seqlen rows
+ *                   are computed and the rest are not written.
+ *   lse             fp32 [Hq, T]         written (entry [h][row] for each row
+ *                   inside a document)
+ * window >= max_seqlen gives the same result as window = 0.
+ */
+gptoss_status gptoss_attn_fwd_varlen(const void* q, const void* k, const void* v,
+                                     const int* cu_seqlens, const float* sinks, int N, int T,
+                                     int Hq, int Hkv, int D, int max_seqlen, int window,
+                                     float softmax_scale, void* out, float* lse, void* stream);
+
+/*
+ * Backward of gptoss_attn_fwd_varlen for the loss sum(dout * out), the
+ * per-document counterpart of gptoss_attn_bwd.
+ *   q, out, dout    bf16 [T, Hq, D]; k, v bf16 [T, Hkv, D]; lse fp32 [Hq, T]
+ *                   as written by the forward                         read
+ *   dq bf16 [T, Hq, D]; dk, dv bf16 [T, Hkv, D]                       written
+ *                   on the rows inside a document (others not written)
+ *   dsinks fp32 [Hq] written: the sum over every document's rows (0 when no
+ *                   row lies inside a document).
+ *   workspace       gptoss_attn_bwd_varlen_workspace_size(T, Hq, Hkv, D) bytes,
+ *                   256-byte aligned; contents on entry ignored.
+ */
+size_t gptoss_attn_bwd_varlen_workspace_size(int T, int Hq, int Hkv, int D);
+gptoss_status gptoss_attn_bwd_varlen(const void* q, const void* k, const void* v,
+                                     const int* cu_seqlens, const float* sinks, const void* out,
+                                     const float* lse, const void* dout, int N, int T, int Hq,
+                                     int Hkv, int D, int max_seqlen, int window,
+                                     float softmax_scale, void* dq, void* dk, void* dv,
+                                     float* dsinks, void* workspace, size_t workspace_bytes,
+                                     void* stream);
 
 #ifdef __cplusplus
 }

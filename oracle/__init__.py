@@ -4,8 +4,9 @@ Imported only by tests/, __graft_entry__.smoke() and bench.py's cpu_baseline
 leg.  The HIP library never imports or calls anything here.
 """
 
-from .attn import allowed_mask, gather_paged, ref_bwd, ref_decode, ref_decode_paged, ref_fwd, unmasked_pairs
-from .brute import brute_fwd
+from .attn import (allowed_mask, gather_paged, ref_bwd, ref_bwd_varlen, ref_decode, ref_decode_paged, ref_fwd,
+                   ref_fwd_varlen, unmasked_pairs)
+from .brute import brute_fwd, brute_fwd_docs
 
 __all__ = ["allowed_mask", "ref_fwd", "ref_bwd", "ref_decode", "ref_decode_paged", "gather_paged", "unmasked_pairs",
-           "brute_fwd"]
+           "ref_fwd_varlen", "ref_bwd_varlen", "brute_fwd", "brute_fwd_docs"]

@@ -23,6 +23,13 @@ definition, materialising the masked score rows):
   title and notes.  Reading: ``window == 0`` is full causal; ``window = W >= 1``
   lets query i see keys j with ``i - W < j <= i`` (W keys including itself).
 * Grouped-query heads: query head h reads K/V head ``h // (Hq // Hkv)``.
+* Documents packed along the token dimension (``ref_fwd_varlen`` /
+  ``ref_bwd_varlen``) -- Megatron-LM issue "gpt-oss implementation",
+  discussion thread, where a user asks for attention confined to each
+  document of a packed sequence (intra-document masking) and gets no answer.
+  Reading: document b is rows ``cu[b] .. cu[b+1]-1``; the definition below
+  applies to each document on its own (positions restart at 0, rows of other
+  documents are never visible); the sink joins every row as usual.
 * Decode (one new token per sequence over a packed per-sequence KV cache) is
   row ``L - 1`` of the same definition over that sequence's ``L`` cached keys
   (the HF blog's "Continuous Batching & Paged Attention" and the serve command
@@ -61,7 +68,7 @@ the four invariants, and central finite differences for the backward.
 import numpy as np
 
 __all__ = ["allowed_mask", "ref_fwd", "ref_bwd", "ref_decode", "ref_decode_paged", "gather_paged",
-           "unmasked_pairs"]
+           "unmasked_pairs", "ref_fwd_varlen", "ref_bwd_varlen"]
 
 
 def allowed_mask(rows, keys, window):
@@ -242,3 +249,47 @@ def ref_decode_paged(q, k_pages, v_pages, block_table, seq_lens, sinks, ring_tok
     attention itself is ref_decode on those rows (all of them visible)."""
     kc, vc, cu = gather_paged(k_pages, v_pages, block_table, seq_lens, ring_tokens, window)
     return ref_decode(q, kc, vc, cu, sinks, 0, scale)
+
+
+def ref_fwd_varlen(q, k, v, cu_seqlens, sinks, window, scale, docs=None, heads=None):
+    """Forward over packed documents: q [T,Hq,D], k/v [T,Hkv,D].
+
+    Each document is the batch-of-one forward of its own rows.  Returns
+    (out [T,Hq,D], lse [Hq,T]); rows outside the computed documents stay NaN.
+    ``docs`` / ``heads`` restrict which documents / query heads are computed.
+    """
+    T, Hq, D = q.shape
+    out = np.full((T, Hq, D), np.nan)
+    lse = np.full((Hq, T), np.nan)
+    n_docs = len(cu_seqlens) - 1
+    for b in (range(n_docs) if docs is None else docs):
+        a, e = int(cu_seqlens[b]), int(cu_seqlens[b + 1])
+        if e <= a:
+            continue
+        o, l = ref_fwd(q[None, a:e], k[None, a:e], v[None, a:e], sinks, window, scale, heads=heads)
+        out[a:e] = o[0]
+        lse[:, a:e] = l[0]
+    return out, lse
+
+
+def ref_bwd_varlen(q, k, v, cu_seqlens, sinks, dout, window, scale, docs=None, heads=None):
+    """Backward of sum(dout * out) over packed documents.
+
+    Returns (dq, dk, dv, dsinks); dq/dk/dv rows outside the computed documents
+    stay NaN and dsinks sums the computed documents' rows.  With ``heads``
+    given, only those query heads contribute (as in ref_bwd).
+    """
+    dq = np.full(q.shape, np.nan)
+    dk = np.full(k.shape, np.nan)
+    dv = np.full(v.shape, np.nan)
+    dsinks = np.zeros(q.shape[1])
+    n_docs = len(cu_seqlens) - 1
+    for b in (range(n_docs) if docs is None else docs):
+        a, e = int(cu_seqlens[b]), int(cu_seqlens[b + 1])
+        if e <= a:
+            continue
+        gq, gk, gv, gs = ref_bwd(q[None, a:e], k[None, a:e], v[None, a:e], sinks, dout[None, a:e], window, scale,
+                                 heads=heads)
+        dq[a:e], dk[a:e], dv[a:e] = gq[0], gk[0], gv[0]
+        dsinks += gs
+    return dq, dk, dv, dsinks

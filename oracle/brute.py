@@ -12,7 +12,7 @@ window: same issue, "Alternating Sliding-Window Attention Pattern".
 
 import math
 
-__all__ = ["brute_fwd"]
+__all__ = ["brute_fwd", "brute_fwd_docs"]
 
 
 def brute_fwd(q, k, v, sinks, window, scale):
@@ -45,4 +45,41 @@ def brute_fwd(q, k, v, sinks, window, scale):
                 for d in range(D):
                     out[b][i][h][d] = math.fsum(w * v[b][j][c][d] for j, w in weights) / Z
                 lse[b][h][i] = math.log(Z)
+    return out, lse
+
+
+def brute_fwd_docs(q, k, v, doc_of_row, sinks, window, scale):
+    """Packed documents as one block-diagonal mask over the token rows.
+
+    q [T][Hq][D], k/v [T][Hkv][D] nested floats; doc_of_row[t] is the document
+    id of row t (None for a row in no document).  Key row j is visible from
+    query row i when both carry the same document id, j <= i and, for a
+    window W >= 1, i - j < W.  (Megatron-LM issue "gpt-oss implementation",
+    discussion thread: attention confined to each document of a packed
+    sequence.)  Returns (out [T][Hq][D], lse [Hq][T]) with None for rows in no
+    document.
+    """
+    T, Hq, D = len(q), len(q[0]), len(q[0][0])
+    Hkv = len(k[0])
+    G = Hq // Hkv
+    out = [[None] * Hq for _ in range(T)]
+    lse = [[None] * T for _ in range(Hq)]
+    for i in range(T):
+        if doc_of_row[i] is None:
+            continue
+        for h in range(Hq):
+            c = h // G
+            weights = []
+            for j in range(T):
+                if doc_of_row[j] != doc_of_row[i] or j > i:
+                    continue
+                if window > 0 and i - j >= window:
+                    continue
+                dot = math.fsum(q[i][h][d] * k[j][c][d] for d in range(D))
+                weights.append((j, math.exp(scale * dot)))
+            sink = float(sinks[h])
+            sink_w = 0.0 if sink == -math.inf else math.exp(sink)
+            Z = math.fsum([w for _, w in weights] + [sink_w])
+            out[i][h] = [math.fsum(w * v[j][c][d] for j, w in weights) / Z for d in range(D)]
+            lse[h][i] = math.log(Z)
     return out, lse

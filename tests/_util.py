@@ -33,13 +33,28 @@ def check_out_lse(out, lse, ref_out, ref_lse, what=""):
     osel = ~np.isnan(ref_out)
     d_out = np.abs(out[osel] - ref_out[osel])
     d_lse = np.abs(lse[sel] - ref_lse[sel])
-    msg = (f"{what}: out max {d_out.max():.3e} mean {d_out.mean():.3e}; "
-           f"lse max {d_lse.max():.3e}")
+    bar = out_bar(ref_out[osel])
+    msg = (f"{what}: out max {d_out.max():.3e} mean {d_out.mean():.3e} (worst vs its bar "
+           f"{(d_out / bar).max():.3f}); lse max {d_lse.max():.3e}")
     assert np.isfinite(out[osel]).all() and np.isfinite(lse[sel]).all(), msg
-    assert d_out.max() <= OUT_MAX_ABS, msg
+    assert (d_out <= bar).all(), msg
     assert d_out.mean() <= OUT_MEAN_ABS, msg
     assert d_lse.max() <= LSE_MAX_ABS, msg
     return d_out.max(), d_out.mean(), d_lse.max()
+
+
+def bf16_ulp(x):
+    """Spacing of bf16 numbers (8 significant bits) at |x|."""
+    e = np.floor(np.log2(np.maximum(np.abs(x), 2.0 ** -126)))
+    return np.exp2(e - 7)
+
+
+def out_bar(ref):
+    """Per-element bar of the bf16 output: OUT_MAX_ABS, or one bf16 ulp of the
+    exact value where that is larger (|out| >= 2, e.g. a window-1 row whose
+    output is one value row; rounding the exact value to bf16 alone costs
+    half an ulp, 0.0156 at |out| >= 4, above the 1e-2 bar)."""
+    return np.maximum(OUT_MAX_ABS, bf16_ulp(ref))
 
 
 def rel_l2(x, ref):

@@ -202,3 +202,70 @@ def test_autograd_wrapper_refuses_host_tensors():
     k = torch.zeros(1, 4, 1, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError, match="HIP device"):
         sink_attention(q, k, k, torch.zeros(8), 0)
+
+
+def _fwd_varlen(lib, **kw):
+    a = dict(q=P, k=P, v=P, cu=P, sinks=P, N=3, T=1000, Hq=64, Hkv=8, D=64, max_seqlen=512, window=0,
+             scale=0.125, out=P, lse=P)
+    a.update(kw)
+    return lib.gptoss_attn_fwd_varlen(a["q"], a["k"], a["v"], a["cu"], a["sinks"], a["N"], a["T"], a["Hq"],
+                                      a["Hkv"], a["D"], a["max_seqlen"], a["window"], a["scale"], a["out"],
+                                      a["lse"], None)
+
+
+def _bwd_varlen(lib, **kw):
+    a = dict(q=P, k=P, v=P, cu=P, sinks=P, out=P, lse=P, dout=P, N=3, T=1000, Hq=64, Hkv=8, D=64,
+             max_seqlen=512, window=0, scale=0.125, dq=P, dk=P, dv=P, dsinks=P, ws=P, ws_bytes=None)
+    a.update(kw)
+    need = lib.gptoss_attn_bwd_varlen_workspace_size(a["T"], a["Hq"], a["Hkv"], a["D"])
+    wb = need if a["ws_bytes"] is None else a["ws_bytes"]
+    return lib.gptoss_attn_bwd_varlen(a["q"], a["k"], a["v"], a["cu"], a["sinks"], a["out"], a["lse"], a["dout"],
+                                      a["N"], a["T"], a["Hq"], a["Hkv"], a["D"], a["max_seqlen"], a["window"],
+                                      a["scale"], a["dq"], a["dk"], a["dv"], a["dsinks"], a["ws"], wb, None)
+
+
+VARLEN_BAD = [
+    (dict(cu=None), "cu_seqlens is NULL"),
+    (dict(q=None), "q is NULL"),
+    (dict(N=-1), "must be >= 0"),
+    (dict(T=-5), "must be >= 0"),
+    (dict(max_seqlen=0), "max_seqlen"),
+    (dict(N=65536), "exceeds"),
+    (dict(Hq=64, Hkv=6), "multiple"),
+    (dict(window=-1), "window"),
+    (dict(scale=math.nan), "softmax_scale"),
+    (dict(k=P + 8), "aligned"),
+]
+
+
+@pytest.mark.parametrize("kw,frag", VARLEN_BAD)
+def test_fwd_varlen_rejects_bad_arguments(lib, kw, frag):
+    assert _fwd_varlen(lib, **kw) == 1
+    assert frag in lib.gptoss_attn_last_error().decode()
+    assert _fwd_varlen(lib, D=128) == 2
+
+
+@pytest.mark.parametrize("kw,frag", VARLEN_BAD + [
+    (dict(dq=None), "dq is NULL"),
+    (dict(dsinks=None), "dsinks is NULL"),
+    (dict(ws_bytes=16), "workspace"),
+    (dict(ws=P + 16), "aligned"),
+])
+def test_bwd_varlen_rejects_bad_arguments(lib, kw, frag):
+    assert _bwd_varlen(lib, **kw) == 1
+    assert frag in lib.gptoss_attn_last_error().decode()
+
+
+def test_varlen_zero_sized_problems_are_noops(lib):
+    nulls = dict(q=None, k=None, v=None, cu=None, sinks=None, out=None, lse=None)
+    assert _fwd_varlen(lib, N=0, **nulls) == 0
+    assert _fwd_varlen(lib, T=0, **nulls) == 0
+    assert _bwd_varlen(lib, N=0, dout=None, dq=None, dk=None, dv=None, dsinks=None, ws=None, **nulls) == 0
+
+
+def test_varlen_workspace_size(lib):
+    # one {lse, Dvec} pair and one dsink term per (row, head), like the dense backward
+    assert lib.gptoss_attn_bwd_varlen_workspace_size(16384, 64, 8, 64) == \
+        lib.gptoss_attn_bwd_workspace_size(4, 4096, 64, 8, 64, 0)
+    assert lib.gptoss_attn_bwd_varlen_workspace_size(0, 64, 8, 64) == 0
+    assert lib.gptoss_attn_bwd_varlen_workspace_size(100, 64, 7, 64) == 0
