@@ -28,10 +28,12 @@
 //   dsink  : one workgroup per head reduces the per-row terms the dq kernel
 //            left in the workspace ([head][token row], contiguous).
 // P and dP are recomputed in both the key-outer and query-outer kernels.
-// dsink does not use Dvec = <dout, out>, whose bf16 `out` carries rounding
-// that a cancelling sum over all rows would amplify: the dq kernel forms
-// r_i = sum_j P_ij dP_ij (= <dout_i, sum_j P_ij v_j>, the same quantity) in
-// fp32 while it sweeps row i's keys and stores exp(sink - lse_i) r_i.
+// dsink does not use Dvec = <dout, out> alone, whose bf16 `out` carries
+// rounding that a cancelling sum over all rows would amplify: the dq kernel
+// forms r_i = sum_j P_ij dP_ij (= <dout_i, sum_j P_ij v_j>, the same quantity)
+// in fp32 as sum_j dS_ij + Dvec_i (1 - P_sink,i) while it sweeps row i's keys
+// (the visible probabilities sum to 1 - P_sink,i, so Dvec's rounding cancels
+// to within the rounding of P) and stores exp(sink - lse_i) r_i.
 #include "common.h"
 #include "launch.h"
 
@@ -438,8 +440,13 @@ bwd_dq_kernel(BwdParams p, int n_qt, int pos_per_block) {
     const int wpmin = p0 + wc0 / G;
     const int wpmax = min(p0 + min(wc0 + 31, used_cols - 1) / G, S - 1);
 
+    // This column's q and dO rows as B operands (d = 16 ks + 8 g + 0..7).
+    // The dP accumulator starts at -Dvec, so the MFMAs deliver dP - Dvec and
+    // dS = P acc.  (q is not pre-scaled by c here: P must sum, with the
+    // sink, to 1 within fp32 rounding for the dsink term below, and a
+    // bf16-rounded c q would perturb it by ~1e-3.)
     bf16x8 qf[4], of[4];
-    float lse2 = INFINITY, dvec = 0.0f, rsum = 0.0f;
+    float lse2 = INFINITY, dvec = 0.0f, dsum = 0.0f;
     {
         const size_t off = (((size_t)sr.row0 + col_pos) * Hq + col_head) * kHeadDim;
 #pragma unroll
@@ -522,7 +529,10 @@ bwd_dq_kernel(BwdParams p, int n_qt, int pos_per_block) {
             for (int mb = 0; mb < 2; ++mb) {
                 f32x16 sacc, dpacc;
 #pragma unroll
-                for (int r = 0; r < 16; ++r) sacc[r] = dpacc[r] = 0.0f;
+                for (int r = 0; r < 16; ++r) {
+                    sacc[r] = 0.0f;
+                    dpacc[r] = -dvec;
+                }
                 const int arow = 32 * mb + perm_row(l32);
 #pragma unroll
                 for (int ks = 0; ks < 4; ++ks) {
@@ -545,9 +555,8 @@ bwd_dq_kernel(BwdParams p, int n_qt, int pos_per_block) {
 #pragma unroll
                         for (int e = 0; e < 2; ++e) {
                             const int r = 8 * h + 2 * j + e;
-                            const float pr = fast_exp2(fmaf(sacc[r], p.c, -lse2));
-                            rsum = fmaf(pr, dpacc[r], rsum);
-                            ds[e] = pr * (dpacc[r] - dvec);
+                            ds[e] = fast_exp2(fmaf(sacc[r], p.c, -lse2)) * dpacc[r];
+                            dsum += ds[e];
                         }
                         w[j] = pack_bf16x2(ds[0], ds[1]);
                     }
@@ -568,12 +577,16 @@ bwd_dq_kernel(BwdParams p, int n_qt, int pos_per_block) {
         __syncthreads();
     }
 
-    rsum = sum_across_halves(rsum);
+    dsum = sum_across_halves(dsum);
     if (col_ok) {
         if (g == 0) {
-            // this row's dsink term; the row's own Q/dO/lse were read above
-            const float s2 = p.sinks[col_head] * kLog2e;
-            p.dsterm[(size_t)col_head * p.T + sr.row0 + col_pos] = fast_exp2(s2 - lse2) * rsum;
+            // this row's dsink term exp(sink - lse) r with
+            // r = sum_j P dP = sum_j dS + Dvec (1 - P_sink): the row's
+            // probabilities sum to 1 - P_sink, so Dvec (and the bf16
+            // rounding of `out` it carries) cancels to within the fp32
+            // rounding of P
+            const float psink = fast_exp2(p.sinks[col_head] * kLog2e - lse2);
+            p.dsterm[(size_t)col_head * p.T + sr.row0 + col_pos] = psink * fmaf(dvec, 1.0f - psink, dsum);
         }
         uint16_t* row = p.dq + (((size_t)sr.row0 + col_pos) * Hq + col_head) * kHeadDim;
 #pragma unroll
