@@ -12,7 +12,7 @@ window: same issue, "Alternating Sliding-Window Attention Pattern".
 
 import math
 
-__all__ = ["brute_fwd", "brute_fwd_docs"]
+__all__ = ["brute_fwd", "brute_fwd_docs", "brute_rope"]
 
 
 def brute_fwd(q, k, v, sinks, window, scale):
@@ -83,3 +83,17 @@ def brute_fwd_docs(q, k, v, doc_of_row, sinks, window, scale):
             out[i][h] = [math.fsum(w * v[j][c][d] for j, w in weights) / Z for d in range(D)]
             lse[h][i] = math.log(Z)
     return out, lse
+
+
+def brute_rope(x, position, freqs, mscale):
+    """Rotary embedding of one vector x (length D, nested floats) as complex
+    multiplication: z_i = (x_i + 1j x_{i+D/2}) * mscale * exp(1j position f_i),
+    y_i = Re z_i, y_{i+D/2} = Im z_i (the half-split pairing).  A restatement
+    of the rotation in oracle/rope.py by a different route, for pins."""
+    import cmath
+    half = len(x) // 2
+    out = [0.0] * len(x)
+    for i in range(half):
+        z = complex(x[i], x[i + half]) * mscale * cmath.exp(1j * position * freqs[i])
+        out[i], out[i + half] = z.real, z.imag
+    return out

@@ -1,0 +1,109 @@
+"""Rotary position embedding with YaRN frequency scaling, for the oracle.
+TEST INFRASTRUCTURE ONLY (imported by tests/, __graft_entry__.smoke() and
+bench.py's cpu_baseline leg; the HIP library never imports it).
+
+Megatron-LM issue "gpt-oss implementation", section "Positional Encodings /
+YaRN RoPE Scaling", names YaRN scaling of rotary embeddings (to 128k+
+context) and cites the YaRN paper, arXiv:2309.00071; the pages give no
+formula and no parameters.  The reading used here restates the paper:
+
+* base frequencies theta_i = base^(-2 i / D), i = 0 .. D/2 - 1;
+* wavelength lambda_i = 2 pi / theta_i and r_i = L / lambda_i, the number of
+  turns of pair i over the original context length L;
+* ramp gamma(r) = 0 for r < alpha, 1 for r > beta, (r - alpha) / (beta -
+  alpha) between; the scaled frequency is
+  h_i = (1 - gamma(r_i)) theta_i / s + gamma(r_i) theta_i  (s = the factor);
+* the attention temperature sqrt(1/t) = 0.1 ln(s) + 1 multiplies both q and k
+  (so it is folded into cos and sin); s = 1 is plain RoPE.
+* pairing (the pages do not fix it): element i is rotated with element
+  i + D/2 ("half-split"), the angle of position p being p h_i:
+  y_i = x_i cos - x_{i+D/2} sin,  y_{i+D/2} = x_{i+D/2} cos + x_i sin.
+* precision (a reading: the attention consumes bf16 q and k, as any bf16
+  pipeline that applies RoPE before attention does): the table holds
+  fp32(m cos(p h_i)) and fp32(m sin(p h_i)) computed in fp64; a rotated
+  element is fp32(fp32(x_i c) - fp32(x_j s)) (resp. + for the partner) and
+  is then rounded to bf16 (nearest even) before the attention products.  The
+  exact fp64 rotation (`apply_rope_exact`) is kept for the pins.
+"""
+
+import math
+
+import numpy as np
+import torch
+
+__all__ = ["yarn_inv_freq", "yarn_mscale", "rope_table", "apply_rope_exact", "apply_rope_bf16",
+           "ref_fwd_rope", "ref_decode_rope"]
+
+
+def yarn_inv_freq(D, base, factor, orig_ctx, alpha, beta):
+    """Scaled frequencies h_i (fp64, length D/2)."""
+    i = np.arange(D // 2, dtype=np.float64)
+    theta = base ** (-2.0 * i / D)
+    if factor == 1.0:
+        return theta
+    r = orig_ctx * theta / (2.0 * math.pi)
+    gamma = np.clip((r - alpha) / (beta - alpha), 0.0, 1.0)
+    return (1.0 - gamma) * theta / factor + gamma * theta
+
+
+def yarn_mscale(factor):
+    return 1.0 if factor <= 1.0 else 0.1 * math.log(factor) + 1.0
+
+
+def rope_table(P, D, base, factor, orig_ctx, alpha, beta, dtype=np.float32):
+    """(cos, sin) tables [P, D/2] of m cos(p h_i), m sin(p h_i), computed in
+    fp64 and rounded to `dtype` (fp32 by default; fp64 for exact pins)."""
+    h = yarn_inv_freq(D, base, factor, orig_ctx, alpha, beta)
+    ang = np.arange(P, dtype=np.float64)[:, None] * h[None, :]
+    m = yarn_mscale(factor)
+    return (m * np.cos(ang)).astype(dtype), (m * np.sin(ang)).astype(dtype)
+
+
+def apply_rope_exact(x, positions, cos, sin):
+    """fp64 rotation of x [..., T, H, D] (positions [T]) with fp64 tables."""
+    half = x.shape[-1] // 2
+    c = cos[positions][:, None, :]
+    s = sin[positions][:, None, :]
+    x1, x2 = x[..., :half], x[..., half:]
+    return np.concatenate([x1 * c - x2 * s, x2 * c + x1 * s], axis=-1)
+
+
+def _to_bf16(a32):
+    return torch.from_numpy(np.ascontiguousarray(a32)).to(torch.bfloat16).to(torch.float64).numpy()
+
+
+def apply_rope_bf16(x, positions, cos32, sin32):
+    """The rotation as the bf16 path computes it (see the header): fp32
+    products and difference with one rounding each, then bf16.  x holds
+    bf16 values (any float dtype); cos32/sin32 are the fp32 tables."""
+    half = x.shape[-1] // 2
+    xf = x.astype(np.float32)
+    c = cos32[positions][:, None, :].astype(np.float32)
+    s = sin32[positions][:, None, :].astype(np.float32)
+    x1, x2 = xf[..., :half], xf[..., half:]
+    y1 = (x1 * c) - (x2 * s)
+    y2 = (x2 * c) + (x1 * s)
+    return _to_bf16(np.concatenate([y1, y2], axis=-1).astype(np.float32))
+
+
+def ref_fwd_rope(q, k, v, sinks, window, scale, cos32, sin32, **kw):
+    """Prefill with RoPE on q and k at positions 0..S-1 of each batch:
+    returns (out, lse, k_rot) where k_rot is the rotated, bf16-rounded k
+    [B, S, Hkv, D] and out/lse are ref_fwd over the rotated q and k."""
+    from .attn import ref_fwd
+    S = q.shape[1]
+    pos = np.arange(S)
+    qr = np.stack([apply_rope_bf16(q[b], pos, cos32, sin32) for b in range(q.shape[0])])
+    kr = np.stack([apply_rope_bf16(k[b], pos, cos32, sin32) for b in range(k.shape[0])])
+    out, lse = ref_fwd(qr, kr, v, sinks, window, scale, **kw)
+    return out, lse, kr
+
+
+def ref_decode_rope(q, k_cache, v_cache, cu_seqlens, sinks, window, scale, cos32, sin32):
+    """Decode with the query rotated at its position L_n - 1 (the cache holds
+    rotated keys); an empty sequence sees only the sink."""
+    from .attn import ref_decode
+    L = np.diff(np.asarray(cu_seqlens))
+    pos = np.maximum(L - 1, 0)
+    qr = apply_rope_bf16(q, pos, cos32, sin32) if q.shape[0] else q
+    return ref_decode(qr, k_cache, v_cache, cu_seqlens, sinks, window, scale)

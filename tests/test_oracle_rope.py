@@ -1,0 +1,160 @@
+"""Pins of the RoPE / YaRN oracle (oracle/rope.py), CPU only.
+
+* the rotation against a scalar complex-multiplication restatement
+  (oracle/brute.py, brute_rope) for random vectors, positions and YaRN
+  settings
+* YaRN's two limits reduce to textbook cases: every pair interpolated
+  (all turns below alpha) is position interpolation, the rotation at position
+  p equals plain RoPE at position p / s; every pair extrapolated (all turns
+  above beta) is plain RoPE; s = 1 is plain RoPE with temperature 1
+* hand values of the ramp on a two-pair head (D = 4)
+* norm: each pair's length is multiplied by the temperature; position 0 is
+  the temperature times the identity
+* relative position: <R(p) q, R(p') k> depends only on p - p'
+* the bf16 path stays within one bf16 ulp of the exact rotation, and equals
+  the exact rotation for a unit pair
+* attention with the identity table is attention without RoPE; decode with
+  RoPE is the last row of prefill with RoPE
+"""
+
+import math
+
+import numpy as np
+import pytest
+
+from oracle import (apply_rope_bf16, apply_rope_exact, brute_rope, ref_decode, ref_decode_rope, ref_fwd,
+                    ref_fwd_rope, rope_table, yarn_inv_freq, yarn_mscale)
+
+GPTOSS_LIKE = dict(base=150000.0, factor=32.0, orig_ctx=4096, alpha=1.0, beta=32.0)
+
+
+def _bf16(a):
+    import torch
+    return torch.tensor(a, dtype=torch.float32).to(torch.bfloat16).to(torch.float64).numpy()
+
+
+@pytest.mark.parametrize("params", [GPTOSS_LIKE, dict(base=10000.0, factor=1.0, orig_ctx=2048, alpha=1.0, beta=32.0),
+                                    dict(base=500000.0, factor=8.0, orig_ctx=8192, alpha=2.0, beta=16.0)])
+def test_rotation_matches_complex_brute_force(params):
+    rng = np.random.default_rng(3)
+    D, P = 64, 300
+    cos, sin = rope_table(P, D, dtype=np.float64, **params)
+    freqs = yarn_inv_freq(D, **params)
+    m = yarn_mscale(params["factor"])
+    x = rng.standard_normal((5, 2, D))
+    pos = np.array([0, 1, 17, 255, 299])
+    y = apply_rope_exact(x, pos, cos, sin)
+    for t in range(5):
+        for h in range(2):
+            ref = brute_rope(x[t, h].tolist(), int(pos[t]), freqs.tolist(), m)
+            np.testing.assert_allclose(y[t, h], ref, rtol=1e-12, atol=1e-12)
+
+
+def test_all_interpolated_is_position_interpolation():
+    # alpha, beta above every pair's turn count: h_i = theta_i / s
+    D, s = 64, 8.0
+    h = yarn_inv_freq(D, 10000.0, s, 4096, 1e9, 2e9)
+    theta = 10000.0 ** (-np.arange(32) * 2.0 / 64)
+    np.testing.assert_allclose(h, theta / s, rtol=1e-15)
+    rng = np.random.default_rng(4)
+    x = rng.standard_normal(D)
+    p = 1000
+    ref = brute_rope(x.tolist(), p / s, theta.tolist(), yarn_mscale(s))  # plain RoPE at p / s
+    cos, sin = rope_table(p + 1, D, 10000.0, s, 4096, 1e9, 2e9, dtype=np.float64)
+    y = apply_rope_exact(x[None, None], np.array([p]), cos, sin)[0, 0]
+    np.testing.assert_allclose(y, ref, rtol=1e-10, atol=1e-12)
+
+
+def test_all_extrapolated_is_plain_rope():
+    # alpha, beta below every pair's turn count: h_i = theta_i
+    h = yarn_inv_freq(64, 10000.0, 8.0, 4096, 1e-9, 2e-9)
+    np.testing.assert_allclose(h, 10000.0 ** (-np.arange(32) * 2.0 / 64), rtol=1e-15)
+    assert yarn_inv_freq(64, 10000.0, 1.0, 4096, 1.0, 32.0).tolist() == \
+        (10000.0 ** (-np.arange(32) * 2.0 / 64)).tolist()
+    assert yarn_mscale(1.0) == 1.0
+    assert abs(yarn_mscale(32.0) - (1 + 0.1 * math.log(32))) < 1e-15
+
+
+def test_ramp_hand_values():
+    # D = 4: theta = (1, base^-1/2) with base = (200 pi)^2, so theta_1 =
+    # 1 / (200 pi); over L = 100 tokens the pairs turn L theta / (2 pi) =
+    # 100 / (2 pi) ~ 15.92 and 1 / (4 pi^2) ~ 0.025 times
+    base = (2 * math.pi * 100) ** 2
+    L = 100
+    th = np.array([1.0, 1.0 / (200 * math.pi)])
+    h = yarn_inv_freq(4, base, 4.0, L, 1.0, 32.0)
+    # pair 0: r = 15.92 inside [1, 32]: gamma = (15.92 - 1) / 31
+    g0 = (L / (2 * math.pi) - 1.0) / 31.0
+    assert abs(h[0] - ((1 - g0) * 1.0 / 4.0 + g0 * 1.0)) < 1e-15
+    # pair 1: r = 1 / (4 pi^2) < 1: fully interpolated
+    assert abs(h[1] - th[1] / 4.0) < 1e-18
+
+
+def test_norm_and_position_zero():
+    rng = np.random.default_rng(5)
+    cos, sin = rope_table(50, 64, dtype=np.float64, **GPTOSS_LIKE)
+    m = yarn_mscale(GPTOSS_LIKE["factor"])
+    x = rng.standard_normal((50, 3, 64))
+    y = apply_rope_exact(x, np.arange(50), cos, sin)
+    pair = lambda a: np.hypot(a[..., :32], a[..., 32:])
+    np.testing.assert_allclose(pair(y), m * pair(x), rtol=1e-13)
+    np.testing.assert_allclose(y[0], m * x[0], rtol=1e-15)
+
+
+def test_relative_position():
+    rng = np.random.default_rng(6)
+    cos, sin = rope_table(400, 64, dtype=np.float64, **GPTOSS_LIKE)
+    q = rng.standard_normal((1, 1, 64))
+    k = rng.standard_normal((1, 1, 64))
+    for p, pk, t in ((10, 3, 100), (200, 200, 37), (5, 90, 250)):
+        a = apply_rope_exact(q, np.array([p]), cos, sin)[0, 0] @ apply_rope_exact(k, np.array([pk]), cos, sin)[0, 0]
+        b = (apply_rope_exact(q, np.array([p + t]), cos, sin)[0, 0]
+             @ apply_rope_exact(k, np.array([pk + t]), cos, sin)[0, 0])
+        assert abs(a - b) <= 1e-10 * max(1.0, abs(a))
+
+
+def test_bf16_path_within_one_ulp_and_exact_on_unit_pair():
+    rng = np.random.default_rng(7)
+    c32, s32 = rope_table(100, 64, **GPTOSS_LIKE)
+    x = _bf16(rng.standard_normal((100, 4, 64)))
+    pos = np.arange(100)
+    y = apply_rope_bf16(x, pos, c32, s32)
+    ex = apply_rope_exact(x, pos, c32.astype(np.float64), s32.astype(np.float64))
+    ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(ex), 1e-30))) - 7)
+    assert (np.abs(y - ex) <= ulp).all()
+    # a unit pair (1, 0) rotates to (c, s) rounded once to bf16
+    e = np.zeros((1, 1, 64))
+    e[0, 0, 5] = 1.0
+    y = apply_rope_bf16(e, np.array([77]), c32, s32)
+    assert y[0, 0, 5] == _bf16(c32[77, 5]) and y[0, 0, 37] == _bf16(s32[77, 5])
+
+
+def test_identity_table_is_attention_without_rope():
+    rng = np.random.default_rng(8)
+    q = _bf16(rng.standard_normal((2, 40, 4, 64)))
+    k = _bf16(rng.standard_normal((2, 40, 2, 64)))
+    v = _bf16(rng.standard_normal((2, 40, 2, 64)))
+    sinks = rng.standard_normal(4)
+    one = np.ones((40, 32), np.float32)
+    zero = np.zeros((40, 32), np.float32)
+    out, lse, kr = ref_fwd_rope(q, k, v, sinks, 7, 0.125, one, zero)
+    o2, l2 = ref_fwd(q, k, v, sinks, 7, 0.125)
+    np.testing.assert_array_equal(out, o2)
+    np.testing.assert_array_equal(lse, l2)
+    np.testing.assert_array_equal(kr, k)
+
+
+@pytest.mark.parametrize("window", [0, 5])
+def test_decode_with_rope_is_last_prefill_row(window):
+    rng = np.random.default_rng(9 + window)
+    c32, s32 = rope_table(64, 64, **GPTOSS_LIKE)
+    lens = [1, 9, 23]
+    for L in lens:
+        q = _bf16(rng.standard_normal((1, L, 8, 64)))
+        k = _bf16(rng.standard_normal((1, L, 1, 64)))
+        v = _bf16(rng.standard_normal((1, L, 1, 64)))
+        sinks = rng.standard_normal(8)
+        out, lse, kr = ref_fwd_rope(q, k, v, sinks, window, 0.125, c32, s32)
+        o, l = ref_decode_rope(q[0, L - 1:L], kr[0], v[0], np.array([0, L]), sinks, window, 0.125, c32, s32)
+        np.testing.assert_allclose(o[0], out[0, L - 1], rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(l[0], lse[0, :, L - 1], rtol=1e-12, atol=1e-13)
