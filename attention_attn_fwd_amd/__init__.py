@@ -12,6 +12,10 @@ all computation runs in the library's HIP kernels.
                             ring_tokens)
     out, lse = fwd_varlen(q, k, v, cu_seqlens, sinks, max_seqlen, window, scale)     # packed documents
     dq, dk, dv, dsinks = bwd_varlen(q, k, v, cu_seqlens, sinks, out, lse, dout, max_seqlen, window, scale)
+    table = rope_table(positions, base, factor, orig_ctx, alpha, beta)          # YaRN rotary table
+    out, lse, k_rot = fwd_rope(q, k, v, sinks, table, window, scale)            # RoPE fused into prefill
+    out, lse = decode_rope(q, k_cache, v_cache, cu_seqlens, sinks, table, max_seqlen, window, scale)
+    y = rope_rows(x, positions, table)                                          # rotate rows (cache append)
 
 Training: attention_attn_fwd_amd.autograd.sink_attention (torch autograd over
 fwd/bwd).
@@ -23,7 +27,8 @@ from . import _lib
 from ._lib import AttnError
 
 __all__ = ["fwd", "bwd", "decode", "decode_paged", "fwd_varlen", "bwd_varlen", "bwd_workspace_size",
-           "bwd_varlen_workspace_size", "decode_workspace_size", "AttnError", "abi_version"]
+           "bwd_varlen_workspace_size", "decode_workspace_size", "rope_table", "rope_rows", "fwd_rope", "decode_rope",
+           "AttnError", "abi_version"]
 
 
 def _need(t, name, dtype, ndim):
@@ -264,3 +269,96 @@ def bwd_varlen(q, k, v, cu_seqlens, sinks, out, lse, dout, max_seqlen, window=0,
                                     _stream(q.device))
     _lib.check(st, lib)
     return dq, dk, dv, dsinks
+
+
+def rope_table(positions, base, factor=1.0, orig_ctx=1.0, alpha=1.0, beta=32.0, device=None, out=None):
+    """YaRN rotary table fp32 [positions, 32, 2] = (m cos(p h_i), m sin(p h_i))."""
+    dev = device if device is not None else torch.device("cuda", torch.cuda.current_device())
+    if out is None:
+        out = torch.empty((int(positions), 32, 2), dtype=torch.float32, device=dev)
+    _need(out, "table", torch.float32, 3)
+    lib = _lib.load()
+    st = lib.gptoss_attn_rope_table(out.data_ptr(), int(positions), 64, float(base), float(factor),
+                                    float(orig_ctx), float(alpha), float(beta), _stream(out.device))
+    _lib.check(st, lib)
+    return out
+
+
+def _need_table(table):
+    _need(table, "table", torch.float32, 3)
+    if table.shape[1:] != (32, 2):
+        raise ValueError("table must be [positions, 32, 2]")
+
+
+def rope_rows(x, positions, table, out=None):
+    """Rotate rows x bf16 [T, H, 64] by positions int32 [T] (device)."""
+    _need(x, "x", torch.bfloat16, 3)
+    _need(positions, "positions", torch.int32, 1)
+    _need_table(table)
+    T, H, D = x.shape
+    if positions.shape != (T,):
+        raise ValueError("positions must be [T]")
+    if out is None:
+        out = torch.empty_like(x)
+    _need(out, "out", torch.bfloat16, 3)
+    lib = _lib.load()
+    st = lib.gptoss_attn_rope_rows(x.data_ptr(), out.data_ptr(), positions.data_ptr(), T, H, D, table.data_ptr(),
+                                   table.shape[0], _stream(x.device))
+    _lib.check(st, lib)
+    return out
+
+
+def fwd_rope(q, k, v, sinks, table, window=0, scale=None, out=None, lse=None, k_rot=None):
+    """Prefill forward over RoPE-rotated q and k (token i at position i).
+    Returns (out, lse, k_rot) with k_rot the rotated keys [B,S,Hkv,64]."""
+    _need(q, "q", torch.bfloat16, 4)
+    _need(k, "k", torch.bfloat16, 4)
+    _need(v, "v", torch.bfloat16, 4)
+    _need(sinks, "sinks", torch.float32, 1)
+    _need_table(table)
+    B, S, Hq, D = q.shape
+    Hkv = k.shape[2]
+    if k.shape != (B, S, Hkv, D) or v.shape != k.shape or sinks.shape != (Hq,):
+        raise ValueError("shape mismatch among q, k, v, sinks")
+    scale = (1.0 / D ** 0.5) if scale is None else float(scale)
+    out = torch.empty_like(q) if out is None else out
+    lse = torch.empty((B, Hq, S), dtype=torch.float32, device=q.device) if lse is None else lse
+    k_rot = torch.empty_like(k) if k_rot is None else k_rot
+    _need(out, "out", torch.bfloat16, 4)
+    _need(lse, "lse", torch.float32, 3)
+    _need(k_rot, "k_rot", torch.bfloat16, 4)
+    lib = _lib.load()
+    st = lib.gptoss_attn_fwd_rope(q.data_ptr(), k.data_ptr(), v.data_ptr(), sinks.data_ptr(), table.data_ptr(),
+                                  table.shape[0], B, S, Hq, Hkv, D, int(window), scale, out.data_ptr(),
+                                  lse.data_ptr(), k_rot.data_ptr(), _stream(q.device))
+    _lib.check(st, lib)
+    return out, lse, k_rot
+
+
+def decode_rope(q, k_cache, v_cache, cu_seqlens, sinks, table, max_seqlen, window=0, scale=None, out=None, lse=None,
+                workspace=None):
+    """Decode with q rotated at position L_n - 1; the caches hold rotated keys."""
+    _need(q, "q", torch.bfloat16, 3)
+    _need(k_cache, "k_cache", torch.bfloat16, 3)
+    _need(v_cache, "v_cache", torch.bfloat16, 3)
+    _need(cu_seqlens, "cu_seqlens", torch.int32, 1)
+    _need(sinks, "sinks", torch.float32, 1)
+    _need_table(table)
+    N, Hq, D = q.shape
+    Hkv = k_cache.shape[1]
+    if (v_cache.shape != k_cache.shape or k_cache.shape[2] != D or cu_seqlens.shape != (N + 1,)
+            or sinks.shape != (Hq,)):
+        raise ValueError("shape mismatch among decode inputs")
+    scale = (1.0 / D ** 0.5) if scale is None else float(scale)
+    out = torch.empty_like(q) if out is None else out
+    lse = torch.empty((N, Hq), dtype=torch.float32, device=q.device) if lse is None else lse
+    need = decode_workspace_size(N, Hq, Hkv, D, max_seqlen, window)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    lib = _lib.load()
+    st = lib.gptoss_attn_decode_rope(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), cu_seqlens.data_ptr(),
+                                     sinks.data_ptr(), table.data_ptr(), table.shape[0], N, Hq, Hkv, D,
+                                     int(max_seqlen), int(window), scale, out.data_ptr(), lse.data_ptr(),
+                                     workspace.data_ptr(), workspace.numel(), _stream(q.device))
+    _lib.check(st, lib)
+    return out, lse

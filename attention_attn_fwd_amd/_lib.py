@@ -19,11 +19,13 @@ EXPORTS = [
     "gptoss_attn_bwd_workspace_size", "gptoss_attn_bwd",
     "gptoss_attn_decode_workspace_size", "gptoss_attn_decode", "gptoss_attn_decode_paged",
     "gptoss_attn_fwd_varlen", "gptoss_attn_bwd_varlen_workspace_size", "gptoss_attn_bwd_varlen",
+    "gptoss_attn_rope_table", "gptoss_attn_rope_rows", "gptoss_attn_fwd_rope", "gptoss_attn_decode_rope",
 ]
 
 _lib = None
 
 c_int, c_float, c_size_t, c_void_p = ctypes.c_int, ctypes.c_float, ctypes.c_size_t, ctypes.c_void_p
+c_double = ctypes.c_double
 
 
 class AttnError(RuntimeError):
@@ -68,6 +70,15 @@ def load(path=None):
     lib.gptoss_attn_bwd_varlen_workspace_size.argtypes = [c_int] * 4
     lib.gptoss_attn_bwd_varlen.restype = c_int
     lib.gptoss_attn_bwd_varlen.argtypes = [c_void_p] * 8 + [c_int] * 7 + [c_float] + [c_void_p] * 5 + \
+        [c_size_t, c_void_p]
+    lib.gptoss_attn_rope_table.restype = c_int
+    lib.gptoss_attn_rope_table.argtypes = [c_void_p, c_int, c_int] + [c_double] * 5 + [c_void_p]
+    lib.gptoss_attn_rope_rows.restype = c_int
+    lib.gptoss_attn_rope_rows.argtypes = [c_void_p] * 3 + [c_int] * 3 + [c_void_p, c_int, c_void_p]
+    lib.gptoss_attn_fwd_rope.restype = c_int
+    lib.gptoss_attn_fwd_rope.argtypes = [c_void_p] * 5 + [c_int] * 7 + [c_float] + [c_void_p] * 4
+    lib.gptoss_attn_decode_rope.restype = c_int
+    lib.gptoss_attn_decode_rope.argtypes = [c_void_p] * 6 + [c_int] * 7 + [c_float] + [c_void_p] * 3 + \
         [c_size_t, c_void_p]
     if path == LIB_PATH:
         _lib = lib

@@ -15,7 +15,7 @@ CSRC = os.path.join(PKG_DIR, "csrc")
 LIB_NAME = "libgptoss_attn.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 
-SOURCES = ["api.cpp", "fwd.hip", "decode.hip", "bwd.hip"]
+SOURCES = ["api.cpp", "fwd.hip", "decode.hip", "bwd.hip", "rope.hip"]
 
 # Packed-fp32 VALU forms are kept out of generated code; hipcc's host pass
 # warns that it does not know the feature, which is harmless.

@@ -118,6 +118,7 @@ gptoss_status gptoss_attn_fwd(const void* q, const void* k, const void* v, const
     a.out = static_cast<uint16_t*>(out);
     a.lse = lse;
     a.cu = nullptr;
+    a.rope = nullptr;
     a.B = B;
     a.S = S;
     a.T = B * S;
@@ -217,6 +218,7 @@ gptoss_status gptoss_attn_fwd_varlen(const void* q, const void* k, const void* v
     a.out = static_cast<uint16_t*>(out);
     a.lse = lse;
     a.cu = cu_seqlens;
+    a.rope = nullptr;
     a.B = N;
     a.S = max_seqlen;
     a.T = T;
@@ -332,6 +334,7 @@ gptoss_status gptoss_attn_decode(const void* q, const void* k_cache, const void*
     a.page_size = 0;
     a.pages_per_seq = 0;
     a.ring_tokens = 0;
+    a.rope = nullptr;
     a.scale = softmax_scale;
     return launched(gptoss::launch_decode(a, static_cast<hipStream_t>(stream)), "decode");
 }
@@ -407,8 +410,163 @@ gptoss_status gptoss_attn_decode_paged(const void* q, const void* k_pages, const
     a.page_size = page_size;
     a.pages_per_seq = pages_per_seq;
     a.ring_tokens = ring_tokens;
+    a.rope = nullptr;
     a.scale = softmax_scale;
     return launched(gptoss::launch_decode(a, static_cast<hipStream_t>(stream)), "paged decode");
+}
+
+// ---------------------------------------------------------------------------
+// Rotary embedding with YaRN scaling.
+
+static gptoss_status check_rope_params(int P, int D, double base, double factor, double orig_ctx, double alpha,
+                                       double beta) {
+    if (D != 64) return fail(GPTOSS_ERR_UNSUPPORTED, "head_dim %d is not supported (only 64)", D);
+    if (P < 1) return fail(GPTOSS_ERR_INVALID_ARGUMENT, "table positions (%d) must be >= 1", P);
+    if (!std::isfinite(base) || !(base > 1.0))
+        return fail(GPTOSS_ERR_INVALID_ARGUMENT, "rope base (%g) must be finite and > 1", base);
+    if (!std::isfinite(factor) || !(factor >= 1.0))
+        return fail(GPTOSS_ERR_INVALID_ARGUMENT, "YaRN factor (%g) must be finite and >= 1", factor);
+    if (factor > 1.0) {
+        if (!std::isfinite(orig_ctx) || !(orig_ctx >= 1.0))
+            return fail(GPTOSS_ERR_INVALID_ARGUMENT, "original context (%g) must be >= 1", orig_ctx);
+        if (!std::isfinite(alpha) || !std::isfinite(beta) || !(beta > alpha))
+            return fail(GPTOSS_ERR_INVALID_ARGUMENT, "YaRN ramp needs finite alpha < beta (got %g, %g)", alpha, beta);
+    }
+    return GPTOSS_OK;
+}
+
+gptoss_status gptoss_attn_rope_table(float* table, int positions, int D, double base, double factor,
+                                     double orig_ctx, double alpha, double beta, void* stream) {
+    gptoss_status st = check_rope_params(positions, D, base, factor, orig_ctx, alpha, beta);
+    if (st != GPTOSS_OK) return st;
+    if ((long long)positions * (D / 2) > kIndexLimit)
+        return fail(GPTOSS_ERR_INVALID_ARGUMENT, "table of %d positions is too large", positions);
+    CHECK_PTR(table, 16);
+    st = check_device();
+    if (st != GPTOSS_OK) return st;
+    return launched(gptoss::launch_rope_table(reinterpret_cast<float2*>(table), positions, base, factor, orig_ctx,
+                                              alpha, beta, static_cast<hipStream_t>(stream)),
+                    "rope table");
+}
+
+gptoss_status gptoss_attn_rope_rows(const void* x, void* y, const int* positions, int T, int H, int D,
+                                    const float* table, int table_positions, void* stream) {
+    if (T < 0 || H < 1) return fail(GPTOSS_ERR_INVALID_ARGUMENT, "T (%d) must be >= 0 and H (%d) >= 1", T, H);
+    if (D != 64) return fail(GPTOSS_ERR_UNSUPPORTED, "head_dim %d is not supported (only 64)", D);
+    if (table_positions < 1)
+        return fail(GPTOSS_ERR_INVALID_ARGUMENT, "table_positions (%d) must be >= 1", table_positions);
+    if (T == 0) return ok();
+    if ((long long)T * H > kIndexLimit)
+        return fail(GPTOSS_ERR_INVALID_ARGUMENT, "T*H = %lld rows exceeds 2^31-1", (long long)T * H);
+    CHECK_PTR(x, 16);
+    CHECK_PTR(y, 16);
+    CHECK_PTR(positions, 4);
+    CHECK_PTR(table, 16);
+    gptoss_status st = check_device();
+    if (st != GPTOSS_OK) return st;
+    return launched(gptoss::launch_rope_rows(static_cast<const uint16_t*>(x), static_cast<uint16_t*>(y), positions,
+                                             reinterpret_cast<const float2*>(table), table_positions,
+                                             (long long)T * H, H, 1, static_cast<hipStream_t>(stream)),
+                    "rope rows");
+}
+
+gptoss_status gptoss_attn_fwd_rope(const void* q, const void* k, const void* v, const float* sinks,
+                                   const float* table, int table_positions, int B, int S, int Hq, int Hkv, int D,
+                                   int window, float softmax_scale, void* out, float* lse, void* k_rot,
+                                   void* stream) {
+    if (B < 0 || S < 0) return fail(GPTOSS_ERR_INVALID_ARGUMENT, "B (%d) and S (%d) must be >= 0", B, S);
+    gptoss_status st = check_common(Hq, Hkv, D, window, softmax_scale);
+    if (st != GPTOSS_OK) return st;
+    if (B == 0 || S == 0) return ok();
+    if ((long long)B * S > kIndexLimit)
+        return fail(GPTOSS_ERR_INVALID_ARGUMENT, "B*S = %lld exceeds 2^31-1", (long long)B * S);
+    if (table_positions < S)
+        return fail(GPTOSS_ERR_INVALID_ARGUMENT, "rope table holds %d positions, S is %d", table_positions, S);
+    CHECK_PTR(q, 16);
+    CHECK_PTR(k, 16);
+    CHECK_PTR(v, 16);
+    CHECK_PTR(sinks, 4);
+    CHECK_PTR(table, 16);
+    CHECK_PTR(out, 16);
+    CHECK_PTR(lse, 4);
+    CHECK_PTR(k_rot, 16);
+    if (k_rot == k) return fail(GPTOSS_ERR_INVALID_ARGUMENT, "k_rot must not alias k");
+    st = check_device();
+    if (st != GPTOSS_OK) return st;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    const float2* tab = reinterpret_cast<const float2*>(table);
+    hipError_t e = gptoss::launch_rope_rows(static_cast<const uint16_t*>(k), static_cast<uint16_t*>(k_rot), nullptr,
+                                            tab, table_positions, (long long)B * S * Hkv, Hkv, S, s);
+    if (e != hipSuccess) return launched(e, "rope on k");
+    gptoss::FwdArgs a;
+    a.q = static_cast<const uint16_t*>(q);
+    a.k = static_cast<const uint16_t*>(k_rot);
+    a.v = static_cast<const uint16_t*>(v);
+    a.sinks = sinks;
+    a.out = static_cast<uint16_t*>(out);
+    a.lse = lse;
+    a.cu = nullptr;
+    a.rope = tab;
+    a.B = B;
+    a.S = S;
+    a.T = B * S;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.window = window;
+    a.scale = softmax_scale;
+    return launched(gptoss::launch_fwd(a, s), "forward with rope");
+}
+
+gptoss_status gptoss_attn_decode_rope(const void* q, const void* k_cache, const void* v_cache, const int* cu_seqlens,
+                                      const float* sinks, const float* table, int table_positions, int N, int Hq,
+                                      int Hkv, int D, int max_seqlen, int window, float softmax_scale, void* out,
+                                      float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+    if (N < 0) return fail(GPTOSS_ERR_INVALID_ARGUMENT, "N (%d) must be >= 0", N);
+    if (max_seqlen < 1) return fail(GPTOSS_ERR_INVALID_ARGUMENT, "max_seqlen (%d) must be >= 1", max_seqlen);
+    gptoss_status st = check_common(Hq, Hkv, D, window, softmax_scale);
+    if (st != GPTOSS_OK) return st;
+    if (table_positions < max_seqlen)
+        return fail(GPTOSS_ERR_INVALID_ARGUMENT, "rope table holds %d positions, max_seqlen is %d", table_positions,
+                    max_seqlen);
+    if (N == 0) return ok();
+    if ((long long)N > 65535)
+        return fail(GPTOSS_ERR_INVALID_ARGUMENT, "N (%d) exceeds 65535 sequences per call", N);
+    CHECK_PTR(q, 16);
+    CHECK_PTR(k_cache, 16);
+    CHECK_PTR(v_cache, 16);
+    CHECK_PTR(cu_seqlens, 4);
+    CHECK_PTR(sinks, 4);
+    CHECK_PTR(table, 16);
+    CHECK_PTR(out, 16);
+    CHECK_PTR(lse, 4);
+    const size_t need = gptoss::decode_workspace_bytes(N, Hq, Hkv, max_seqlen, window);
+    if (workspace_bytes < need)
+        return fail(GPTOSS_ERR_INVALID_ARGUMENT, "workspace_bytes %zu < required %zu", workspace_bytes, need);
+    if (need > 0) CHECK_PTR(workspace, 256);
+    st = check_device();
+    if (st != GPTOSS_OK) return st;
+    gptoss::DecodeArgs a;
+    a.q = static_cast<const uint16_t*>(q);
+    a.k_cache = static_cast<const uint16_t*>(k_cache);
+    a.v_cache = static_cast<const uint16_t*>(v_cache);
+    a.cu_seqlens = cu_seqlens;
+    a.block_table = nullptr;
+    a.seq_lens = nullptr;
+    a.sinks = sinks;
+    a.out = static_cast<uint16_t*>(out);
+    a.lse = lse;
+    a.workspace = workspace;
+    a.N = N;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.max_seqlen = max_seqlen;
+    a.window = window;
+    a.page_size = 0;
+    a.pages_per_seq = 0;
+    a.ring_tokens = 0;
+    a.rope = reinterpret_cast<const float2*>(table);
+    a.scale = softmax_scale;
+    return launched(gptoss::launch_decode(a, static_cast<hipStream_t>(stream)), "decode with rope");
 }
 
 }  // extern "C"

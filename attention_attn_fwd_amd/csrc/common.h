@@ -127,6 +127,43 @@ __device__ __forceinline__ bf16x8 tile_read_tr8(const uint4* tile, int r0, int c
 // register can alias a load still in flight, which costs a full wait.)
 __device__ __forceinline__ size_t row_off(int row, uint32_t stride) { return (size_t)(uint32_t)row * stride; }
 
+// Rotary embedding of 8 element pairs: a holds elements i .. i+7 and b their
+// partners i+32 .. i+39 (half-split pairing of a 64-wide head), cs the
+// (cos, sin) pairs of i .. i+7 as four float4 {c_i, s_i, c_{i+1}, s_{i+1}}.
+//   a' = a c - b s,  b' = b c + a s
+// Each product and the sum are rounded once to fp32 (no fused multiply-add),
+// then the results to bf16 (nearest even).
+__device__ __forceinline__ void rope8(uint4& a, uint4& b, const float4 (&cs)[4]) {
+#pragma clang fp contract(off)
+    const uint32_t aw[4] = {a.x, a.y, a.z, a.w}, bw[4] = {b.x, b.y, b.z, b.w};
+    uint32_t ra[4], rb[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const float a0 = __uint_as_float(aw[u] << 16), a1 = __uint_as_float(aw[u] & 0xffff0000u);
+        const float b0 = __uint_as_float(bw[u] << 16), b1 = __uint_as_float(bw[u] & 0xffff0000u);
+        const float c0 = cs[u].x, s0 = cs[u].y, c1 = cs[u].z, s1 = cs[u].w;
+        const float ya0 = a0 * c0 - b0 * s0, ya1 = a1 * c1 - b1 * s1;
+        const float yb0 = b0 * c0 + a0 * s0, yb1 = b1 * c1 + a1 * s1;
+        bf16x2 pa, pb;
+        pa[0] = (__bf16)ya0;
+        pa[1] = (__bf16)ya1;
+        pb[0] = (__bf16)yb0;
+        pb[1] = (__bf16)yb1;
+        ra[u] = __builtin_bit_cast(uint32_t, pa);
+        rb[u] = __builtin_bit_cast(uint32_t, pb);
+    }
+    a = make_uint4(ra[0], ra[1], ra[2], ra[3]);
+    b = make_uint4(rb[0], rb[1], rb[2], rb[3]);
+}
+
+// The four (cos, sin) float4 of pairs i .. i+7 (i even) at `position` of a
+// table of 32 pairs per position.
+__device__ __forceinline__ void load_rope8(const float2* tab, int position, int i, float4 (&cs)[4]) {
+    const float4* t = reinterpret_cast<const float4*>(tab + (size_t)position * 32 + i);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) cs[u] = t[u];
+}
+
 // Rows of sequence b in a [token, head, d] tensor.  A dense batch
 // (cu == nullptr) puts sequence b at rows b * S .. b * S + S - 1; a packed
 // batch of variable-length documents puts it at rows cu[b] .. cu[b + 1] - 1,

@@ -56,6 +56,7 @@ struct DecParams {
     float* part;      // [N][Hq][n_splits][kPartStride]
     const int* bt;    // paged cache: block table [N][pps]; nullptr for the contiguous cache
     const int* lens;  // paged cache: L_n per sequence
+    const float2* rope;  // (cos, sin) table: q rotated at position L_n - 1 (keys arrive rotated); nullptr = none
     int ps_shift, ps_mask, pps, ring_mask;  // page size = 1 << ps_shift; slot = position & ring_mask
     int Hq, Hkv, G, window, n_splits, n_hblk, max_seqlen;
     int chunk_keys;   // visible keys per chunk (a multiple of 64)
@@ -124,15 +125,21 @@ decode_split_kernel(DecParams p) {
     const uint16_t* vb = p.vc + ((size_t)base * p.Hkv + kvh) * kHeadDim;
     const int* bt_row = kPaged ? p.bt + (size_t)n * p.pps : nullptr;
 
-    bf16x8 qf[4];
+    uint4 qraw[4];
     {
         const uint16_t* qrow = p.q + ((size_t)n * p.Hq + head) * kHeadDim;
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
-            uint4 x = make_uint4(0, 0, 0, 0);
-            if (col_ok) x = ld16(qrow + 16 * ks + 8 * g);
-            qf[ks] = as_bf16x8(x);
+            qraw[ks] = make_uint4(0, 0, 0, 0);
+            if (col_ok) qraw[ks] = ld16(qrow + 16 * ks + 8 * g);
         }
+    }
+    // rotary table entries of the query at position L - 1 (pairs d, d + 32
+    // are fragments ks and ks + 2), loaded ahead of the first tile
+    float4 rcs[2][4];
+    if (p.rope != nullptr) {
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) load_rope8(p.rope, L - 1, 16 * ks + 8 * g, rcs[ks]);
     }
 
     // tile loads: eight consecutive lanes read one whole 128-byte K or V row
@@ -172,6 +179,13 @@ decode_split_kernel(DecParams p) {
     } else {
         load_tile(0);  // n_tiles >= 1 here
     }
+    if (p.rope != nullptr) {
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) rope8(qraw[ks], qraw[ks + 2], rcs[ks]);
+    }
+    bf16x8 qf[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) qf[ks] = as_bf16x8(qraw[ks]);
     for (int t = 0; t < n_tiles; ++t) {
         // K and V tiles -> this wave's LDS tiles.  Only this wave touches
         // them and a wave's LDS operations complete in order, so the previous
@@ -417,6 +431,7 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
     p.c = a.scale * kLog2e;
     p.bt = a.block_table;
     p.lens = a.seq_lens;
+    p.rope = a.rope;
     p.ps_shift = 0;
     while (a.page_size > 0 && (1 << p.ps_shift) < a.page_size) ++p.ps_shift;
     p.ps_mask = a.page_size > 0 ? a.page_size - 1 : 0;

@@ -54,6 +54,7 @@ struct FwdParams {
     uint16_t* out;
     float* lse;
     const int* cu;      // packed documents: sequence b = rows cu[b] .. cu[b+1]-1; nullptr = dense batch
+    const float2* rope; // (cos, sin) table [position][32]: q rotated at load (k arrives rotated); nullptr = none
     int S, Hq, Hkv, G, window;  // S = sequence length (dense) or the longest document (packed)
     int T;              // total token rows (B * S when dense)
     int pos_per_block;  // positions per workgroup = floor(256 / G)
@@ -155,16 +156,33 @@ fwd_kernel(FwdParams p) {
     const int wpmax = min(p0 + (min(wc0 + 63, used_cols - 1)) / G, S - 1);
 
     // ---- Q fragments (B operand of S^T = K Q^T): column n, d = 16ks + 8g + 0..7
-    bf16x8 qf[2][4];
+    uint4 qraw[2][4];
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
         const uint16_t* qrow = p.q + ((size_t)(sr.row0 + col_pos[nb]) * p.Hq + col_head[nb]) * kHeadDim;
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
-            uint4 x = make_uint4(0, 0, 0, 0);
-            if (col_ok[nb]) x = ld16(qrow + 16 * ks + 8 * g);
-            qf[nb][ks] = as_bf16x8(x);
+            qraw[nb][ks] = make_uint4(0, 0, 0, 0);
+            if (col_ok[nb]) qraw[nb][ks] = ld16(qrow + 16 * ks + 8 * g);
         }
+    }
+    // rotary table entries of this lane's q elements (pairs d, d + 32 are
+    // fragments ks and ks + 2), loaded before the first K/V tile so that the
+    // rotation waits only for them and the q loads
+    float4 rcs[2][2][4];
+    const bool rope = p.rope != nullptr;
+    if (rope) {
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                if (col_ok[nb]) {
+                    load_rope8(p.rope, col_pos[nb], 16 * ks + 8 * g, rcs[nb][ks]);
+                } else {
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) rcs[nb][ks][u] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+                }
+            }
     }
 
     // ---- softmax state, seeded by the sink: m = sink * log2(e), l = 1
@@ -217,10 +235,19 @@ fwd_kernel(FwdParams p) {
         }
     };
 
-    if (t_begin <= t_end) {
-        load_tile(t_begin);
-        store_tile(0);
+    if (t_begin <= t_end) load_tile(t_begin);
+    if (rope) {
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) rope8(qraw[nb][ks], qraw[nb][ks + 2], rcs[nb][ks]);
     }
+    bf16x8 qf[2][4];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) qf[nb][ks] = as_bf16x8(qraw[nb][ks]);
+    if (t_begin <= t_end) store_tile(0);
     __syncthreads();
 
     bool fresh[2] = {true, true};  // row has not seen a key yet
@@ -385,6 +412,7 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {
     p.out = a.out;
     p.lse = a.lse;
     p.cu = a.cu;
+    p.rope = a.rope;
     p.S = a.S;
     p.T = a.T;
     p.Hq = a.Hq;

@@ -16,6 +16,7 @@ struct FwdArgs {
     uint16_t* out;
     float* lse;
     const int* cu;  // packed documents (sequence b = rows cu[b] .. cu[b+1]-1), nullptr = dense [B, S]
+    const float2* rope;  // (cos, sin) table [positions][32]: q rotated at load; nullptr = no rotation
     int B, S, Hq, Hkv, window;  // packed: B = documents, S = longest document
     int T;                      // total token rows (B * S when dense)
     float scale;
@@ -53,6 +54,7 @@ struct DecodeArgs {
     void* workspace;
     int N, Hq, Hkv, max_seqlen, window;
     int page_size, pages_per_seq, ring_tokens;  // paged only (ring_tokens 0 = linear)
+    const float2* rope;  // (cos, sin) table: q rotated at position L_n - 1; nullptr = no rotation
     float scale;
 };
 
@@ -62,6 +64,11 @@ size_t bwd_workspace_bytes(long long total_rows, int Hq);
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream);
 
 size_t decode_workspace_bytes(int N, int Hq, int Hkv, int max_seqlen, int window);
+
+hipError_t launch_rope_table(float2* tab, int P, double base, double factor, double orig_ctx, double alpha,
+                             double beta, hipStream_t stream);
+hipError_t launch_rope_rows(const uint16_t* x, uint16_t* y, const int* positions, const float2* tab, int tab_len,
+                            long long rows, int H, int S, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 
 }  // namespace gptoss

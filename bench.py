@@ -20,7 +20,8 @@ the fraction of the bounding roof) are printed in `parts`; `parts` also times
 paths outside the step: decode through a paged and a ring cache, a training
 step through the autograd wrapper, and prefill of packed documents (16384
 tokens in documents of U{1..4096} tokens, same heads; FLOPs over the pairs
-visible inside each document).
+visible inside each document), and prefill and decode with the YaRN rotary
+embedding fused in (the same FLOPs; bytes add the rotated-key write).
 """
 
 import argparse
@@ -340,6 +341,41 @@ def main():
                 "bound": "mfma" if roof_tf >= BF16_PEAK_TFLOPS else "hbm",
                 "frac_of_roof": round(tf / roof_tf, 4)}
     del vsets
+    # RoPE with YaRN scaling fused into the prefill (q rotated in the load
+    # stage, k once into the rotated-key cache) and into decode (the query);
+    # gpt-oss-like table parameters (base 150000, factor 32 over a 4096-token
+    # original context, ramp 1..32)
+    yarn = dict(base=150000.0, factor=32.0, orig_ctx=4096.0, alpha=1.0, beta=32.0)
+    tab = attn.rope_table(max(S, dec.max_seqlen), **yarn)
+    krots = [torch.empty_like(x["k"]) for x in sets]
+
+    def fwd_rope(w, i=0):
+        x = sets[i % NSETS]
+        o, l = x["outs"][w]
+        attn.fwd_rope(x["q"], x["k"], x["v"], sinks, tab, w, scale, out=o, lse=l, k_rot=krots[i % NSETS])
+
+    def decode_rope(w, i=0):
+        x = sets[i % NSETS]
+        o, l = x["dec_out"][w]
+        attn.decode_rope(x["dq"], x["dk"], x["dv"], dcu, dsinks_, tab, dec.max_seqlen, w, dec.scale, out=o, lse=l,
+                         workspace=dws)
+
+    for name, fn, base in (("fwd_rope", fwd_rope, "fwd"), ("decode_rope", decode_rope, "decode")):
+        for w in WINDOWS:
+            g = capture(lambda: [fn(w, i) for i in range(reps)])
+            g.replay()
+            ms = sorted(timed(g.replay, 1) for _ in range(3))[1] / reps
+            del g
+            extra = 2 * 2 * k.numel() if base == "fwd" else 0  # k read and k_rot written by the pre-pass
+            tf = flops[(base, w)] / (ms * 1e-3) / 1e12
+            gbs = (bytes_[(base, w)] + extra) / (ms * 1e-3) / 1e9
+            ai = flops[(base, w)] / (bytes_[(base, w)] + extra)
+            roof_tf = min(BF16_PEAK_TFLOPS, ai * HBM_PEAK_GBS / 1e3)
+            bound = "mfma" if roof_tf >= BF16_PEAK_TFLOPS else "hbm"
+            parts[f"{name}_{'full' if w == 0 else 'w%d' % w}"] = {
+                "ms": round(ms, 4), "tflops": round(tf, 2), "gbs": round(gbs, 1), "bound": bound,
+                "frac_of_roof": round(tf / roof_tf if bound == "mfma" else gbs / HBM_PEAK_GBS, 4)}
+    del krots
     tf_train = (flops[("fwd", 0)] + flops[("bwd", 0)]) / (ms_train * 1e-3) / 1e12
     parts["autograd_train_full"] = {"ms": round(ms_train, 4), "tflops": round(tf_train, 2), "bound": "mfma",
                                     "frac_of_roof": round(tf_train / BF16_PEAK_TFLOPS, 4)}

@@ -219,6 +219,66 @@ gptoss_status gptoss_attn_bwd_varlen(const void* q, const void* k, const void* v
                                      float* dsinks, void* workspace, size_t workspace_bytes,
                                      void* stream);
 
+/*
+ * Rotary position embedding with YaRN scaling, fused into the prefill and
+ * decode load stage.  Megatron-LM issue "gpt-oss implementation", section
+ * "Positional Encodings / YaRN RoPE Scaling", names YaRN (to 128k+ context)
+ * and cites the YaRN paper (arXiv:2309.00071), whose definitions are used;
+ * the pages give no formula or parameters.  For pair i = 0..31 of a 64-wide
+ * head:
+ *   theta_i = base^(-2i/64);  r_i = orig_ctx * theta_i / (2 pi)  (turns over
+ *   the original context);  gamma_i = clamp((r_i - alpha) / (beta - alpha),
+ *   0, 1);  h_i = (1 - gamma_i) theta_i / factor + gamma_i theta_i;
+ *   m = 0.1 ln(factor) + 1 (m = 1 and h_i = theta_i when factor = 1).
+ * Element i of a q or k row at position p is rotated with element i + 32:
+ *   y_i = x_i c - x_{i+32} s,  y_{i+32} = x_{i+32} c + x_i s,
+ *   c = m cos(p h_i), s = m sin(p h_i)  (fp32, from the table below);
+ * each product and the sum are rounded once to fp32 and the result to bf16
+ * (nearest even): the attention consumes bf16 q and k.
+ *
+ * gptoss_attn_rope_table: fills table, fp32 [positions][32][2] = (c, s),
+ *   evaluated in fp64.  Requires D == 64, positions >= 1, base > 1,
+ *   factor >= 1, and for factor > 1 orig_ctx >= 1 and alpha < beta.
+ */
+gptoss_status gptoss_attn_rope_table(float* table, int positions, int D, double base, double factor,
+                                     double orig_ctx, double alpha, double beta, void* stream);
+
+/*
+ * Rotates rows x bf16 [T, H, D] (token t at position positions[t], int32 [T]
+ * on the device; positions outside [0, table_positions) are clamped) into y
+ * (same layout; y may equal x, otherwise they must not overlap).  Used to
+ * append a new token's key to a rotated KV cache.
+ */
+gptoss_status gptoss_attn_rope_rows(const void* x, void* y, const int* positions, int T, int H, int D,
+                                    const float* table, int table_positions, void* stream);
+
+/*
+ * Prefill forward with the rotation fused: q and k are the unrotated
+ * projections [B, S, H, D] (token i of every batch at position i); the
+ * operation is gptoss_attn_fwd over the rotated q and k.  k is rotated once
+ * by a pre-pass into k_rot (bf16 [B, S, Hkv, D], written; it is also the
+ * rotated key cache a decoder keeps; it must not overlap k); q is rotated in
+ * the attention kernel's load stage.  table: gptoss_attn_rope_table output
+ * with table_positions >= S.
+ */
+gptoss_status gptoss_attn_fwd_rope(const void* q, const void* k, const void* v, const float* sinks,
+                                   const float* table, int table_positions, int B, int S, int Hq, int Hkv,
+                                   int D, int window, float softmax_scale, void* out, float* lse, void* k_rot,
+                                   void* stream);
+
+/*
+ * Decode with the query rotation fused: as gptoss_attn_decode, with q the
+ * unrotated projection of the new token, rotated at its position L_n - 1 in
+ * the kernel's load stage; the caches hold rotated keys (k_rot of the
+ * prefill, then each new token's key through gptoss_attn_rope_rows).
+ * table_positions >= max_seqlen.
+ */
+gptoss_status gptoss_attn_decode_rope(const void* q, const void* k_cache, const void* v_cache,
+                                      const int* cu_seqlens, const float* sinks, const float* table,
+                                      int table_positions, int N, int Hq, int Hkv, int D, int max_seqlen,
+                                      int window, float softmax_scale, void* out, float* lse,
+                                      void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

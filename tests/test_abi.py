@@ -269,3 +269,52 @@ def test_varlen_workspace_size(lib):
         lib.gptoss_attn_bwd_workspace_size(4, 4096, 64, 8, 64, 0)
     assert lib.gptoss_attn_bwd_varlen_workspace_size(0, 64, 8, 64) == 0
     assert lib.gptoss_attn_bwd_varlen_workspace_size(100, 64, 7, 64) == 0
+
+
+def _table(lib, **kw):
+    a = dict(t=P, P=4096, D=64, base=150000.0, factor=32.0, ctx=4096.0, alpha=1.0, beta=32.0)
+    a.update(kw)
+    return lib.gptoss_attn_rope_table(a["t"], a["P"], a["D"], a["base"], a["factor"], a["ctx"], a["alpha"],
+                                      a["beta"], None)
+
+
+@pytest.mark.parametrize("kw,status,frag", [
+    (dict(t=None), 1, "table is NULL"),
+    (dict(t=P + 4), 1, "aligned"),
+    (dict(P=0), 1, "positions"),
+    (dict(D=128), 2, "head_dim"),
+    (dict(base=1.0), 1, "base"),
+    (dict(base=math.nan), 1, "base"),
+    (dict(factor=0.5), 1, "factor"),
+    (dict(ctx=0.0), 1, "original context"),
+    (dict(alpha=32.0, beta=32.0), 1, "alpha < beta"),
+    (dict(beta=math.inf), 1, "alpha < beta"),
+])
+def test_rope_table_rejects_bad_arguments(lib, kw, status, frag):
+    assert _table(lib, **kw) == status
+    assert frag in lib.gptoss_attn_last_error().decode()
+
+
+def test_rope_rows_and_fused_entry_points_reject_bad_arguments(lib):
+    assert lib.gptoss_attn_rope_rows(P, P, None, 4, 8, 64, P, 16, None) == 1
+    assert "positions is NULL" in lib.gptoss_attn_last_error().decode()
+    assert lib.gptoss_attn_rope_rows(P, P, P, 4, 8, 64, P, 0, None) == 1
+    assert lib.gptoss_attn_rope_rows(P, P, P, 4, 8, 32, P, 16, None) == 2
+    assert lib.gptoss_attn_rope_rows(None, None, None, 0, 8, 64, P, 16, None) == 0  # T = 0 is a no-op
+    # forward: the table must cover S; k_rot is required and must not alias k
+    fa = [P, P, P, P, P, 4096, 1, 4097, 64, 8, 64, 0, 0.125, P, P, P, None]
+    assert lib.gptoss_attn_fwd_rope(*fa) == 1 and "rope table" in lib.gptoss_attn_last_error().decode()
+    fa[7] = 4096
+    fa[15] = None
+    assert lib.gptoss_attn_fwd_rope(*fa) == 1 and "k_rot is NULL" in lib.gptoss_attn_last_error().decode()
+    fa[15] = P
+    assert lib.gptoss_attn_fwd_rope(*fa) == 1 and "alias" in lib.gptoss_attn_last_error().decode()
+    fa[4] = None
+    fa[15] = P + 256
+    assert lib.gptoss_attn_fwd_rope(*fa) == 1 and "table is NULL" in lib.gptoss_attn_last_error().decode()
+    # decode: the table must cover max_seqlen
+    da = [P, P, P, P, P, P, 1000, 2, 64, 8, 64, 1024, 0, 0.125, P, P, P, 1 << 30, None]
+    assert lib.gptoss_attn_decode_rope(*da) == 1 and "rope table" in lib.gptoss_attn_last_error().decode()
+    da[5] = None
+    da[6] = 1024
+    assert lib.gptoss_attn_decode_rope(*da) == 1 and "table is NULL" in lib.gptoss_attn_last_error().decode()
