@@ -11,9 +11,13 @@
 // P_sink (0 - Dvec); Megatron-LM issue "gpt-oss implementation", "Attention
 // Sinks", names the feature; the pages give no formula.)
 //
-// Four launches on the caller's stream (pre, dkdv, dq, dsink), no atomics,
+// Three launches on the caller's stream (dq, dkdv, dsink), no atomics,
 // deterministic:
-//   pre    : Dvec and lse*log2(e) per (b, position, head) -> workspace
+//   dq     : query-outer, like the forward: S^T = K Q^T and dP^T = V dO^T
+//            put one column per lane, which is the operand layout of
+//            dQ^T += K^T dS^T (K^T through transposing LDS reads).  Each
+//            row's Dvec = <dout, out> is formed in its prologue and stored
+//            with lse*log2(e) in the workspace for dkdv.
 //   dkdv   : key-outer.  A workgroup owns 128 keys of one KV head (32 per
 //            wave) and walks the query columns (position, head-of-group) that
 //            can see them, 64 columns per step.  S = Q K^T and dP = dO V^T
@@ -22,9 +26,6 @@
 //            that contract over columns: dV^T += dO^T P and dK^T += Q^T dS.
 //            Q^T and dO^T come from the row-major LDS tiles through
 //            transposing LDS reads.
-//   dq     : query-outer, like the forward: S^T = K Q^T and dP^T = V dO^T
-//            put one column per lane, which is the operand layout of
-//            dQ^T += K^T dS^T (K^T through transposing LDS reads).
 //   dsink  : one workgroup per head reduces the per-row terms the dq kernel
 //            left in the workspace ([head][token row], contiguous).
 // P and dP are recomputed in both the key-outer and query-outer kernels.
@@ -64,45 +65,8 @@ struct BwdParams {
     float c;  // scale * log2(e)
 };
 
-// ---------------------------------------------------------------------------
-// pre: 8 lanes per (b, position, head) row, 16 bytes of out and dout each.
-__global__ void __launch_bounds__(kThreads)
-bwd_pre_kernel(BwdParams p, long long rows) {
-    const long long row = (long long)blockIdx.x * 32 + (threadIdx.x >> 3);
-    const int chunk = threadIdx.x & 7;
-    float acc = 0.0f;
-    if (row < rows) {
-        const uint4 o = ld16(p.out + row * kHeadDim + 8 * chunk);
-        const uint4 d = ld16(p.dout + row * kHeadDim + 8 * chunk);
-        const uint32_t ow[4] = {o.x, o.y, o.z, o.w}, dw[4] = {d.x, d.y, d.z, d.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            acc = fmaf(bf16_lo(ow[i]), bf16_lo(dw[i]), acc);
-            acc = fmaf(bf16_hi(ow[i]), bf16_hi(dw[i]), acc);
-        }
-    }
-    acc += __shfl_xor(acc, 1);
-    acc += __shfl_xor(acc, 2);
-    acc += __shfl_xor(acc, 4);
-    if (row < rows && chunk == 0) {
-        const int h = (int)(row % p.Hq);
-        const int tok = (int)(row / p.Hq);
-        size_t li;
-        if (p.cu == nullptr) {
-            const int b = tok / p.S, pos = tok % p.S;
-            li = ((size_t)b * p.Hq + h) * p.S + pos;
-        } else {
-            li = (size_t)h * p.T + tok;
-            // rows outside every document keep a zero dsink term (the dq
-            // kernel overwrites the rows it covers)
-            p.dsterm[li] = 0.0f;
-        }
-        p.ld[row] = make_float2(p.lse[li] * kLog2e, acc);
-    }
-}
-
 // dsink: one workgroup per head sums the rows' exp(sink - lse) r terms
-// (contiguous per head; 16-byte loads, four independent partial sums).
+// (contiguous per head and sequence; four independent partial sums).
 __global__ void __launch_bounds__(kThreads)
 bwd_dsink_kernel(BwdParams p) {
     __shared__ float red[kThreads / 64];
@@ -110,16 +74,20 @@ bwd_dsink_kernel(BwdParams p) {
     const long long n = p.T;
     const float* src = p.dsterm + (size_t)h * n;
     float a0 = 0.0f, a1 = 0.0f, a2 = 0.0f, a3 = 0.0f;
-    const long long n4 = ((size_t)h * n) % 4 == 0 ? n / 4 : 0;  // float4 part (rows start 16-byte aligned)
-    const float4* src4 = reinterpret_cast<const float4*>(src);
-    for (long long i = threadIdx.x; i < n4; i += kThreads) {
-        const float4 v = src4[i];
-        a0 += v.x;
-        a1 += v.y;
-        a2 += v.z;
-        a3 += v.w;
+    // the rows of each sequence (for packed documents, only rows inside a
+    // document hold a term: the dq kernel wrote those), four partial sums
+    for (int b = 0; b < p.B; ++b) {
+        const SeqRows sr = seq_rows(p.cu, p.S, p.Hq, p.T, b);
+        const float* seg = src + sr.row0;
+        int i = threadIdx.x;
+        for (; i + 3 * kThreads < sr.len; i += 4 * kThreads) {
+            a0 += seg[i];
+            a1 += seg[i + kThreads];
+            a2 += seg[i + 2 * kThreads];
+            a3 += seg[i + 3 * kThreads];
+        }
+        for (; i < sr.len; i += kThreads) a0 += seg[i];
     }
-    for (long long i = 4 * n4 + threadIdx.x; i < n; i += kThreads) a0 += src[i];
     float acc = (a0 + a1) + (a2 + a3);
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
@@ -445,24 +413,37 @@ bwd_dq_kernel(BwdParams p, int n_qt, int pos_per_block) {
     // dS = P acc.  (q is not pre-scaled by c here: P must sum, with the
     // sink, to 1 within fp32 rounding for the dsink term below, and a
     // bf16-rounded c q would perturb it by ~1e-3.)
+    //
+    // The row's Dvec = <dout, out> is formed here from the same dO fragments
+    // (the two lane halves hold d = 16 ks + 8 g + 0..7), and {lse log2(e),
+    // Dvec} is stored for the key-outer kernel, which runs after this one.
     bf16x8 qf[4], of[4];
     float lse2 = INFINITY, dvec = 0.0f, dsum = 0.0f;
     {
-        const size_t off = (((size_t)sr.row0 + col_pos) * Hq + col_head) * kHeadDim;
+        const size_t row = ((size_t)sr.row0 + col_pos) * Hq + col_head;
+        const size_t off = row * kHeadDim;
+        float dot = 0.0f;
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
-            uint4 x = make_uint4(0, 0, 0, 0), y = make_uint4(0, 0, 0, 0);
+            uint4 x = make_uint4(0, 0, 0, 0), y = make_uint4(0, 0, 0, 0), o = make_uint4(0, 0, 0, 0);
             if (col_ok) {
                 x = ld16(p.q + off + 16 * ks + 8 * g);
                 y = ld16(p.dout + off + 16 * ks + 8 * g);
+                o = ld16(p.out + off + 16 * ks + 8 * g);
             }
             qf[ks] = as_bf16x8(x);
             of[ks] = as_bf16x8(y);
+            const uint32_t ow[4] = {o.x, o.y, o.z, o.w}, dw[4] = {y.x, y.y, y.z, y.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                dot = fmaf(bf16_lo(ow[i]), bf16_lo(dw[i]), dot);
+                dot = fmaf(bf16_hi(ow[i]), bf16_hi(dw[i]), dot);
+            }
         }
+        dvec = sum_across_halves(dot);
         if (col_ok) {
-            const float2 v = p.ld[((size_t)sr.row0 + col_pos) * Hq + col_head];
-            lse2 = v.x;
-            dvec = v.y;
+            lse2 = p.lse[sr.lse_base + col_head * sr.lse_hstride + col_pos] * kLog2e;
+            if (g == 0) p.ld[row] = make_float2(lse2, dvec);
         }
     }
 
@@ -640,18 +621,15 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
     p.scale = a.scale;
     p.c = a.scale * kLog2e;
 
-    const long long rows = (long long)a.T * a.Hq;
     const int n_kt = (a.S + kKeysPerBlock - 1) / kKeysPerBlock;
     const int ppb = kDqCols / p.G >= 1 ? kDqCols / p.G : 1;
     const int n_qt = (a.S + ppb - 1) / ppb;
-    if ((rows + 31) / 32 > 0x7fffffffLL || (long long)n_qt * a.B * a.Hkv > 0x7fffffffLL)
-        return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(bwd_pre_kernel, dim3((unsigned)((rows + 31) / 32)), dim3(kThreads), 0, stream, p, rows);
+    if ((long long)n_qt * a.B * a.Hkv > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    // dq first: it also stores {lse log2(e), Dvec} per row for dkdv
+    hipLaunchKernelGGL(bwd_dq_kernel, dim3((unsigned)(n_qt * a.B * a.Hkv)), dim3(kThreads), 0, stream, p, n_qt, ppb);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(bwd_dkdv_kernel, dim3((unsigned)(n_kt * a.B * a.Hkv)), dim3(kThreads), 0, stream, p, n_kt);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(bwd_dq_kernel, dim3((unsigned)(n_qt * a.B * a.Hkv)), dim3(kThreads), 0, stream, p, n_qt, ppb);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(bwd_dsink_kernel, dim3(a.Hq), dim3(kThreads), 0, stream, p);
     return hipGetLastError();

@@ -382,7 +382,7 @@ def main():
     log(json.dumps(parts, indent=1))
 
     # Dominant unit of the step: the backward entry point of the full-causal
-    # layer (4 launches: pre, dkdv, dq, dsink; dkdv is the largest).  Its
+    # layer (3 launches: dq, dkdv, dsink; dkdv is the largest).  Its
     # duration per call comes from events on the stream its kernels run on,
     # around a graph of back-to-back calls; achieved uses the algorithmic
     # 10*D FLOPs per visible pair.
@@ -391,7 +391,7 @@ def main():
     tb = measured_traffic("bwd_full")
     roofline = {"bound": "mfma", "achieved": round(ach, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(ach / BF16_PEAK_TFLOPS, 4), "traffic": tb,
-                "kernel": "gptoss_attn_bwd, full-causal layer (bwd_pre + bwd_dkdv + bwd_dq + bwd_dsink)",
+                "kernel": "gptoss_attn_bwd, full-causal layer (bwd_dq + bwd_dkdv + bwd_dsink)",
                 "ms_per_launch": round(ms_b, 4)}
     ach_f = flops[("fwd", 0)] / (part_ms[("fwd", 0)] * 1e-3) / 1e12
     roofline_fwd = {"bound": "mfma", "achieved": round(ach_f, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
