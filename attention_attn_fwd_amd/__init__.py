@@ -16,6 +16,7 @@ all computation runs in the library's HIP kernels.
     out, lse, k_rot = fwd_rope(q, k, v, sinks, table, window, scale)            # RoPE fused into prefill
     out, lse = decode_rope(q, k_cache, v_cache, cu_seqlens, sinks, table, max_seqlen, window, scale)
     y = rope_rows(x, positions, table)                                          # rotate rows (cache append)
+    dq, dk, dv, dsinks = bwd_rope(q, k_rot, v, sinks, table, out, lse, dout, window, scale)  # grads wrt unrotated q, k
 
 Training: attention_attn_fwd_amd.autograd.sink_attention (torch autograd over
 fwd/bwd).
@@ -28,6 +29,7 @@ from ._lib import AttnError
 
 __all__ = ["fwd", "bwd", "decode", "decode_paged", "fwd_varlen", "bwd_varlen", "bwd_workspace_size",
            "bwd_varlen_workspace_size", "decode_workspace_size", "rope_table", "rope_rows", "fwd_rope", "decode_rope",
+           "bwd_rope", "bwd_rope_workspace_size",
            "AttnError", "abi_version"]
 
 
@@ -290,8 +292,9 @@ def _need_table(table):
         raise ValueError("table must be [positions, 32, 2]")
 
 
-def rope_rows(x, positions, table, out=None):
-    """Rotate rows x bf16 [T, H, 64] by positions int32 [T] (device)."""
+def rope_rows(x, positions, table, out=None, transpose=False):
+    """Rotate rows x bf16 [T, H, 64] by positions int32 [T] (device); with
+    transpose, apply the adjoint R^T (gradients back to unrotated rows)."""
     _need(x, "x", torch.bfloat16, 3)
     _need(positions, "positions", torch.int32, 1)
     _need_table(table)
@@ -303,7 +306,7 @@ def rope_rows(x, positions, table, out=None):
     _need(out, "out", torch.bfloat16, 3)
     lib = _lib.load()
     st = lib.gptoss_attn_rope_rows(x.data_ptr(), out.data_ptr(), positions.data_ptr(), T, H, D, table.data_ptr(),
-                                   table.shape[0], _stream(x.device))
+                                   table.shape[0], 1 if transpose else 0, _stream(x.device))
     _lib.check(st, lib)
     return out
 
@@ -362,3 +365,39 @@ def decode_rope(q, k_cache, v_cache, cu_seqlens, sinks, table, max_seqlen, windo
                                      workspace.data_ptr(), workspace.numel(), _stream(q.device))
     _lib.check(st, lib)
     return out, lse
+
+
+def bwd_rope_workspace_size(B, S, Hq, Hkv, D=64):
+    return int(_lib.load().gptoss_attn_bwd_rope_workspace_size(B, S, Hq, Hkv, D))
+
+
+def bwd_rope(q, k_rot, v, sinks, table, out, lse, dout, window=0, scale=None, workspace=None, grads=None):
+    """Backward of fwd_rope for sum(dout * out): (dq, dk, dv, dsinks) with dq,
+    dk the gradients with respect to the unrotated q and k.  k_rot is
+    fwd_rope's rotated-key output."""
+    for t, n in ((q, "q"), (k_rot, "k_rot"), (v, "v"), (out, "out"), (dout, "dout")):
+        _need(t, n, torch.bfloat16, 4)
+    _need(sinks, "sinks", torch.float32, 1)
+    _need(lse, "lse", torch.float32, 3)
+    _need_table(table)
+    B, S, Hq, D = q.shape
+    Hkv = k_rot.shape[2]
+    if (k_rot.shape != (B, S, Hkv, D) or v.shape != k_rot.shape or out.shape != q.shape or dout.shape != q.shape
+            or lse.shape != (B, Hq, S) or sinks.shape != (Hq,)):
+        raise ValueError("shape mismatch among backward inputs")
+    scale = (1.0 / D ** 0.5) if scale is None else float(scale)
+    if grads is None:
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k_rot), torch.empty_like(v)
+        dsinks = torch.empty((Hq,), dtype=torch.float32, device=q.device)
+    else:
+        dq, dk, dv, dsinks = grads
+    need = bwd_rope_workspace_size(B, S, Hq, Hkv, D)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    lib = _lib.load()
+    st = lib.gptoss_attn_bwd_rope(q.data_ptr(), k_rot.data_ptr(), v.data_ptr(), sinks.data_ptr(), table.data_ptr(),
+                                  table.shape[0], out.data_ptr(), lse.data_ptr(), dout.data_ptr(), B, S, Hq, Hkv, D,
+                                  int(window), scale, dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), dsinks.data_ptr(),
+                                  workspace.data_ptr(), workspace.numel(), _stream(q.device))
+    _lib.check(st, lib)
+    return dq, dk, dv, dsinks

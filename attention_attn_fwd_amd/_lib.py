@@ -20,6 +20,7 @@ EXPORTS = [
     "gptoss_attn_decode_workspace_size", "gptoss_attn_decode", "gptoss_attn_decode_paged",
     "gptoss_attn_fwd_varlen", "gptoss_attn_bwd_varlen_workspace_size", "gptoss_attn_bwd_varlen",
     "gptoss_attn_rope_table", "gptoss_attn_rope_rows", "gptoss_attn_fwd_rope", "gptoss_attn_decode_rope",
+    "gptoss_attn_bwd_rope_workspace_size", "gptoss_attn_bwd_rope",
 ]
 
 _lib = None
@@ -74,12 +75,17 @@ def load(path=None):
     lib.gptoss_attn_rope_table.restype = c_int
     lib.gptoss_attn_rope_table.argtypes = [c_void_p, c_int, c_int] + [c_double] * 5 + [c_void_p]
     lib.gptoss_attn_rope_rows.restype = c_int
-    lib.gptoss_attn_rope_rows.argtypes = [c_void_p] * 3 + [c_int] * 3 + [c_void_p, c_int, c_void_p]
+    lib.gptoss_attn_rope_rows.argtypes = [c_void_p] * 3 + [c_int] * 3 + [c_void_p, c_int, c_int, c_void_p]
     lib.gptoss_attn_fwd_rope.restype = c_int
     lib.gptoss_attn_fwd_rope.argtypes = [c_void_p] * 5 + [c_int] * 7 + [c_float] + [c_void_p] * 4
     lib.gptoss_attn_decode_rope.restype = c_int
     lib.gptoss_attn_decode_rope.argtypes = [c_void_p] * 6 + [c_int] * 7 + [c_float] + [c_void_p] * 3 + \
         [c_size_t, c_void_p]
+    lib.gptoss_attn_bwd_rope_workspace_size.restype = c_size_t
+    lib.gptoss_attn_bwd_rope_workspace_size.argtypes = [c_int] * 5
+    lib.gptoss_attn_bwd_rope.restype = c_int
+    lib.gptoss_attn_bwd_rope.argtypes = [c_void_p] * 5 + [c_int] + [c_void_p] * 3 + [c_int] * 6 + [c_float] + \
+        [c_void_p] * 5 + [c_size_t, c_void_p]
     if path == LIB_PATH:
         _lib = lib
     return lib

@@ -450,7 +450,7 @@ gptoss_status gptoss_attn_rope_table(float* table, int positions, int D, double 
 }
 
 gptoss_status gptoss_attn_rope_rows(const void* x, void* y, const int* positions, int T, int H, int D,
-                                    const float* table, int table_positions, void* stream) {
+                                    const float* table, int table_positions, int transpose, void* stream) {
     if (T < 0 || H < 1) return fail(GPTOSS_ERR_INVALID_ARGUMENT, "T (%d) must be >= 0 and H (%d) >= 1", T, H);
     if (D != 64) return fail(GPTOSS_ERR_UNSUPPORTED, "head_dim %d is not supported (only 64)", D);
     if (table_positions < 1)
@@ -466,7 +466,8 @@ gptoss_status gptoss_attn_rope_rows(const void* x, void* y, const int* positions
     if (st != GPTOSS_OK) return st;
     return launched(gptoss::launch_rope_rows(static_cast<const uint16_t*>(x), static_cast<uint16_t*>(y), positions,
                                              reinterpret_cast<const float2*>(table), table_positions,
-                                             (long long)T * H, H, 1, static_cast<hipStream_t>(stream)),
+                                             (long long)T * H, H, 1, transpose != 0,
+                                             static_cast<hipStream_t>(stream)),
                     "rope rows");
 }
 
@@ -496,7 +497,7 @@ gptoss_status gptoss_attn_fwd_rope(const void* q, const void* k, const void* v, 
     const hipStream_t s = static_cast<hipStream_t>(stream);
     const float2* tab = reinterpret_cast<const float2*>(table);
     hipError_t e = gptoss::launch_rope_rows(static_cast<const uint16_t*>(k), static_cast<uint16_t*>(k_rot), nullptr,
-                                            tab, table_positions, (long long)B * S * Hkv, Hkv, S, s);
+                                            tab, table_positions, (long long)B * S * Hkv, Hkv, S, false, s);
     if (e != hipSuccess) return launched(e, "rope on k");
     gptoss::FwdArgs a;
     a.q = static_cast<const uint16_t*>(q);
@@ -567,6 +568,87 @@ gptoss_status gptoss_attn_decode_rope(const void* q, const void* k_cache, const 
     a.rope = reinterpret_cast<const float2*>(table);
     a.scale = softmax_scale;
     return launched(gptoss::launch_decode(a, static_cast<hipStream_t>(stream)), "decode with rope");
+}
+
+// Backward through the rotation: q is rotated into the workspace, the
+// backward runs on the rotated q and k, and dq, dk are carried back through
+// R^T in place.
+static size_t align256(size_t n) { return (n + 255) / 256 * 256; }
+
+size_t gptoss_attn_bwd_rope_workspace_size(int B, int S, int Hq, int Hkv, int D) {
+    if (B <= 0 || S <= 0 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || D != 64) return 0;
+    return align256((size_t)B * S * Hq * D * 2) + gptoss::bwd_workspace_bytes((long long)B * S, Hq);
+}
+
+gptoss_status gptoss_attn_bwd_rope(const void* q, const void* k_rot, const void* v, const float* sinks,
+                                   const float* table, int table_positions, const void* out, const float* lse,
+                                   const void* dout, int B, int S, int Hq, int Hkv, int D, int window,
+                                   float softmax_scale, void* dq, void* dk, void* dv, float* dsinks,
+                                   void* workspace, size_t workspace_bytes, void* stream) {
+    if (B < 0 || S < 0) return fail(GPTOSS_ERR_INVALID_ARGUMENT, "B (%d) and S (%d) must be >= 0", B, S);
+    gptoss_status st = check_common(Hq, Hkv, D, window, softmax_scale);
+    if (st != GPTOSS_OK) return st;
+    if (B == 0 || S == 0) return ok();
+    if ((long long)B * S > kIndexLimit)
+        return fail(GPTOSS_ERR_INVALID_ARGUMENT, "B*S = %lld exceeds 2^31-1", (long long)B * S);
+    if ((long long)B * S * Hq > kIndexLimit)
+        return fail(GPTOSS_ERR_INVALID_ARGUMENT, "B*S*Hq = %lld rows exceeds 2^31-1", (long long)B * S * Hq);
+    if (table_positions < S)
+        return fail(GPTOSS_ERR_INVALID_ARGUMENT, "rope table holds %d positions, S is %d", table_positions, S);
+    CHECK_PTR(q, 16);
+    CHECK_PTR(k_rot, 16);
+    CHECK_PTR(v, 16);
+    CHECK_PTR(sinks, 4);
+    CHECK_PTR(table, 16);
+    CHECK_PTR(out, 16);
+    CHECK_PTR(lse, 4);
+    CHECK_PTR(dout, 16);
+    CHECK_PTR(dq, 16);
+    CHECK_PTR(dk, 16);
+    CHECK_PTR(dv, 16);
+    CHECK_PTR(dsinks, 4);
+    const size_t need = gptoss_attn_bwd_rope_workspace_size(B, S, Hq, Hkv, D);
+    if (workspace_bytes < need)
+        return fail(GPTOSS_ERR_INVALID_ARGUMENT, "workspace_bytes %zu < required %zu", workspace_bytes, need);
+    CHECK_PTR(workspace, 256);
+    st = check_device();
+    if (st != GPTOSS_OK) return st;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    const float2* tab = reinterpret_cast<const float2*>(table);
+    uint16_t* q_rot = static_cast<uint16_t*>(workspace);
+    void* bwd_ws = static_cast<char*>(workspace) + align256((size_t)B * S * Hq * D * 2);
+    hipError_t e = gptoss::launch_rope_rows(static_cast<const uint16_t*>(q), q_rot, nullptr, tab, table_positions,
+                                            (long long)B * S * Hq, Hq, S, false, s);
+    if (e != hipSuccess) return launched(e, "rope on q");
+    gptoss::BwdArgs a;
+    a.q = q_rot;
+    a.k = static_cast<const uint16_t*>(k_rot);
+    a.v = static_cast<const uint16_t*>(v);
+    a.sinks = sinks;
+    a.out = static_cast<const uint16_t*>(out);
+    a.lse = lse;
+    a.dout = static_cast<const uint16_t*>(dout);
+    a.dq = static_cast<uint16_t*>(dq);
+    a.dk = static_cast<uint16_t*>(dk);
+    a.dv = static_cast<uint16_t*>(dv);
+    a.dsinks = dsinks;
+    a.workspace = bwd_ws;
+    a.cu = nullptr;
+    a.B = B;
+    a.S = S;
+    a.T = B * S;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.window = window;
+    a.scale = softmax_scale;
+    e = gptoss::launch_bwd(a, s);
+    if (e != hipSuccess) return launched(e, "backward with rope");
+    e = gptoss::launch_rope_rows(static_cast<const uint16_t*>(dq), static_cast<uint16_t*>(dq), nullptr, tab,
+                                 table_positions, (long long)B * S * Hq, Hq, S, true, s);
+    if (e != hipSuccess) return launched(e, "rope adjoint on dq");
+    e = gptoss::launch_rope_rows(static_cast<const uint16_t*>(dk), static_cast<uint16_t*>(dk), nullptr, tab,
+                                 table_positions, (long long)B * S * Hkv, Hkv, S, true, s);
+    return launched(e, "rope adjoint on dk");
 }
 
 }  // extern "C"

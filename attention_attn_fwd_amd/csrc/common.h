@@ -130,10 +130,12 @@ __device__ __forceinline__ size_t row_off(int row, uint32_t stride) { return (si
 // Rotary embedding of 8 element pairs: a holds elements i .. i+7 and b their
 // partners i+32 .. i+39 (half-split pairing of a 64-wide head), cs the
 // (cos, sin) pairs of i .. i+7 as four float4 {c_i, s_i, c_{i+1}, s_{i+1}}.
-//   a' = a c - b s,  b' = b c + a s
+//   a' = a c - b s,  b' = b c + a s            (the rotation R)
+// or, with transpose, the adjoint R^T that carries gradients back:
+//   a' = a c + b s,  b' = b c - a s
 // Each product and the sum are rounded once to fp32 (no fused multiply-add),
 // then the results to bf16 (nearest even).
-__device__ __forceinline__ void rope8(uint4& a, uint4& b, const float4 (&cs)[4]) {
+__device__ __forceinline__ void rope8(uint4& a, uint4& b, const float4 (&cs)[4], bool transpose = false) {
 #pragma clang fp contract(off)
     const uint32_t aw[4] = {a.x, a.y, a.z, a.w}, bw[4] = {b.x, b.y, b.z, b.w};
     uint32_t ra[4], rb[4];
@@ -141,7 +143,8 @@ __device__ __forceinline__ void rope8(uint4& a, uint4& b, const float4 (&cs)[4])
     for (int u = 0; u < 4; ++u) {
         const float a0 = __uint_as_float(aw[u] << 16), a1 = __uint_as_float(aw[u] & 0xffff0000u);
         const float b0 = __uint_as_float(bw[u] << 16), b1 = __uint_as_float(bw[u] & 0xffff0000u);
-        const float c0 = cs[u].x, s0 = cs[u].y, c1 = cs[u].z, s1 = cs[u].w;
+        const float c0 = cs[u].x, c1 = cs[u].z;
+        const float s0 = transpose ? -cs[u].y : cs[u].y, s1 = transpose ? -cs[u].w : cs[u].w;
         const float ya0 = a0 * c0 - b0 * s0, ya1 = a1 * c1 - b1 * s1;
         const float yb0 = b0 * c0 + a0 * s0, yb1 = b1 * c1 + a1 * s1;
         bf16x2 pa, pb;

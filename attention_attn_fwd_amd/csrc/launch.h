@@ -68,7 +68,7 @@ size_t decode_workspace_bytes(int N, int Hq, int Hkv, int max_seqlen, int window
 hipError_t launch_rope_table(float2* tab, int P, double base, double factor, double orig_ctx, double alpha,
                              double beta, hipStream_t stream);
 hipError_t launch_rope_rows(const uint16_t* x, uint16_t* y, const int* positions, const float2* tab, int tab_len,
-                            long long rows, int H, int S, hipStream_t stream);
+                            long long rows, int H, int S, bool transpose, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 
 }  // namespace gptoss

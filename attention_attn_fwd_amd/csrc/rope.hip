@@ -42,10 +42,11 @@ __global__ void __launch_bounds__(256) rope_table_kernel(float2* tab, long long 
 
 // Rotates rows [T, H, 64] (bf16) by their token's position: positions[t]
 // (clamped into the table) or, when positions is null, t mod S (a dense
-// [B, S, H, 64] tensor).  One thread per (row, 8-pair octet); y may be x.
+// [B, S, H, 64] tensor); transpose applies R^T (gradients).  One thread per
+// (row, 8-pair octet); y may be x.
 __global__ void __launch_bounds__(256) rope_rows_kernel(const uint16_t* x, uint16_t* y, const int* positions,
                                                          const float2* tab, int tab_len, long long rows, int H,
-                                                         int S) {
+                                                         int S, int transpose) {
     const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
     if (idx >= rows * 4) return;
     const long long row = idx >> 2;
@@ -57,7 +58,7 @@ __global__ void __launch_bounds__(256) rope_rows_kernel(const uint16_t* x, uint1
     uint4 a = ld16(src), b = ld16(src + kPairs);
     float4 cs[4];
     load_rope8(tab, pos, 8 * o, cs);
-    rope8(a, b, cs);
+    rope8(a, b, cs, transpose != 0);
     uint16_t* dst = y + row * kHeadDim + 8 * o;
     st16(dst, a);
     st16(dst + kPairs, b);
@@ -77,11 +78,11 @@ hipError_t launch_rope_table(float2* tab, int P, double base, double factor, dou
 }
 
 hipError_t launch_rope_rows(const uint16_t* x, uint16_t* y, const int* positions, const float2* tab, int tab_len,
-                            long long rows, int H, int S, hipStream_t stream) {
+                            long long rows, int H, int S, bool transpose, hipStream_t stream) {
     const long long blocks = (rows * 4 + 255) / 256;
     if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL(rope_rows_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, x, y, positions, tab, tab_len,
-                       rows, H, S);
+                       rows, H, S, transpose ? 1 : 0);
     return hipGetLastError();
 }
 

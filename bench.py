@@ -21,7 +21,10 @@ paths outside the step: decode through a paged and a ring cache, a training
 step through the autograd wrapper, and prefill of packed documents (16384
 tokens in documents of U{1..4096} tokens, same heads; FLOPs over the pairs
 visible inside each document), and prefill and decode with the YaRN rotary
-embedding fused in (the same FLOPs; bytes add the rotated-key write).
+embedding fused in (the same FLOPs; bytes add the rotated-key write; the
+backward adds the query pre-pass and the adjoint rotation of dq and dk), and
+the forward of the small (B=1, S=512, 8q/1kv) and long-context (B=1,
+S=65536) workloads.
 """
 
 import argparse
@@ -261,15 +264,18 @@ def main():
     del g_steps
 
     # ---- per-part launch durations: a graph of `reps` back-to-back calls of
-    # one part (rotating over the buffer sets), replayed three times; the
-    # median replay / reps
-    reps = 4 * NSETS
+    # one part (rotating over the buffer sets), replayed once untimed, then
+    # five times timed; the median replay / reps
+    def median_replay(g):
+        return sorted(timed(g.replay, 1) for _ in range(5))[2]
+
+    reps = 5 * NSETS  # 20 back-to-back calls per graph
     part_ms = {}
     for name, fn in (("fwd", fwd), ("bwd", bwd), ("decode", decode)):
         for w in WINDOWS:
             g = capture(lambda: [fn(w, i) for i in range(reps)])
             g.replay()
-            part_ms[(name, w)] = sorted(timed(g.replay, 1) for _ in range(3))[1] / reps
+            part_ms[(name, w)] = median_replay(g) / reps
             del g
     # training step of one full-causal layer through the autograd wrapper
     # (forward + backward, the same kernels; timed eagerly, host marshalling
@@ -315,7 +321,7 @@ def main():
                               out=o, lse=l, workspace=dws)
         g = capture(lambda: [pfn(i) for i in range(reps)])
         g.replay()
-        ms = sorted(timed(g.replay, 1) for _ in range(3))[1] / reps
+        ms = median_replay(g) / reps
         del g
         gbs = bytes_[("decode", w)] / (ms * 1e-3) / 1e9
         parts[label] = {"ms": round(ms, 4), "gbs": round(gbs, 1), "bound": "hbm",
@@ -330,7 +336,7 @@ def main():
         for w in WINDOWS:
             g = capture(lambda: [fn(w, i) for i in range(reps)])
             g.replay()
-            ms = sorted(timed(g.replay, 1) for _ in range(3))[1] / reps
+            ms = median_replay(g) / reps
             del g
             tf = flops[(name, w)] / (ms * 1e-3) / 1e12
             gbs = bytes_[(name, w)] / (ms * 1e-3) / 1e9
@@ -364,7 +370,7 @@ def main():
         for w in WINDOWS:
             g = capture(lambda: [fn(w, i) for i in range(reps)])
             g.replay()
-            ms = sorted(timed(g.replay, 1) for _ in range(3))[1] / reps
+            ms = median_replay(g) / reps
             del g
             extra = 2 * 2 * k.numel() if base == "fwd" else 0  # k read and k_rot written by the pre-pass
             tf = flops[(base, w)] / (ms * 1e-3) / 1e12
@@ -375,7 +381,58 @@ def main():
             parts[f"{name}_{'full' if w == 0 else 'w%d' % w}"] = {
                 "ms": round(ms, 4), "tflops": round(tf, 2), "gbs": round(gbs, 1), "bound": bound,
                 "frac_of_roof": round(tf / roof_tf if bound == "mfma" else gbs / HBM_PEAK_GBS, 4)}
-    del krots
+    # backward with RoPE (training): out, lse and k_rot are those fwd_rope
+    # left in every buffer set above; q is rotated by a pre-pass into the
+    # workspace and dq, dk are carried back by the adjoint rotation in place
+    rws = torch.empty(attn.bwd_rope_workspace_size(B, S, Hq, Hkv, D), dtype=torch.uint8, device=dev)
+
+    def bwd_rope(w, i=0):
+        x = sets[i % NSETS]
+        o, l = x["outs"][w]
+        attn.bwd_rope(x["q"], krots[i % NSETS], x["v"], sinks, tab, o, l, x["dout"], w, scale, workspace=rws,
+                      grads=x["grads"][w])
+
+    for w in WINDOWS:
+        g = capture(lambda: [bwd_rope(w, i) for i in range(reps)])
+        g.replay()
+        ms = median_replay(g) / reps
+        del g
+        extra = 2 * 2 * q.numel() + 2 * 2 * (q.numel() + k.numel())  # q pre-pass; adjoint on dq, dk
+        tf = flops[("bwd", w)] / (ms * 1e-3) / 1e12
+        gbs = (bytes_[("bwd", w)] + extra) / (ms * 1e-3) / 1e9
+        roof_tf = min(BF16_PEAK_TFLOPS, flops[("bwd", w)] / (bytes_[("bwd", w)] + extra) * HBM_PEAK_GBS / 1e3)
+        parts[f"bwd_rope_{'full' if w == 0 else 'w%d' % w}"] = {
+            "ms": round(ms, 4), "tflops": round(tf, 2), "gbs": round(gbs, 1),
+            "bound": "mfma" if roof_tf >= BF16_PEAK_TFLOPS else "hbm", "frac_of_roof": round(tf / roof_tf, 4)}
+    del krots, rws
+    # the small workload (B=1, S=512, 8q/1kv) and the long-context workload
+    # (B=1, S=65536, 64q/8kv, values ~ N(0, 0.5^2)): forward of both layers
+    for cname, label in (("c0_b1_s512_h8x1", "c0"), ("c2_b1_s65536_h64x8", "c2")):
+        cc = synth.config_inputs(cname)
+        cB, cS, cHq, _ = cc.q.shape
+        csets = []
+        for _ in range(NSETS):
+            cq = cc.q.to(dev)
+            csets.append((cq, cc.k.to(dev), cc.v.to(dev), torch.empty_like(cq),
+                          torch.empty(cB, cHq, cS, device=dev)))
+        csk = cc.sinks.to(dev)
+        for w in WINDOWS:
+            def cfn(i, w=w):
+                cq, ck, cv, co, cl = csets[i % NSETS]
+                attn.fwd(cq, ck, cv, csk, w, cc.scale, out=co, lse=cl)
+            g = capture(lambda: [cfn(i) for i in range(reps)])
+            g.replay()
+            ms = median_replay(g) / reps
+            del g
+            fl = 4 * D * cB * cHq * pairs_per_head(cS, w)
+            by = 2 * (2 * cc.q.numel() + 2 * cc.k.numel()) + 4 * cB * cHq * cS
+            tf = fl / (ms * 1e-3) / 1e12
+            gbs = by / (ms * 1e-3) / 1e9
+            roof_tf = min(BF16_PEAK_TFLOPS, fl / by * HBM_PEAK_GBS / 1e3)
+            parts[f"{label}_fwd_{'full' if w == 0 else 'w%d' % w}"] = {
+                "ms": round(ms, 4), "tflops": round(tf, 2), "gbs": round(gbs, 1),
+                "bound": "mfma" if roof_tf >= BF16_PEAK_TFLOPS else "hbm", "frac_of_roof": round(tf / roof_tf, 4)}
+        del csets
     tf_train = (flops[("fwd", 0)] + flops[("bwd", 0)]) / (ms_train * 1e-3) / 1e12
     parts["autograd_train_full"] = {"ms": round(ms_train, 4), "tflops": round(tf_train, 2), "bound": "mfma",
                                     "frac_of_roof": round(tf_train / BF16_PEAK_TFLOPS, 4)}

@@ -247,10 +247,13 @@ gptoss_status gptoss_attn_rope_table(float* table, int positions, int D, double 
  * Rotates rows x bf16 [T, H, D] (token t at position positions[t], int32 [T]
  * on the device; positions outside [0, table_positions) are clamped) into y
  * (same layout; y may equal x, otherwise they must not overlap).  Used to
- * append a new token's key to a rotated KV cache.
+ * append a new token's key to a rotated KV cache.  transpose != 0 applies
+ * the adjoint R^T instead (y_i = x_i c + x_{i+32} s, y_{i+32} = x_{i+32} c -
+ * x_i s), which carries a gradient with respect to rotated rows back to the
+ * unrotated ones.
  */
 gptoss_status gptoss_attn_rope_rows(const void* x, void* y, const int* positions, int T, int H, int D,
-                                    const float* table, int table_positions, void* stream);
+                                    const float* table, int table_positions, int transpose, void* stream);
 
 /*
  * Prefill forward with the rotation fused: q and k are the unrotated
@@ -278,6 +281,28 @@ gptoss_status gptoss_attn_decode_rope(const void* q, const void* k_cache, const 
                                       int table_positions, int N, int Hq, int Hkv, int D, int max_seqlen,
                                       int window, float softmax_scale, void* out, float* lse,
                                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Training backward of gptoss_attn_fwd_rope for the loss sum(dout * out):
+ * gradients with respect to the unrotated q and k.  Takes q (unrotated) and
+ * k_rot (the forward's rotated keys); q is rotated into the workspace, the
+ * backward of gptoss_attn_bwd runs on the rotated q and k, and dq, dk are
+ * carried back through the adjoint rotation R^T (in place, after rounding to
+ * bf16).  The rounding of the rotated q and k to bf16 is not differentiated
+ * (its derivative is taken as 1).
+ *   q, out, dout bf16 [B, S, Hq, D]; k_rot, v bf16 [B, S, Hkv, D];
+ *   lse fp32 [B, Hq, S] as written by gptoss_attn_fwd_rope      read
+ *   dq [B,S,Hq,D], dk, dv [B,S,Hkv,D] bf16; dsinks fp32 [Hq]    written
+ *   workspace  gptoss_attn_bwd_rope_workspace_size(B, S, Hq, Hkv, D) bytes,
+ *              256-byte aligned (the rotated q, then the backward's own).
+ */
+size_t gptoss_attn_bwd_rope_workspace_size(int B, int S, int Hq, int Hkv, int D);
+gptoss_status gptoss_attn_bwd_rope(const void* q, const void* k_rot, const void* v, const float* sinks,
+                                   const float* table, int table_positions, const void* out,
+                                   const float* lse, const void* dout, int B, int S, int Hq, int Hkv,
+                                   int D, int window, float softmax_scale, void* dq, void* dk,
+                                   void* dv, float* dsinks, void* workspace,
+                                   size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -32,7 +32,7 @@ import numpy as np
 import torch
 
 __all__ = ["yarn_inv_freq", "yarn_mscale", "rope_table", "apply_rope_exact", "apply_rope_bf16",
-           "ref_fwd_rope", "ref_decode_rope"]
+           "apply_rope_adjoint", "ref_fwd_rope", "ref_decode_rope", "ref_bwd_rope"]
 
 
 def yarn_inv_freq(D, base, factor, orig_ctx, alpha, beta):
@@ -66,6 +66,16 @@ def apply_rope_exact(x, positions, cos, sin):
     s = sin[positions][:, None, :]
     x1, x2 = x[..., :half], x[..., half:]
     return np.concatenate([x1 * c - x2 * s, x2 * c + x1 * s], axis=-1)
+
+
+def apply_rope_adjoint(g, positions, cos, sin):
+    """The adjoint R^T of the rotation (fp64): carries a gradient with
+    respect to rotated rows back to the unrotated ones."""
+    half = g.shape[-1] // 2
+    c = cos[positions][:, None, :]
+    s = sin[positions][:, None, :]
+    g1, g2 = g[..., :half], g[..., half:]
+    return np.concatenate([g1 * c + g2 * s, g2 * c - g1 * s], axis=-1)
 
 
 def _to_bf16(a32):
@@ -107,3 +117,26 @@ def ref_decode_rope(q, k_cache, v_cache, cu_seqlens, sinks, window, scale, cos32
     pos = np.maximum(L - 1, 0)
     qr = apply_rope_bf16(q, pos, cos32, sin32) if q.shape[0] else q
     return ref_decode(qr, k_cache, v_cache, cu_seqlens, sinks, window, scale)
+
+
+def ref_bwd_rope(q, k, v, sinks, dout, window, scale, cos, sin, exact=False, **kw):
+    """Backward of sum(dout * out) for prefill with RoPE on q and k, with
+    respect to the unrotated q and k: the rotated q, k enter ref_bwd and
+    dq, dk come back through the adjoint.  exact=False follows the bf16 path
+    (rotated q, k rounded as in ref_fwd_rope; cos/sin the fp32 tables; the
+    rounding's derivative taken as 1); exact=True rotates in fp64 (cos/sin
+    fp64 tables), the plain derivative for finite-difference pins."""
+    from .attn import ref_bwd
+    S = q.shape[1]
+    pos = np.arange(S)
+    if exact:
+        rot = lambda x: apply_rope_exact(x, pos, cos, sin)
+    else:
+        rot = lambda x: apply_rope_bf16(x, pos, cos, sin)
+    qr = np.stack([rot(q[b]) for b in range(q.shape[0])])
+    kr = np.stack([rot(k[b]) for b in range(k.shape[0])])
+    dqr, dkr, dv, ds = ref_bwd(qr, kr, v, sinks, dout, window, scale, **kw)
+    c64, s64 = cos.astype(np.float64), sin.astype(np.float64)
+    dq = np.stack([apply_rope_adjoint(dqr[b], pos, c64, s64) for b in range(q.shape[0])])
+    dk = np.stack([apply_rope_adjoint(dkr[b], pos, c64, s64) for b in range(k.shape[0])])
+    return dq, dk, dv, ds

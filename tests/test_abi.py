@@ -296,11 +296,11 @@ def test_rope_table_rejects_bad_arguments(lib, kw, status, frag):
 
 
 def test_rope_rows_and_fused_entry_points_reject_bad_arguments(lib):
-    assert lib.gptoss_attn_rope_rows(P, P, None, 4, 8, 64, P, 16, None) == 1
+    assert lib.gptoss_attn_rope_rows(P, P, None, 4, 8, 64, P, 16, 0, None) == 1
     assert "positions is NULL" in lib.gptoss_attn_last_error().decode()
-    assert lib.gptoss_attn_rope_rows(P, P, P, 4, 8, 64, P, 0, None) == 1
-    assert lib.gptoss_attn_rope_rows(P, P, P, 4, 8, 32, P, 16, None) == 2
-    assert lib.gptoss_attn_rope_rows(None, None, None, 0, 8, 64, P, 16, None) == 0  # T = 0 is a no-op
+    assert lib.gptoss_attn_rope_rows(P, P, P, 4, 8, 64, P, 0, 0, None) == 1
+    assert lib.gptoss_attn_rope_rows(P, P, P, 4, 8, 32, P, 16, 0, None) == 2
+    assert lib.gptoss_attn_rope_rows(None, None, None, 0, 8, 64, P, 16, 1, None) == 0  # T = 0 is a no-op
     # forward: the table must cover S; k_rot is required and must not alias k
     fa = [P, P, P, P, P, 4096, 1, 4097, 64, 8, 64, 0, 0.125, P, P, P, None]
     assert lib.gptoss_attn_fwd_rope(*fa) == 1 and "rope table" in lib.gptoss_attn_last_error().decode()
@@ -318,3 +318,21 @@ def test_rope_rows_and_fused_entry_points_reject_bad_arguments(lib):
     da[5] = None
     da[6] = 1024
     assert lib.gptoss_attn_decode_rope(*da) == 1 and "table is NULL" in lib.gptoss_attn_last_error().decode()
+
+
+def test_bwd_rope_rejects_bad_arguments(lib):
+    need = lib.gptoss_attn_bwd_rope_workspace_size(1, 256, 8, 1, 64)
+    assert need >= 256 * 8 * 64 * 2
+    args = [P, P, P, P, P, 256, P, P, P, 1, 256, 8, 1, 64, 0, 0.125, P, P, P, P, P, need, None]
+    assert lib.gptoss_attn_bwd_rope(*args) != 1 or "workspace" not in lib.gptoss_attn_last_error().decode()
+    bad = list(args)
+    bad[5] = 255  # the table must cover S
+    assert lib.gptoss_attn_bwd_rope(*bad) == 1 and "rope table" in lib.gptoss_attn_last_error().decode()
+    bad = list(args)
+    bad[21] = need - 1
+    assert lib.gptoss_attn_bwd_rope(*bad) == 1 and "workspace" in lib.gptoss_attn_last_error().decode()
+    bad = list(args)
+    bad[4] = None
+    assert lib.gptoss_attn_bwd_rope(*bad) == 1 and "table is NULL" in lib.gptoss_attn_last_error().decode()
+    assert lib.gptoss_attn_bwd_rope(*([None] * 5), 1, *([None] * 3), 0, 4, 8, 1, 64, 0, 0.125,
+                                    *([None] * 5), 0, None) == 0

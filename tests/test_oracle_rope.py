@@ -15,6 +15,9 @@
   the exact rotation for a unit pair
 * attention with the identity table is attention without RoPE; decode with
   RoPE is the last row of prefill with RoPE
+* backward: the adjoint satisfies <R x, y> = <x, R^T y>; gradients with
+  respect to the unrotated q and k (and v, sinks) against central finite
+  differences of the fp64 loss through the rotation
 """
 
 import math
@@ -22,8 +25,8 @@ import math
 import numpy as np
 import pytest
 
-from oracle import (apply_rope_bf16, apply_rope_exact, brute_rope, ref_decode, ref_decode_rope, ref_fwd,
-                    ref_fwd_rope, rope_table, yarn_inv_freq, yarn_mscale)
+from oracle import (apply_rope_adjoint, apply_rope_bf16, apply_rope_exact, brute_rope, ref_bwd_rope, ref_decode,
+                    ref_decode_rope, ref_fwd, ref_fwd_rope, rope_table, yarn_inv_freq, yarn_mscale)
 
 GPTOSS_LIKE = dict(base=150000.0, factor=32.0, orig_ctx=4096, alpha=1.0, beta=32.0)
 
@@ -158,3 +161,54 @@ def test_decode_with_rope_is_last_prefill_row(window):
         o, l = ref_decode_rope(q[0, L - 1:L], kr[0], v[0], np.array([0, L]), sinks, window, 0.125, c32, s32)
         np.testing.assert_allclose(o[0], out[0, L - 1], rtol=1e-12, atol=1e-13)
         np.testing.assert_allclose(l[0], lse[0, :, L - 1], rtol=1e-12, atol=1e-13)
+
+
+def test_adjoint_identity():
+    rng = np.random.default_rng(20)
+    cos, sin = rope_table(30, 64, dtype=np.float64, **GPTOSS_LIKE)
+    pos = rng.integers(0, 30, 12)
+    x = rng.standard_normal((12, 3, 64))
+    y = rng.standard_normal((12, 3, 64))
+    a = np.sum(apply_rope_exact(x, pos, cos, sin) * y)
+    b = np.sum(x * apply_rope_adjoint(y, pos, cos, sin))
+    assert abs(a - b) <= 1e-12 * max(1.0, abs(a))
+
+
+@pytest.mark.parametrize("window", [0, 2])
+def test_bwd_rope_finite_differences(window):
+    rng = np.random.default_rng(21 + window)
+    B, S, Hq, Hkv, D = 1, 5, 2, 1, 8
+    params = dict(base=100.0, factor=4.0, orig_ctx=6, alpha=0.5, beta=3.0)
+    cos, sin = rope_table(S, D, dtype=np.float64, **params)
+    q = rng.standard_normal((B, S, Hq, D)) * 0.7
+    k = rng.standard_normal((B, S, Hkv, D)) * 0.7
+    v = rng.standard_normal((B, S, Hkv, D))
+    sinks = rng.standard_normal(Hq)
+    dout = rng.standard_normal((B, S, Hq, D))
+    scale = 0.4
+    pos = np.arange(S)
+
+    def loss(q_, k_, v_, s_):
+        qr = np.stack([apply_rope_exact(q_[b], pos, cos, sin) for b in range(B)])
+        kr = np.stack([apply_rope_exact(k_[b], pos, cos, sin) for b in range(B)])
+        out, _ = ref_fwd(qr, kr, v_, s_, window, scale)
+        return float(np.sum(out * dout))
+
+    grads = ref_bwd_rope(q, k, v, sinks, dout, window, scale, cos, sin, exact=True)
+    args = [q, k, v, sinks]
+    h = 1e-6
+    for idx, grad in enumerate(grads):
+        x = args[idx]
+        num = np.zeros_like(x)
+        it = np.nditer(x, flags=["multi_index"])
+        for _ in it:
+            mi = it.multi_index
+            old = x[mi]
+            x[mi] = old + h
+            lp = loss(*args)
+            x[mi] = old - h
+            lm = loss(*args)
+            x[mi] = old
+            num[mi] = (lp - lm) / (2 * h)
+        rel = np.linalg.norm(num - grad) / np.linalg.norm(grad)
+        assert rel <= 1e-6, (idx, rel)

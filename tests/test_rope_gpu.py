@@ -9,7 +9,7 @@ import torch
 
 import attention_attn_fwd_amd as attn
 from attention_attn_fwd_amd import synth
-from oracle import apply_rope_bf16, ref_decode_rope, ref_fwd_rope, rope_table
+from oracle import apply_rope_bf16, ref_bwd_rope, ref_decode_rope, ref_fwd_rope, rope_table
 
 from _util import check_out_lse, f64, need_gpu, seed_of
 
@@ -173,3 +173,83 @@ def test_prefill_cache_then_decode_rope_matches_prefill_row():
     torch.cuda.synchronize()
     assert (o.float() - out_full[0, L - 1].float()).abs().max().item() <= 1e-2
     assert (l[0] - lse_full[0, :, L - 1]).abs().max().item() <= 1e-4
+
+
+def _rel_errs(grads, ref, heads=None, kv_heads=None):
+    from _util import rel_l2
+    dq, dk, dv, ds = (f64(t) for t in grads)
+    rdq, rdk, rdv, rds = ref
+    if heads is not None:
+        dq, rdq, ds, rds = dq[:, :, heads], rdq[:, :, heads], ds[heads], rds[heads]
+        dk, rdk, dv, rdv = dk[:, :, kv_heads], rdk[:, :, kv_heads], dv[:, :, kv_heads], rdv[:, :, kv_heads]
+    return {n: rel_l2(a, r) for n, a, r in (("dq", dq, rdq), ("dk", dk, rdk), ("dv", dv, rdv), ("dsinks", ds, rds))}
+
+
+@pytest.mark.parametrize("shape", SMALL, ids=lambda s: "B%dS%dH%dx%d" % s)
+@pytest.mark.parametrize("window", [0, 128])
+def test_bwd_rope_small(shape, window):
+    """Gradients with respect to the unrotated q and k through the fused
+    rotation (q rotated in the backward's pre-pass, dq and dk carried back by
+    the adjoint rotation)."""
+    from _util import GRAD_REL_L2
+    dev = need_gpu()
+    B, S, Hq, Hkv = shape
+    case = synth.make_prefill(B, S, Hq, Hkv, seed=seed_of(shape, window, "bwd_rope"))
+    dout = synth.make_dout(tuple(case.q.shape), seed=seed_of("dout", shape, window))
+    print(f"bwd_rope shape={shape} W={window}", flush=True)
+    tab = attn.rope_table(max(S, 64), **GPTOSS_LIKE)
+    q, k, v, sk = (t.to(dev) for t in (case.q, case.k, case.v, case.sinks))
+    out, lse, k_rot = attn.fwd_rope(q, k, v, sk, tab, window, case.scale)
+    grads = attn.bwd_rope(q, k_rot, v, sk, tab, out, lse, dout.to(dev), window, case.scale)
+    torch.cuda.synchronize()
+    c, s = _oracle_table(max(S, 64), GPTOSS_LIKE)
+    ref = ref_bwd_rope(f64(case.q), f64(case.k), f64(case.v), f64(case.sinks), f64(dout), window, case.scale, c, s)
+    errs = _rel_errs(grads, ref)
+    print(errs, flush=True)
+    assert all(e <= GRAD_REL_L2 for e in errs.values()), errs
+
+
+@pytest.mark.parametrize("window", [128, 0])
+def test_bwd_rope_workload_group(window):
+    """The training shape (B=4, S=4096, 64q/8kv) with the YaRN table, in the
+    configuration bench.py times; every gradient of KV group 0 (query heads
+    0..7, all batches) against the oracle."""
+    from _util import GRAD_REL_L2
+    dev = need_gpu()
+    case, dout = synth.config_inputs("c3_bwd_b4_s4096_h64x8")
+    print(f"bwd_rope workload W={window}", flush=True)
+    S = case.q.shape[1]
+    tab = attn.rope_table(S, **GPTOSS_LIKE)
+    q, k, v, sk = (t.to(dev) for t in (case.q, case.k, case.v, case.sinks))
+    out, lse, k_rot = attn.fwd_rope(q, k, v, sk, tab, window, case.scale)
+    grads = attn.bwd_rope(q, k_rot, v, sk, tab, out, lse, dout.to(dev), window, case.scale)
+    torch.cuda.synchronize()
+    for t in grads:
+        assert torch.isfinite(t.float()).all()
+    c, s = _oracle_table(S, GPTOSS_LIKE)
+    heads = list(range(8))
+    ref = ref_bwd_rope(f64(case.q), f64(case.k), f64(case.v), f64(case.sinks), f64(dout), window, case.scale, c, s,
+                       heads=heads)
+    errs = _rel_errs(grads, ref, heads=heads, kv_heads=[0])
+    print(errs, flush=True)
+    assert all(e <= GRAD_REL_L2 for e in errs.values()), errs
+
+
+def test_autograd_rope_matches_entry_points():
+    """sink_attention_rope through torch autograd gives the fused forward's
+    output and the fused backward's gradients, bit for bit."""
+    from attention_attn_fwd_amd.autograd import sink_attention_rope
+    dev = need_gpu()
+    case = synth.make_prefill(2, 257, 16, 2, seed=51)
+    dout = synth.make_dout(tuple(case.q.shape), seed=52).to(dev)
+    tab = attn.rope_table(257, **GPTOSS_LIKE)
+    q, k, v, sk = (t.to(dev) for t in (case.q, case.k, case.v, case.sinks))
+    leaves = [t.detach().clone().requires_grad_(True) for t in (q, k, v, sk)]
+    out = sink_attention_rope(*leaves, tab, 128, case.scale)
+    out.backward(dout)
+    o2, l2, k_rot = attn.fwd_rope(q, k, v, sk, tab, 128, case.scale)
+    g2 = attn.bwd_rope(q, k_rot, v, sk, tab, o2, l2, dout, 128, case.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(out, o2)
+    for leaf, g in zip(leaves, g2):
+        assert torch.equal(leaf.grad, g)
