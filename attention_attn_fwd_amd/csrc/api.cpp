@@ -617,11 +617,8 @@ gptoss_status gptoss_attn_bwd_rope(const void* q, const void* k_rot, const void*
     const float2* tab = reinterpret_cast<const float2*>(table);
     uint16_t* q_rot = static_cast<uint16_t*>(workspace);
     void* bwd_ws = static_cast<char*>(workspace) + align256((size_t)B * S * Hq * D * 2);
-    hipError_t e = gptoss::launch_rope_rows(static_cast<const uint16_t*>(q), q_rot, nullptr, tab, table_positions,
-                                            (long long)B * S * Hq, Hq, S, false, s);
-    if (e != hipSuccess) return launched(e, "rope on q");
     gptoss::BwdArgs a;
-    a.q = q_rot;
+    a.q = static_cast<const uint16_t*>(q);
     a.k = static_cast<const uint16_t*>(k_rot);
     a.v = static_cast<const uint16_t*>(v);
     a.sinks = sinks;
@@ -634,6 +631,8 @@ gptoss_status gptoss_attn_bwd_rope(const void* q, const void* k_rot, const void*
     a.dsinks = dsinks;
     a.workspace = bwd_ws;
     a.cu = nullptr;
+    a.rope = tab;
+    a.q_rot = q_rot;
     a.B = B;
     a.S = S;
     a.T = B * S;
@@ -641,14 +640,7 @@ gptoss_status gptoss_attn_bwd_rope(const void* q, const void* k_rot, const void*
     a.Hkv = Hkv;
     a.window = window;
     a.scale = softmax_scale;
-    e = gptoss::launch_bwd(a, s);
-    if (e != hipSuccess) return launched(e, "backward with rope");
-    e = gptoss::launch_rope_rows(static_cast<const uint16_t*>(dq), static_cast<uint16_t*>(dq), nullptr, tab,
-                                 table_positions, (long long)B * S * Hq, Hq, S, true, s);
-    if (e != hipSuccess) return launched(e, "rope adjoint on dq");
-    e = gptoss::launch_rope_rows(static_cast<const uint16_t*>(dk), static_cast<uint16_t*>(dk), nullptr, tab,
-                                 table_positions, (long long)B * S * Hkv, Hkv, S, true, s);
-    return launched(e, "rope adjoint on dk");
+    return launched(gptoss::launch_bwd(a, s), "backward with rope");
 }
 
 }  // extern "C"

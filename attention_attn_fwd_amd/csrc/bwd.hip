@@ -59,6 +59,8 @@ struct BwdParams {
     float2* ld;      // [T][Hq] {lse * log2(e), Dvec} per token row and head
     float* dsterm;   // [Hq][T] exp(sink - lse) * sum_j P dP per row
     const int* cu;   // packed documents: sequence b = rows cu[b] .. cu[b+1]-1; nullptr = dense batch
+    const float2* rope;  // (cos, sin) [position][32]: q rotated by dq (into q_rot), dq/dk through R^T; or nullptr
+    uint16_t* q_rot;     // rotated q written by the dq kernel, read by dkdv (rope only)
     int B, S, Hq, Hkv, G, window;  // S = sequence length (dense) or the longest document (packed)
     int T;           // total token rows (B * S when dense)
     float scale;
@@ -192,7 +194,8 @@ bwd_dkdv_kernel(BwdParams p, int n_kt) {
     const int st_row = tid >> 3, st_unit = tid & 7;
     const bool g64 = (kColsPerStep % G) == 0;
     const size_t pos_stride = (size_t)Hq * kHeadDim;  // elements per position
-    const uint16_t* qcol_base = p.q + ((size_t)sr.row0 * Hq + (size_t)kvh * G) * kHeadDim + 8 * st_unit;
+    const uint16_t* qsrc = p.rope != nullptr ? p.q_rot : p.q;  // with RoPE: q as the dq kernel rotated it
+    const uint16_t* qcol_base = qsrc + ((size_t)sr.row0 * Hq + (size_t)kvh * G) * kHeadDim + 8 * st_unit;
     const uint16_t* ocol_base = p.dout + ((size_t)sr.row0 * Hq + (size_t)kvh * G) * kHeadDim + 8 * st_unit;
     const float2* ld_base = p.ld + (size_t)sr.row0 * Hq + (size_t)kvh * G;
     uint4 rq[2], ro[2];
@@ -343,22 +346,42 @@ bwd_dkdv_kernel(BwdParams p, int n_kt) {
         __syncthreads();
     }
 
-    // epilogue: lane = key, registers = d rows (acc_row); 4 contiguous d per store
+    // epilogue: lane = key, registers = d rows (acc_row); 4 contiguous d per
+    // store.  Element d of db = 0 and d + 32 of db = 1 sit in the same
+    // register index, so with RoPE the adjoint rotation of dk is in-lane.
     if (my_key < S) {
         const size_t off = ((size_t)sr.row0 + my_key) * kv_stride + (size_t)kvh * kHeadDim;
-#pragma unroll
-        for (int db = 0; db < 2; ++db)
+        float4 et[8];  // table entries of pairs 8 r4 + 4 g + 0..3, loaded before any store
+        if (p.rope != nullptr) {
+            const float4* t = reinterpret_cast<const float4*>(p.rope + (size_t)my_key * 32);
 #pragma unroll
             for (int r4 = 0; r4 < 4; ++r4) {
+                et[2 * r4] = t[4 * r4 + 2 * g];
+                et[2 * r4 + 1] = t[4 * r4 + 2 * g + 1];
+            }
+        }
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+            float ka[4], kb2[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                ka[j] = dkacc[0][4 * r4 + j] * p.scale;
+                kb2[j] = dkacc[1][4 * r4 + j] * p.scale;
+            }
+            if (p.rope != nullptr) rope4_adjoint_f32(ka, kb2, et[2 * r4], et[2 * r4 + 1]);
+#pragma unroll
+            for (int db = 0; db < 2; ++db) {
                 const int d0 = 32 * db + 8 * r4 + 4 * g;
+                const float* kx = db == 0 ? ka : kb2;
                 uint2 wk, wv;
-                wk.x = pack_bf16x2(dkacc[db][4 * r4 + 0] * p.scale, dkacc[db][4 * r4 + 1] * p.scale);
-                wk.y = pack_bf16x2(dkacc[db][4 * r4 + 2] * p.scale, dkacc[db][4 * r4 + 3] * p.scale);
+                wk.x = pack_bf16x2(kx[0], kx[1]);
+                wk.y = pack_bf16x2(kx[2], kx[3]);
                 wv.x = pack_bf16x2(dvacc[db][4 * r4 + 0], dvacc[db][4 * r4 + 1]);
                 wv.y = pack_bf16x2(dvacc[db][4 * r4 + 2], dvacc[db][4 * r4 + 3]);
                 *reinterpret_cast<uint2*>(p.dk + off + d0) = wk;
                 *reinterpret_cast<uint2*>(p.dv + off + d0) = wv;
             }
+        }
     }
 }
 
@@ -417,21 +440,45 @@ bwd_dq_kernel(BwdParams p, int n_qt, int pos_per_block) {
     // The row's Dvec = <dout, out> is formed here from the same dO fragments
     // (the two lane halves hold d = 16 ks + 8 g + 0..7), and {lse log2(e),
     // Dvec} is stored for the key-outer kernel, which runs after this one.
+    //
+    // With RoPE the q fragments ks and ks + 2 hold the pairs (d, d + 32) of
+    // this lane's d, so q is rotated in-lane and written to q_rot for dkdv
+    // (each column belongs to exactly one workgroup and lane pair).
     bf16x8 qf[4], of[4];
     float lse2 = INFINITY, dvec = 0.0f, dsum = 0.0f;
+    const bool rope = p.rope != nullptr;
     {
         const size_t row = ((size_t)sr.row0 + col_pos) * Hq + col_head;
         const size_t off = row * kHeadDim;
+        float4 rcs[2][4];
+        if (rope && col_ok) {
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) load_rope8(p.rope, col_pos, 16 * ks + 8 * g, rcs[ks]);
+        }
+        // every load is issued before the q_rot store (which the compiler
+        // must assume may alias them)
+        uint4 xq[4], yq[4], oq[4];
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            xq[ks] = yq[ks] = oq[ks] = make_uint4(0, 0, 0, 0);
+            if (col_ok) {
+                xq[ks] = ld16(p.q + off + 16 * ks + 8 * g);
+                yq[ks] = ld16(p.dout + off + 16 * ks + 8 * g);
+                oq[ks] = ld16(p.out + off + 16 * ks + 8 * g);
+            }
+        }
+        if (col_ok) lse2 = p.lse[sr.lse_base + col_head * sr.lse_hstride + col_pos] * kLog2e;
+        if (rope && col_ok) {
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) rope8(xq[ks], xq[ks + 2], rcs[ks]);
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) *reinterpret_cast<uint4*>(p.q_rot + off + 16 * ks + 8 * g) = xq[ks];
+        }
         float dot = 0.0f;
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
-            uint4 x = make_uint4(0, 0, 0, 0), y = make_uint4(0, 0, 0, 0), o = make_uint4(0, 0, 0, 0);
-            if (col_ok) {
-                x = ld16(p.q + off + 16 * ks + 8 * g);
-                y = ld16(p.dout + off + 16 * ks + 8 * g);
-                o = ld16(p.out + off + 16 * ks + 8 * g);
-            }
-            qf[ks] = as_bf16x8(x);
+            const uint4 y = yq[ks], o = oq[ks];
+            qf[ks] = as_bf16x8(xq[ks]);
             of[ks] = as_bf16x8(y);
             const uint32_t ow[4] = {o.x, o.y, o.z, o.w}, dw[4] = {y.x, y.y, y.z, y.w};
 #pragma unroll
@@ -441,10 +488,7 @@ bwd_dq_kernel(BwdParams p, int n_qt, int pos_per_block) {
             }
         }
         dvec = sum_across_halves(dot);
-        if (col_ok) {
-            lse2 = p.lse[sr.lse_base + col_head * sr.lse_hstride + col_pos] * kLog2e;
-            if (g == 0) p.ld[row] = make_float2(lse2, dvec);
-        }
+        if (col_ok && g == 0) p.ld[row] = make_float2(lse2, dvec);
     }
 
     f32x16 dqacc[2];
@@ -559,6 +603,17 @@ bwd_dq_kernel(BwdParams p, int n_qt, int pos_per_block) {
     }
 
     dsum = sum_across_halves(dsum);
+    // RoPE table entries of this lane's dq pairs d = 8 r4 + 4 g + 0..3, all
+    // loaded before the stores below
+    float4 et[8];
+    if (rope && col_ok) {
+        const float4* t = reinterpret_cast<const float4*>(p.rope + (size_t)col_pos * 32);
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+            et[2 * r4] = t[4 * r4 + 2 * g];
+            et[2 * r4 + 1] = t[4 * r4 + 2 * g + 1];
+        }
+    }
     if (col_ok) {
         if (g == 0) {
             // this row's dsink term exp(sink - lse) r with
@@ -569,17 +624,27 @@ bwd_dq_kernel(BwdParams p, int n_qt, int pos_per_block) {
             const float psink = fast_exp2(p.sinks[col_head] * kLog2e - lse2);
             p.dsterm[(size_t)col_head * p.T + sr.row0 + col_pos] = psink * fmaf(dvec, 1.0f - psink, dsum);
         }
+        // d and d + 32 share a register index (db = 0, 1): RoPE's adjoint
+        // is in-lane, applied to the fp32 values before the one rounding
         uint16_t* row = p.dq + (((size_t)sr.row0 + col_pos) * Hq + col_head) * kHeadDim;
 #pragma unroll
-        for (int db = 0; db < 2; ++db)
+        for (int r4 = 0; r4 < 4; ++r4) {
+            float qa[4], qb[4];
 #pragma unroll
-            for (int r4 = 0; r4 < 4; ++r4) {
-                const int d0 = 32 * db + 8 * r4 + 4 * g;
-                uint2 w;
-                w.x = pack_bf16x2(dqacc[db][4 * r4 + 0] * p.scale, dqacc[db][4 * r4 + 1] * p.scale);
-                w.y = pack_bf16x2(dqacc[db][4 * r4 + 2] * p.scale, dqacc[db][4 * r4 + 3] * p.scale);
-                *reinterpret_cast<uint2*>(row + d0) = w;
+            for (int j = 0; j < 4; ++j) {
+                qa[j] = dqacc[0][4 * r4 + j] * p.scale;
+                qb[j] = dqacc[1][4 * r4 + j] * p.scale;
             }
+            if (rope) rope4_adjoint_f32(qa, qb, et[2 * r4], et[2 * r4 + 1]);
+#pragma unroll
+            for (int db = 0; db < 2; ++db) {
+                const float* x = db == 0 ? qa : qb;
+                uint2 w;
+                w.x = pack_bf16x2(x[0], x[1]);
+                w.y = pack_bf16x2(x[2], x[3]);
+                *reinterpret_cast<uint2*>(row + 32 * db + 8 * r4 + 4 * g) = w;
+            }
+        }
     }
 }
 
@@ -611,6 +676,8 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
     p.ld = static_cast<float2*>(a.workspace);
     p.dsterm = reinterpret_cast<float*>(static_cast<char*>(a.workspace) + ld_region_bytes(a.T, a.Hq));
     p.cu = a.cu;
+    p.rope = a.rope;
+    p.q_rot = a.q_rot;
     p.B = a.B;
     p.S = a.S;
     p.T = a.T;

@@ -159,6 +159,22 @@ __device__ __forceinline__ void rope8(uint4& a, uint4& b, const float4 (&cs)[4],
     b = make_uint4(rb[0], rb[1], rb[2], rb[3]);
 }
 
+// The adjoint rotation R^T on fp32 values: a[j] holds element i + j and b[j]
+// its partner i + 32 + j (j = 0..3, i even), t0, t1 the (cos, sin) pairs of
+// i .. i+3.  Products and sums rounded once to fp32, as in rope8.
+__device__ __forceinline__ void rope4_adjoint_f32(float (&a)[4], float (&b)[4], const float4& t0,
+                                                  const float4& t1) {
+#pragma clang fp contract(off)
+    const float c[4] = {t0.x, t0.z, t1.x, t1.z}, s[4] = {t0.y, t0.w, t1.y, t1.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const float ya = a[j] * c[j] + b[j] * s[j];
+        const float yb = b[j] * c[j] - a[j] * s[j];
+        a[j] = ya;
+        b[j] = yb;
+    }
+}
+
 // The four (cos, sin) float4 of pairs i .. i+7 (i even) at `position` of a
 // table of 32 pairs per position.
 __device__ __forceinline__ void load_rope8(const float2* tab, int position, int i, float4 (&cs)[4]) {

@@ -36,6 +36,12 @@ struct BwdArgs {
     float* dsinks;
     void* workspace;
     const int* cu;  // as in FwdArgs
+    // RoPE (dense batches): q arrives unrotated and k rotated; the dq kernel
+    // rotates q with this (cos, sin) table [position][32] and writes it to
+    // q_rot (B*S*Hq*64 bf16) for dkdv, and dq, dk leave through the adjoint
+    // rotation.  nullptr = no rotation.
+    const float2* rope = nullptr;
+    uint16_t* q_rot = nullptr;
     int B, S, Hq, Hkv, window;
     int T;
     float scale;

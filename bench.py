@@ -22,7 +22,7 @@ step through the autograd wrapper, and prefill of packed documents (16384
 tokens in documents of U{1..4096} tokens, same heads; FLOPs over the pairs
 visible inside each document), and prefill and decode with the YaRN rotary
 embedding fused in (the same FLOPs; bytes add the rotated-key write; the
-backward adds the query pre-pass and the adjoint rotation of dq and dk), and
+backward counts the plain backward's bytes), and
 the forward of the small (B=1, S=512, 8q/1kv) and long-context (B=1,
 S=65536) workloads.
 """
@@ -382,8 +382,10 @@ def main():
                 "ms": round(ms, 4), "tflops": round(tf, 2), "gbs": round(gbs, 1), "bound": bound,
                 "frac_of_roof": round(tf / roof_tf if bound == "mfma" else gbs / HBM_PEAK_GBS, 4)}
     # backward with RoPE (training): out, lse and k_rot are those fwd_rope
-    # left in every buffer set above; q is rotated by a pre-pass into the
-    # workspace and dq, dk are carried back by the adjoint rotation in place
+    # left in every buffer set above; the dq kernel rotates q (and leaves it
+    # in the workspace for dkdv) and the dq, dk epilogues apply the adjoint
+    # rotation.  Algorithmic bytes as the plain backward (q_rot is not an
+    # output; its write is overhead the fraction shows)
     rws = torch.empty(attn.bwd_rope_workspace_size(B, S, Hq, Hkv, D), dtype=torch.uint8, device=dev)
 
     def bwd_rope(w, i=0):
@@ -397,10 +399,9 @@ def main():
         g.replay()
         ms = median_replay(g) / reps
         del g
-        extra = 2 * 2 * q.numel() + 2 * 2 * (q.numel() + k.numel())  # q pre-pass; adjoint on dq, dk
         tf = flops[("bwd", w)] / (ms * 1e-3) / 1e12
-        gbs = (bytes_[("bwd", w)] + extra) / (ms * 1e-3) / 1e9
-        roof_tf = min(BF16_PEAK_TFLOPS, flops[("bwd", w)] / (bytes_[("bwd", w)] + extra) * HBM_PEAK_GBS / 1e3)
+        gbs = bytes_[("bwd", w)] / (ms * 1e-3) / 1e9
+        roof_tf = min(BF16_PEAK_TFLOPS, flops[("bwd", w)] / bytes_[("bwd", w)] * HBM_PEAK_GBS / 1e3)
         parts[f"bwd_rope_{'full' if w == 0 else 'w%d' % w}"] = {
             "ms": round(ms, 4), "tflops": round(tf, 2), "gbs": round(gbs, 1),
             "bound": "mfma" if roof_tf >= BF16_PEAK_TFLOPS else "hbm", "frac_of_roof": round(tf / roof_tf, 4)}

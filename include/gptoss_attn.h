@@ -285,11 +285,12 @@ gptoss_status gptoss_attn_decode_rope(const void* q, const void* k_cache, const 
 /*
  * Training backward of gptoss_attn_fwd_rope for the loss sum(dout * out):
  * gradients with respect to the unrotated q and k.  Takes q (unrotated) and
- * k_rot (the forward's rotated keys); q is rotated into the workspace, the
- * backward of gptoss_attn_bwd runs on the rotated q and k, and dq, dk are
- * carried back through the adjoint rotation R^T (in place, after rounding to
- * bf16).  The rounding of the rotated q and k to bf16 is not differentiated
- * (its derivative is taken as 1).
+ * k_rot (the forward's rotated keys); the backward of gptoss_attn_bwd runs
+ * on the rotated q and k (the dq kernel rotates q, as gptoss_attn_fwd_rope
+ * does, and leaves it in the workspace for the dk/dv kernel), and dq, dk are
+ * carried back through the adjoint rotation R^T, applied to the fp32
+ * gradients before their one rounding to bf16.  The rounding of the rotated
+ * q and k to bf16 is not differentiated (its derivative is taken as 1).
  *   q, out, dout bf16 [B, S, Hq, D]; k_rot, v bf16 [B, S, Hkv, D];
  *   lse fp32 [B, Hq, S] as written by gptoss_attn_fwd_rope      read
  *   dq [B,S,Hq,D], dk, dv [B,S,Hkv,D] bf16; dsinks fp32 [Hq]    written
