@@ -63,6 +63,34 @@ def test_decode_empty_sequences():
     check_out_lse(o[[1, 3]], l[[1, 3]], ro[[1, 3]], rl[[1, 3]], "non-empty rows")
 
 
+@pytest.mark.parametrize("window", [0, 200])
+def test_decode_fewer_keys_than_workgroups(window):
+    """max_seqlen 4096 (the chunk plan cuts each sequence's visible range
+    into several chunks) with 6 keys in all: most chunks are empty, empty
+    sequences see only the sink."""
+    dev = need_gpu()
+    lengths = [0, 1, 2, 0, 3, 0]
+    case = synth.make_decode(len(lengths), 16, 2, lengths=lengths, seed=7 + window)
+    out, lse = _run(case, window, dev, max_seqlen=4096)
+    ro, rl = _oracle(case, window)
+    o, l = f64(out), f64(lse)
+    for n in (0, 3, 5):
+        assert (o[n] == 0).all()
+        np.testing.assert_array_equal(l[n], f64(case.sinks))
+    check_out_lse(o[[1, 2, 4]], l[[1, 2, 4]], ro[[1, 2, 4]], rl[[1, 2, 4]], f"sparse W={window}")
+
+
+@pytest.mark.parametrize("N", [512, 600])
+def test_decode_many_sequences(N):
+    """More sequences than CUs: one workgroup per (sequence, KV-head group),
+    several per CU."""
+    dev = need_gpu()
+    case = synth.make_decode(N, 8, 1, max_len=300, seed=17 + N)
+    out, lse = _run(case, 0, dev)
+    ro, rl = _oracle(case, 0)
+    check_out_lse(f64(out), f64(lse), ro, rl, f"N={N}")
+
+
 @pytest.mark.parametrize("window", [0, 128])
 def test_decode_multi_step(window):
     """Append one token per sequence and decode again, five times over; every
