@@ -431,6 +431,41 @@ bwd_dq_kernel(BwdParams p, int n_qt, int pos_per_block) {
     const int wpmin = p0 + wc0 / G;
     const int wpmax = min(p0 + min(wc0 + 31, used_cols - 1) / G, S - 1);
 
+    // K/V tiles of 64 keys, staged through LDS; the first tile's loads are
+    // issued ahead of the row prologue below so the two round trips overlap
+    const int key_lo = W > 0 ? max(0, p0 - W + 1) : 0;
+    const int t_begin = key_lo / kBk;
+    const int t_end = P1 / kBk;
+
+    const size_t kv_stride = (size_t)p.Hkv * kHeadDim;
+    const uint16_t* kbase = p.k + ((size_t)sr.row0 * p.Hkv + kvh) * kHeadDim;
+    const uint16_t* vbase = p.v + ((size_t)sr.row0 * p.Hkv + kvh) * kHeadDim;
+    const int st_row = tid >> 3, st_unit = tid & 7;
+    uint4 rk[2], rv[2];
+    auto load_tile = [&](int t) {
+        const int kt0 = t * kBk;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int key = kt0 + st_row + 32 * j;
+            rk[j] = make_uint4(0, 0, 0, 0);
+            rv[j] = make_uint4(0, 0, 0, 0);
+            if (key < S) {
+                rk[j] = ld16(kbase + row_off(key, (uint32_t)kv_stride) + 8 * st_unit);
+                rv[j] = ld16(vbase + row_off(key, (uint32_t)kv_stride) + 8 * st_unit);
+            }
+        }
+    };
+    auto store_tile = [&](int buf) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int row = st_row + 32 * j;
+            sK[buf][tile_unit(row, st_unit)] = rk[j];
+            sV[buf][tile_unit(row, st_unit)] = rv[j];
+        }
+    };
+
+    if (t_begin <= t_end) load_tile(t_begin);
+
     // This column's q and dO rows as B operands (d = 16 ks + 8 g + 0..7).
     // The dP accumulator starts at -Dvec, so the MFMAs deliver dP - Dvec and
     // dS = P acc.  (q is not pre-scaled by c here: P must sum, with the
@@ -497,41 +532,7 @@ bwd_dq_kernel(BwdParams p, int n_qt, int pos_per_block) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) dqacc[db][r] = 0.0f;
 
-    const int key_lo = W > 0 ? max(0, p0 - W + 1) : 0;
-    const int t_begin = key_lo / kBk;
-    const int t_end = P1 / kBk;
-
-    const size_t kv_stride = (size_t)p.Hkv * kHeadDim;
-    const uint16_t* kbase = p.k + ((size_t)sr.row0 * p.Hkv + kvh) * kHeadDim;
-    const uint16_t* vbase = p.v + ((size_t)sr.row0 * p.Hkv + kvh) * kHeadDim;
-    const int st_row = tid >> 3, st_unit = tid & 7;
-    uint4 rk[2], rv[2];
-    auto load_tile = [&](int t) {
-        const int kt0 = t * kBk;
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int key = kt0 + st_row + 32 * j;
-            rk[j] = make_uint4(0, 0, 0, 0);
-            rv[j] = make_uint4(0, 0, 0, 0);
-            if (key < S) {
-                rk[j] = ld16(kbase + row_off(key, (uint32_t)kv_stride) + 8 * st_unit);
-                rv[j] = ld16(vbase + row_off(key, (uint32_t)kv_stride) + 8 * st_unit);
-            }
-        }
-    };
-    auto store_tile = [&](int buf) {
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int row = st_row + 32 * j;
-            sK[buf][tile_unit(row, st_unit)] = rk[j];
-            sV[buf][tile_unit(row, st_unit)] = rv[j];
-        }
-    };
-
-    if (t_begin <= t_end) {
-        load_tile(t_begin);
-        store_tile(0);
-    }
+    if (t_begin <= t_end) store_tile(0);
     __syncthreads();
 
     for (int t = t_begin; t <= t_end; ++t) {

@@ -125,6 +125,9 @@ decode_split_kernel(DecParams p) {
     const uint16_t* vb = p.vc + ((size_t)base * p.Hkv + kvh) * kHeadDim;
     const int* bt_row = kPaged ? p.bt + (size_t)n * p.pps : nullptr;
 
+    // the sink is only needed when a single-chunk sequence is finished, but
+    // is loaded here so that its latency hides behind the tiles
+    const float sink = col_ok ? p.sinks[head] : 0.0f;
     uint4 qraw[4];
     {
         const uint16_t* qrow = p.q + ((size_t)n * p.Hq + head) * kHeadDim;
@@ -265,7 +268,6 @@ decode_split_kernel(DecParams p) {
     if (!col_ok) return;
     if (n_act == 1) {
         // finish in place: fold in the sink
-        const float sink = p.sinks[head];
         const float s2 = sink * kLog2e;
         const float mf = fmaxf(s2, m_run);
         const float a = fast_exp2(m_run - mf);
