@@ -46,6 +46,47 @@ def _need(t, name, dtype, ndim):
         raise ValueError(f"{name} must be contiguous")
 
 
+def _on(dev, *named):
+    """Every (tensor, name) pair lives on device `dev`."""
+    for t, name in named:
+        if t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, expected {dev} (all tensors of a call on one device)")
+
+
+def _buffer(t, name, dtype, shape, dev):
+    """A caller-provided output buffer: exact dtype, shape, contiguity and
+    device (the kernels write exactly that many elements)."""
+    _need(t, name, dtype, len(shape))
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    _on(dev, (t, name))
+    return t
+
+
+def _workspace(ws, need, dev):
+    """The caller's workspace (any dtype, contiguous, on `dev`) or a new one;
+    returns (tensor, size in bytes).  The library checks the size."""
+    if ws is None:
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    if not isinstance(ws, torch.Tensor) or not ws.is_contiguous():
+        raise ValueError("workspace must be a contiguous torch.Tensor")
+    _on(dev, (ws, "workspace"))
+    return ws, ws.numel() * ws.element_size()
+
+
+def _grads(grads, q, k, v, Hq):
+    """Gradient buffers: new ones, or the caller's (dq, dk, dv, dsinks) checked
+    against q, k, v and Hq."""
+    if grads is None:
+        return (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v),
+                torch.empty((Hq,), dtype=torch.float32, device=q.device))
+    dq, dk, dv, dsinks = grads
+    for t, n, ref in ((dq, "dq", q), (dk, "dk", k), (dv, "dv", v)):
+        _buffer(t, n, torch.bfloat16, ref.shape, q.device)
+    _buffer(dsinks, "dsinks", torch.float32, (Hq,), q.device)
+    return dq, dk, dv, dsinks
+
+
 def _stream(dev):
     return torch.cuda.current_stream(dev).cuda_stream
 
@@ -67,13 +108,11 @@ def fwd(q, k, v, sinks, window=0, scale=None, out=None, lse=None):
     Hkv = k.shape[2]
     if k.shape != (B, S, Hkv, D) or v.shape != k.shape or sinks.shape != (Hq,):
         raise ValueError("shape mismatch among q, k, v, sinks")
+    _on(q.device, (k, "k"), (v, "v"), (sinks, "sinks"))
     scale = (1.0 / D ** 0.5) if scale is None else float(scale)
-    if out is None:
-        out = torch.empty_like(q)
-    if lse is None:
-        lse = torch.empty((B, Hq, S), dtype=torch.float32, device=q.device)
-    _need(out, "out", torch.bfloat16, 4)
-    _need(lse, "lse", torch.float32, 3)
+    out = torch.empty_like(q) if out is None else _buffer(out, "out", torch.bfloat16, q.shape, q.device)
+    lse = (torch.empty((B, Hq, S), dtype=torch.float32, device=q.device) if lse is None
+           else _buffer(lse, "lse", torch.float32, (B, Hq, S), q.device))
     lib = _lib.load()
     st = lib.gptoss_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), sinks.data_ptr(), B, S, Hq, Hkv, D,
                              int(window), scale, out.data_ptr(), lse.data_ptr(), _stream(q.device))
@@ -97,29 +136,25 @@ def bwd(q, k, v, sinks, out, lse, dout, window=0, scale=None, workspace=None, gr
     if (k.shape != (B, S, Hkv, D) or v.shape != k.shape or out.shape != q.shape or dout.shape != q.shape
             or lse.shape != (B, Hq, S) or sinks.shape != (Hq,)):
         raise ValueError("shape mismatch among backward inputs")
+    _on(q.device, (k, "k"), (v, "v"), (sinks, "sinks"), (out, "out"), (lse, "lse"), (dout, "dout"))
     scale = (1.0 / D ** 0.5) if scale is None else float(scale)
-    if grads is None:
-        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-        dsinks = torch.empty((Hq,), dtype=torch.float32, device=q.device)
-    else:
-        dq, dk, dv, dsinks = grads
-        for t, n, ref in ((dq, "dq", q), (dk, "dk", k), (dv, "dv", v)):
-            _need(t, n, torch.bfloat16, 4)
-            if t.shape != ref.shape:
-                raise ValueError(f"{n} must have shape {tuple(ref.shape)}")
-        _need(dsinks, "dsinks", torch.float32, 1)
-        if dsinks.shape != (Hq,):
-            raise ValueError(f"dsinks must have shape ({Hq},)")
-    need = bwd_workspace_size(B, S, Hq, Hkv, D, window)
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    dq, dk, dv, dsinks = _grads(grads, q, k, v, Hq)
+    workspace, ws_bytes = _workspace(workspace, bwd_workspace_size(B, S, Hq, Hkv, D, window), q.device)
     lib = _lib.load()
     st = lib.gptoss_attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), sinks.data_ptr(), out.data_ptr(),
                              lse.data_ptr(), dout.data_ptr(), B, S, Hq, Hkv, D, int(window), scale,
                              dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), dsinks.data_ptr(),
-                             workspace.data_ptr(), workspace.numel(), _stream(q.device))
+                             workspace.data_ptr(), ws_bytes, _stream(q.device))
     _lib.check(st, lib)
     return dq, dk, dv, dsinks
+
+
+def _decode_outputs(out, lse, q):
+    N, Hq, _ = q.shape
+    out = torch.empty_like(q) if out is None else _buffer(out, "out", torch.bfloat16, q.shape, q.device)
+    lse = (torch.empty((N, Hq), dtype=torch.float32, device=q.device) if lse is None
+           else _buffer(lse, "lse", torch.float32, (N, Hq), q.device))
+    return out, lse
 
 
 def decode_workspace_size(N, Hq, Hkv, D=64, max_seqlen=1, window=0):
@@ -140,18 +175,14 @@ def decode(q, k_cache, v_cache, cu_seqlens, sinks, max_seqlen, window=0, scale=N
     if (v_cache.shape != k_cache.shape or k_cache.shape[2] != D or cu_seqlens.shape != (N + 1,)
             or sinks.shape != (Hq,)):
         raise ValueError("shape mismatch among decode inputs")
+    _on(q.device, (k_cache, "k_cache"), (v_cache, "v_cache"), (cu_seqlens, "cu_seqlens"), (sinks, "sinks"))
     scale = (1.0 / D ** 0.5) if scale is None else float(scale)
-    if out is None:
-        out = torch.empty_like(q)
-    if lse is None:
-        lse = torch.empty((N, Hq), dtype=torch.float32, device=q.device)
-    need = decode_workspace_size(N, Hq, Hkv, D, max_seqlen, window)
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    out, lse = _decode_outputs(out, lse, q)
+    workspace, ws_bytes = _workspace(workspace, decode_workspace_size(N, Hq, Hkv, D, max_seqlen, window), q.device)
     lib = _lib.load()
     st = lib.gptoss_attn_decode(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), cu_seqlens.data_ptr(),
                                 sinks.data_ptr(), N, Hq, Hkv, D, int(max_seqlen), int(window), scale,
-                                out.data_ptr(), lse.data_ptr(), workspace.data_ptr(), workspace.numel(),
+                                out.data_ptr(), lse.data_ptr(), workspace.data_ptr(), ws_bytes,
                                 _stream(q.device))
     _lib.check(st, lib)
     return out, lse
@@ -173,19 +204,16 @@ def decode_paged(q, k_pages, v_pages, block_table, seq_lens, sinks, max_seqlen, 
     if (v_pages.shape != k_pages.shape or Dk != D or block_table.shape[0] != N or seq_lens.shape != (N,)
             or sinks.shape != (Hq,)):
         raise ValueError("shape mismatch among paged decode inputs")
+    _on(q.device, (k_pages, "k_pages"), (v_pages, "v_pages"), (block_table, "block_table"), (seq_lens, "seq_lens"),
+        (sinks, "sinks"))
     scale = (1.0 / D ** 0.5) if scale is None else float(scale)
-    if out is None:
-        out = torch.empty_like(q)
-    if lse is None:
-        lse = torch.empty((N, Hq), dtype=torch.float32, device=q.device)
-    need = decode_workspace_size(N, Hq, Hkv, D, max_seqlen, window)
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    out, lse = _decode_outputs(out, lse, q)
+    workspace, ws_bytes = _workspace(workspace, decode_workspace_size(N, Hq, Hkv, D, max_seqlen, window), q.device)
     lib = _lib.load()
     st = lib.gptoss_attn_decode_paged(q.data_ptr(), k_pages.data_ptr(), v_pages.data_ptr(), block_table.data_ptr(),
                                       seq_lens.data_ptr(), sinks.data_ptr(), N, Hq, Hkv, D, page_size,
                                       block_table.shape[1], int(ring_tokens), int(max_seqlen), int(window), scale,
-                                      out.data_ptr(), lse.data_ptr(), workspace.data_ptr(), workspace.numel(),
+                                      out.data_ptr(), lse.data_ptr(), workspace.data_ptr(), ws_bytes,
                                       _stream(q.device))
     _lib.check(st, lib)
     return out, lse
@@ -210,15 +238,11 @@ def fwd_varlen(q, k, v, cu_seqlens, sinks, max_seqlen, window=0, scale=None, out
     N = cu_seqlens.shape[0] - 1
     if N < 0 or k.shape != (T, Hkv, D) or v.shape != k.shape or sinks.shape != (Hq,):
         raise ValueError("shape mismatch among q, k, v, cu_seqlens, sinks")
+    _on(q.device, (k, "k"), (v, "v"), (cu_seqlens, "cu_seqlens"), (sinks, "sinks"))
     scale = (1.0 / D ** 0.5) if scale is None else float(scale)
-    if out is None:
-        out = torch.empty_like(q)
-    if lse is None:
-        lse = torch.empty((Hq, T), dtype=torch.float32, device=q.device)
-    _need(out, "out", torch.bfloat16, 3)
-    _need(lse, "lse", torch.float32, 2)
-    if out.shape != q.shape or lse.shape != (Hq, T):
-        raise ValueError("out must be [T,Hq,D] and lse [Hq,T]")
+    out = torch.empty_like(q) if out is None else _buffer(out, "out", torch.bfloat16, q.shape, q.device)
+    lse = (torch.empty((Hq, T), dtype=torch.float32, device=q.device) if lse is None
+           else _buffer(lse, "lse", torch.float32, (Hq, T), q.device))
     lib = _lib.load()
     st = lib.gptoss_attn_fwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), cu_seqlens.data_ptr(),
                                     sinks.data_ptr(), N, T, Hq, Hkv, D, int(max_seqlen), int(window), scale,
@@ -247,27 +271,16 @@ def bwd_varlen(q, k, v, cu_seqlens, sinks, out, lse, dout, max_seqlen, window=0,
     if (N < 0 or k.shape != (T, Hkv, D) or v.shape != k.shape or out.shape != q.shape or dout.shape != q.shape
             or lse.shape != (Hq, T) or sinks.shape != (Hq,)):
         raise ValueError("shape mismatch among varlen backward inputs")
+    _on(q.device, (k, "k"), (v, "v"), (cu_seqlens, "cu_seqlens"), (sinks, "sinks"), (out, "out"), (lse, "lse"),
+        (dout, "dout"))
     scale = (1.0 / D ** 0.5) if scale is None else float(scale)
-    if grads is None:
-        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-        dsinks = torch.empty((Hq,), dtype=torch.float32, device=q.device)
-    else:
-        dq, dk, dv, dsinks = grads
-        for t, n, ref in ((dq, "dq", q), (dk, "dk", k), (dv, "dv", v)):
-            _need(t, n, torch.bfloat16, 3)
-            if t.shape != ref.shape:
-                raise ValueError(f"{n} must have shape {tuple(ref.shape)}")
-        _need(dsinks, "dsinks", torch.float32, 1)
-        if dsinks.shape != (Hq,):
-            raise ValueError(f"dsinks must have shape ({Hq},)")
-    need = bwd_varlen_workspace_size(T, Hq, Hkv, D)
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    dq, dk, dv, dsinks = _grads(grads, q, k, v, Hq)
+    workspace, ws_bytes = _workspace(workspace, bwd_varlen_workspace_size(T, Hq, Hkv, D), q.device)
     lib = _lib.load()
     st = lib.gptoss_attn_bwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), cu_seqlens.data_ptr(),
                                     sinks.data_ptr(), out.data_ptr(), lse.data_ptr(), dout.data_ptr(), N, T, Hq,
                                     Hkv, D, int(max_seqlen), int(window), scale, dq.data_ptr(), dk.data_ptr(),
-                                    dv.data_ptr(), dsinks.data_ptr(), workspace.data_ptr(), workspace.numel(),
+                                    dv.data_ptr(), dsinks.data_ptr(), workspace.data_ptr(), ws_bytes,
                                     _stream(q.device))
     _lib.check(st, lib)
     return dq, dk, dv, dsinks
@@ -276,9 +289,8 @@ def bwd_varlen(q, k, v, cu_seqlens, sinks, out, lse, dout, max_seqlen, window=0,
 def rope_table(positions, base, factor=1.0, orig_ctx=1.0, alpha=1.0, beta=32.0, device=None, out=None):
     """YaRN rotary table fp32 [positions, 32, 2] = (m cos(p h_i), m sin(p h_i))."""
     dev = device if device is not None else torch.device("cuda", torch.cuda.current_device())
-    if out is None:
-        out = torch.empty((int(positions), 32, 2), dtype=torch.float32, device=dev)
-    _need(out, "table", torch.float32, 3)
+    out = (torch.empty((int(positions), 32, 2), dtype=torch.float32, device=dev) if out is None
+           else _buffer(out, "table", torch.float32, (int(positions), 32, 2), out.device))
     lib = _lib.load()
     st = lib.gptoss_attn_rope_table(out.data_ptr(), int(positions), 64, float(base), float(factor),
                                     float(orig_ctx), float(alpha), float(beta), _stream(out.device))
@@ -301,9 +313,8 @@ def rope_rows(x, positions, table, out=None, transpose=False):
     T, H, D = x.shape
     if positions.shape != (T,):
         raise ValueError("positions must be [T]")
-    if out is None:
-        out = torch.empty_like(x)
-    _need(out, "out", torch.bfloat16, 3)
+    _on(x.device, (positions, "positions"), (table, "table"))
+    out = torch.empty_like(x) if out is None else _buffer(out, "out", torch.bfloat16, x.shape, x.device)
     lib = _lib.load()
     st = lib.gptoss_attn_rope_rows(x.data_ptr(), out.data_ptr(), positions.data_ptr(), T, H, D, table.data_ptr(),
                                    table.shape[0], 1 if transpose else 0, _stream(x.device))
@@ -323,13 +334,12 @@ def fwd_rope(q, k, v, sinks, table, window=0, scale=None, out=None, lse=None, k_
     Hkv = k.shape[2]
     if k.shape != (B, S, Hkv, D) or v.shape != k.shape or sinks.shape != (Hq,):
         raise ValueError("shape mismatch among q, k, v, sinks")
+    _on(q.device, (k, "k"), (v, "v"), (sinks, "sinks"), (table, "table"))
     scale = (1.0 / D ** 0.5) if scale is None else float(scale)
-    out = torch.empty_like(q) if out is None else out
-    lse = torch.empty((B, Hq, S), dtype=torch.float32, device=q.device) if lse is None else lse
-    k_rot = torch.empty_like(k) if k_rot is None else k_rot
-    _need(out, "out", torch.bfloat16, 4)
-    _need(lse, "lse", torch.float32, 3)
-    _need(k_rot, "k_rot", torch.bfloat16, 4)
+    out = torch.empty_like(q) if out is None else _buffer(out, "out", torch.bfloat16, q.shape, q.device)
+    lse = (torch.empty((B, Hq, S), dtype=torch.float32, device=q.device) if lse is None
+           else _buffer(lse, "lse", torch.float32, (B, Hq, S), q.device))
+    k_rot = torch.empty_like(k) if k_rot is None else _buffer(k_rot, "k_rot", torch.bfloat16, k.shape, q.device)
     lib = _lib.load()
     st = lib.gptoss_attn_fwd_rope(q.data_ptr(), k.data_ptr(), v.data_ptr(), sinks.data_ptr(), table.data_ptr(),
                                   table.shape[0], B, S, Hq, Hkv, D, int(window), scale, out.data_ptr(),
@@ -352,17 +362,16 @@ def decode_rope(q, k_cache, v_cache, cu_seqlens, sinks, table, max_seqlen, windo
     if (v_cache.shape != k_cache.shape or k_cache.shape[2] != D or cu_seqlens.shape != (N + 1,)
             or sinks.shape != (Hq,)):
         raise ValueError("shape mismatch among decode inputs")
+    _on(q.device, (k_cache, "k_cache"), (v_cache, "v_cache"), (cu_seqlens, "cu_seqlens"), (sinks, "sinks"),
+        (table, "table"))
     scale = (1.0 / D ** 0.5) if scale is None else float(scale)
-    out = torch.empty_like(q) if out is None else out
-    lse = torch.empty((N, Hq), dtype=torch.float32, device=q.device) if lse is None else lse
-    need = decode_workspace_size(N, Hq, Hkv, D, max_seqlen, window)
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    out, lse = _decode_outputs(out, lse, q)
+    workspace, ws_bytes = _workspace(workspace, decode_workspace_size(N, Hq, Hkv, D, max_seqlen, window), q.device)
     lib = _lib.load()
     st = lib.gptoss_attn_decode_rope(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), cu_seqlens.data_ptr(),
                                      sinks.data_ptr(), table.data_ptr(), table.shape[0], N, Hq, Hkv, D,
                                      int(max_seqlen), int(window), scale, out.data_ptr(), lse.data_ptr(),
-                                     workspace.data_ptr(), workspace.numel(), _stream(q.device))
+                                     workspace.data_ptr(), ws_bytes, _stream(q.device))
     _lib.check(st, lib)
     return out, lse
 
@@ -385,19 +394,15 @@ def bwd_rope(q, k_rot, v, sinks, table, out, lse, dout, window=0, scale=None, wo
     if (k_rot.shape != (B, S, Hkv, D) or v.shape != k_rot.shape or out.shape != q.shape or dout.shape != q.shape
             or lse.shape != (B, Hq, S) or sinks.shape != (Hq,)):
         raise ValueError("shape mismatch among backward inputs")
+    _on(q.device, (k_rot, "k_rot"), (v, "v"), (sinks, "sinks"), (table, "table"), (out, "out"), (lse, "lse"),
+        (dout, "dout"))
     scale = (1.0 / D ** 0.5) if scale is None else float(scale)
-    if grads is None:
-        dq, dk, dv = torch.empty_like(q), torch.empty_like(k_rot), torch.empty_like(v)
-        dsinks = torch.empty((Hq,), dtype=torch.float32, device=q.device)
-    else:
-        dq, dk, dv, dsinks = grads
-    need = bwd_rope_workspace_size(B, S, Hq, Hkv, D)
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    dq, dk, dv, dsinks = _grads(grads, q, k_rot, v, Hq)
+    workspace, ws_bytes = _workspace(workspace, bwd_rope_workspace_size(B, S, Hq, Hkv, D), q.device)
     lib = _lib.load()
     st = lib.gptoss_attn_bwd_rope(q.data_ptr(), k_rot.data_ptr(), v.data_ptr(), sinks.data_ptr(), table.data_ptr(),
                                   table.shape[0], out.data_ptr(), lse.data_ptr(), dout.data_ptr(), B, S, Hq, Hkv, D,
                                   int(window), scale, dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), dsinks.data_ptr(),
-                                  workspace.data_ptr(), workspace.numel(), _stream(q.device))
+                                  workspace.data_ptr(), ws_bytes, _stream(q.device))
     _lib.check(st, lib)
     return dq, dk, dv, dsinks
