@@ -201,8 +201,11 @@ __device__ __forceinline__ SeqRows seq_rows(const int* cu, int S, int H, int tot
         r.lse_base = (size_t)b * H * S;
         r.lse_hstride = (size_t)S;
     } else {
-        r.row0 = cu[b];
-        r.len = min(cu[b + 1] - r.row0, S);
+        // clamped to [0, total_rows] so that offsets that break the contract
+        // (negative, decreasing or past the end) cannot reach outside the
+        // tensors; valid offsets pass unchanged
+        r.row0 = min(max(cu[b], 0), total_rows);
+        r.len = min(min(max(cu[b + 1], r.row0), total_rows) - r.row0, S);
         r.lse_base = (size_t)r.row0;
         r.lse_hstride = (size_t)total_rows;
     }

@@ -184,7 +184,10 @@ gptoss_status gptoss_attn_decode_paged(const void* q, const void* k_pages, const
  *   k, v            bf16 [T, Hkv, D]     read
  *   cu_seqlens      int32 [N + 1], device, non-decreasing, 0 <= cu[0],
  *                   cu[N] <= T.  Rows outside every document are neither
- *                   read as keys nor written.
+ *                   read as keys nor written.  The kernels clamp the
+ *                   offsets into [0, T], so offsets that break this contract
+ *                   give unspecified results but no access outside the
+ *                   tensors.
  *   max_seqlen      host-side upper bound of every document length (>= 1); it
  *                   sizes the grid without reading device memory.  A longer
  *                   document is a caller error: only its first max_seqlen rows
