@@ -65,6 +65,21 @@ def test_bwd_small_shapes(shape, window):
     _check(grads, _oracle(case, dout, window), f"{shape} W={window}")
 
 
+@pytest.mark.parametrize("heads", [(16, 1), (32, 1), (64, 1), (128, 1), (12, 1), (80, 2)], ids=lambda h: "H%dx%d" % h)
+@pytest.mark.parametrize("window", [0, 128])
+def test_bwd_large_groups(heads, window):
+    """Group sizes up to the supported 128 (the key-outer kernel's 64-column
+    steps hold 64 / G positions when G divides 64, else a column walk by
+    division; the query-outer kernel's 128 columns hold 128 / G positions)."""
+    dev = need_gpu()
+    Hq, Hkv = heads
+    case = synth.make_prefill(1, 190, Hq, Hkv, seed=seed_of(heads, window, "bwdG"))
+    dout = synth.make_dout(tuple(case.q.shape), seed=seed_of(heads, window, "doutG"))
+    print(f"bwd heads={heads} window={window}", flush=True)
+    grads = _run(case, dout, window, dev)
+    _check(grads, _oracle(case, dout, window), f"heads={heads} W={window}")
+
+
 @pytest.mark.parametrize("sink", [-np.inf, 5.0])
 @pytest.mark.parametrize("window", [0, 128])
 def test_bwd_extreme_sinks(sink, window):

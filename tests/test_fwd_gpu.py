@@ -42,6 +42,24 @@ def test_fwd_small_shapes(shape, window):
     check_out_lse(f64(out), f64(lse), ro, rl, f"{shape} W={window}")
 
 
+# group sizes G = Hq / Hkv up to the supported 128: a workgroup's 256
+# columns hold 256 / G positions (16 .. 2), and G = 12 and 40 divide neither
+# 256 nor the backward's 64-column steps
+LARGE_GROUPS = [(16, 1), (32, 1), (64, 1), (128, 1), (12, 1), (80, 2)]
+
+
+@pytest.mark.parametrize("heads", LARGE_GROUPS, ids=lambda h: "H%dx%d" % h)
+@pytest.mark.parametrize("window", [0, 128])
+def test_fwd_large_groups(heads, window):
+    dev = need_gpu()
+    Hq, Hkv = heads
+    case = synth.make_prefill(1, 190, Hq, Hkv, seed=seed_of(heads, window, "fwdG"))
+    print(f"fwd heads={heads} window={window}", flush=True)
+    out, lse = _run(case, window, dev)
+    ro, rl = _oracle(case, window)
+    check_out_lse(f64(out), f64(lse), ro, rl, f"heads={heads} W={window}")
+
+
 @pytest.mark.parametrize("sink", [-np.inf, 20.0, -20.0])
 @pytest.mark.parametrize("window", [0, 128])
 def test_fwd_extreme_sinks(sink, window):
