@@ -39,7 +39,7 @@ EDGE_LENGTHS = [1, 2, 63, 64, 65, 127, 128, 129, 255, 256, 257, 511, 512, 513, 1
 
 
 @pytest.mark.parametrize("window", [0, 1, 127, 128, 129])
-@pytest.mark.parametrize("heads", [(64, 8), (8, 1), (8, 8), (6, 2), (40, 1)])
+@pytest.mark.parametrize("heads", [(64, 8), (8, 1), (8, 8), (6, 2), (40, 1), (128, 1), (64, 2), (16, 1)])
 def test_decode_edge_lengths(window, heads):
     dev = need_gpu()
     Hq, Hkv = heads

@@ -30,7 +30,7 @@ def _oracle(case, window):
 
 @pytest.mark.parametrize("page_size", [1, 16, 64, 256])
 @pytest.mark.parametrize("window", [0, 128])
-@pytest.mark.parametrize("heads", [(64, 8), (8, 1)])
+@pytest.mark.parametrize("heads", [(64, 8), (8, 1), (128, 2)])
 def test_paged_linear(page_size, window, heads):
     dev = need_gpu()
     case = synth.make_paged_decode(len(EDGE_LENGTHS), *heads, page_size, lengths=EDGE_LENGTHS,

@@ -73,7 +73,7 @@ LAYOUTS = [  # document lengths, rows before, rows after
     ([700, 1, 1, 450], 0, 7),
     ([0, 0, 17], 40, 0),
 ]
-HEADS = [(8, 1), (16, 2), (6, 2), (1, 1)]
+HEADS = [(8, 1), (16, 2), (6, 2), (1, 1), (64, 1)]
 
 
 @pytest.mark.parametrize("layout", LAYOUTS, ids=lambda l: "L%d-%d-%d" % (len(l[0]), l[1], l[2]))
