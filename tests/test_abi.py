@@ -336,3 +336,11 @@ def test_bwd_rope_rejects_bad_arguments(lib):
     assert lib.gptoss_attn_bwd_rope(*bad) == 1 and "table is NULL" in lib.gptoss_attn_last_error().decode()
     assert lib.gptoss_attn_bwd_rope(*([None] * 5), 1, *([None] * 3), 0, 4, 8, 1, 64, 0, 0.125,
                                     *([None] * 5), 0, None) == 0
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    """No fallback: a library that is not built is an error, not a silent
+    path through something else."""
+    from attention_attn_fwd_amd import _lib
+    with pytest.raises(RuntimeError, match="is not built"):
+        _lib.load(str(tmp_path / "libgptoss_attn.so"))
