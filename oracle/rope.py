@@ -21,17 +21,20 @@ formula and no parameters.  The reading used here restates the paper:
 * precision (a reading: the attention consumes bf16 q and k, as any bf16
   pipeline that applies RoPE before attention does): the table holds
   fp32(m cos(p h_i)) and fp32(m sin(p h_i)) computed in fp64; a rotated
-  element is fp32(fp32(x_i c) - fp32(x_j s)) (resp. + for the partner) and
-  is then rounded to bf16 (nearest even) before the attention products.  The
-  exact fp64 rotation (`apply_rope_exact`) is kept for the pins.
+  element is the exact value x_i c - x_j s (resp. x_j c + x_i s) of those
+  fp32 entries and the bf16 inputs, rounded once to bf16 (nearest, ties to
+  even) -- the plain definition of "the rotation, in bf16".  The products
+  are exact in fp64 (8 x 24 significant bits); the sum is carried as an
+  unevaluated fp64 pair (Knuth's two-sum) so that the one rounding sees the
+  exact value.  The fp64 rotation without the final rounding
+  (`apply_rope_exact`) is kept for the pins.
 """
 
 import math
 
 import numpy as np
-import torch
 
-__all__ = ["yarn_inv_freq", "yarn_mscale", "rope_table", "apply_rope_exact", "apply_rope_bf16",
+__all__ = ["yarn_inv_freq", "yarn_mscale", "rope_table", "apply_rope_exact", "apply_rope_bf16", "round_bf16",
            "apply_rope_adjoint", "ref_fwd_rope", "ref_decode_rope", "ref_bwd_rope"]
 
 
@@ -78,22 +81,48 @@ def apply_rope_adjoint(g, positions, cos, sin):
     return np.concatenate([g1 * c + g2 * s, g2 * c - g1 * s], axis=-1)
 
 
-def _to_bf16(a32):
-    return torch.from_numpy(np.ascontiguousarray(a32)).to(torch.bfloat16).to(torch.float64).numpy()
+def _two_sum(a, b):
+    """Knuth's error-free sum: a + b == s + e exactly, s = fl(a + b)."""
+    s = a + b
+    bb = s - a
+    e = (a - (s - bb)) + (b - bb)
+    return s, e
+
+
+def round_bf16(hi, lo=None):
+    """Round the exact value hi + lo (an unevaluated fp64 pair, |lo| at most
+    half an fp64 ulp of hi; lo = 0 when omitted) to the nearest bf16 (8
+    significant bits), ties to even; returns fp64.  Only hi can sit exactly
+    on a midpoint between two bf16 numbers (a midpoint strictly between
+    hi + lo and hi would be closer to hi + lo than hi is); there the sign of
+    lo decides.  Values must be 0 or of magnitude >= 2^-126 (bf16 normals)
+    and below the bf16 overflow threshold."""
+    hi = np.asarray(hi, dtype=np.float64)
+    lo = np.zeros_like(hi) if lo is None else np.asarray(lo, dtype=np.float64)
+    a = np.abs(hi[hi != 0])
+    if a.size and (a.min() < 2.0 ** -126 or a.max() >= 2.0 ** 128 * (1 - 2.0 ** -9)):
+        raise ValueError("round_bf16: value outside the bf16 normal range")
+    m, e = np.frexp(hi)                 # hi = m 2^e, 0.5 <= |m| < 1
+    t = np.ldexp(m, 8)                  # 8 significant bits above the point
+    r = np.rint(t)                      # nearest, ties to even
+    mid = (t - np.floor(t)) == 0.5
+    r = np.where(mid & (lo > 0), np.ceil(t), r)
+    r = np.where(mid & (lo < 0), np.floor(t), r)
+    return np.ldexp(r, e - 8)
 
 
 def apply_rope_bf16(x, positions, cos32, sin32):
-    """The rotation as the bf16 path computes it (see the header): fp32
-    products and difference with one rounding each, then bf16.  x holds
-    bf16 values (any float dtype); cos32/sin32 are the fp32 tables."""
+    """The rotation in bf16 (see the header): the exact value of the
+    rotation of x (bf16 values, any float dtype) with the fp32 table entries
+    cos32/sin32, rounded once to bf16, nearest even."""
     half = x.shape[-1] // 2
-    xf = x.astype(np.float32)
-    c = cos32[positions][:, None, :].astype(np.float32)
-    s = sin32[positions][:, None, :].astype(np.float32)
-    x1, x2 = xf[..., :half], xf[..., half:]
-    y1 = (x1 * c) - (x2 * s)
-    y2 = (x2 * c) + (x1 * s)
-    return _to_bf16(np.concatenate([y1, y2], axis=-1).astype(np.float32))
+    xd = np.asarray(x, dtype=np.float64)
+    c = np.asarray(cos32[positions], dtype=np.float64)[:, None, :]
+    s = np.asarray(sin32[positions], dtype=np.float64)[:, None, :]
+    x1, x2 = xd[..., :half], xd[..., half:]
+    y1 = round_bf16(*_two_sum(x1 * c, -(x2 * s)))
+    y2 = round_bf16(*_two_sum(x2 * c, x1 * s))
+    return np.concatenate([y1, y2], axis=-1)
 
 
 def ref_fwd_rope(q, k, v, sinks, window, scale, cos32, sin32, **kw):

@@ -11,8 +11,11 @@
 * norm: each pair's length is multiplied by the temperature; position 0 is
   the temperature times the identity
 * relative position: <R(p) q, R(p') k> depends only on p - p'
-* the bf16 path stays within one bf16 ulp of the exact rotation, and equals
-  the exact rotation for a unit pair
+* the bf16 rotation is the exact rational value rounded once to bf16
+  (checked element by element by integer arithmetic), including a hand case
+  where two fp32 roundings would land on the other side of a bf16 midpoint;
+  the rounding's ties and its two-term input on hand values
+* the temperature m = 0.1 ln(s) + 1 at s = e and s = e^10 (1.1 and 2.0)
 * attention with the identity table is attention without RoPE; decode with
   RoPE is the last row of prefill with RoPE
 * backward: the adjoint satisfies <R x, y> = <x, R^T y>; gradients with
@@ -21,12 +24,13 @@
 """
 
 import math
+from fractions import Fraction
 
 import numpy as np
 import pytest
 
 from oracle import (apply_rope_adjoint, apply_rope_bf16, apply_rope_exact, brute_rope, ref_bwd_rope, ref_decode,
-                    ref_decode_rope, ref_fwd, ref_fwd_rope, rope_table, yarn_inv_freq, yarn_mscale)
+                    ref_decode_rope, ref_fwd, ref_fwd_rope, rope_table, round_bf16, yarn_inv_freq, yarn_mscale)
 
 GPTOSS_LIKE = dict(base=150000.0, factor=32.0, orig_ctx=4096, alpha=1.0, beta=32.0)
 
@@ -116,20 +120,96 @@ def test_relative_position():
         assert abs(a - b) <= 1e-10 * max(1.0, abs(a))
 
 
-def test_bf16_path_within_one_ulp_and_exact_on_unit_pair():
+def _exact_bf16(fr):
+    """Nearest bf16 (ties to even) of an exact rational, by integer
+    arithmetic on the rational itself (no floating point on the value)."""
+    if fr == 0:
+        return 0.0
+    sign, a = (1 if fr > 0 else -1), abs(fr)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    while Fraction(2) ** e > a:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= a:
+        e += 1
+    ulp = Fraction(2) ** (e - 7)  # 8 significant bits
+    n, rem = divmod(a, ulp)
+    n = int(n)
+    if rem * 2 > ulp or (rem * 2 == ulp and n % 2 == 1):
+        n += 1
+    return sign * float(n * ulp)
+
+
+def test_bf16_rotation_is_the_exact_value_rounded_once():
+    """Every element against the exact rational value of the rotation with
+    the fp32 table entries, rounded to bf16 by integer arithmetic."""
     rng = np.random.default_rng(7)
-    c32, s32 = rope_table(100, 64, **GPTOSS_LIKE)
-    x = _bf16(rng.standard_normal((100, 4, 64)))
-    pos = np.arange(100)
+    c32, s32 = rope_table(4096, 64, **GPTOSS_LIKE)
+    x = _bf16(rng.standard_normal((40, 2, 64)))
+    pos = rng.integers(0, 4096, 40)
     y = apply_rope_bf16(x, pos, c32, s32)
+    for t in range(40):
+        for h in range(2):
+            for i in range(32):
+                c, s = Fraction(float(c32[pos[t], i])), Fraction(float(s32[pos[t], i]))
+                a, b = Fraction(float(x[t, h, i])), Fraction(float(x[t, h, i + 32]))
+                assert y[t, h, i] == _exact_bf16(a * c - b * s)
+                assert y[t, h, i + 32] == _exact_bf16(b * c + a * s)
+    # and so within half a bf16 ulp of the fp64 rotation (no second rounding)
     ex = apply_rope_exact(x, pos, c32.astype(np.float64), s32.astype(np.float64))
-    ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(ex), 1e-30))) - 7)
-    assert (np.abs(y - ex) <= ulp).all()
+    ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(y), 1e-30))) - 7)
+    assert (np.abs(y - ex) <= 0.5 * ulp * (1 + 1e-12)).all()
     # a unit pair (1, 0) rotates to (c, s) rounded once to bf16
     e = np.zeros((1, 1, 64))
     e[0, 0, 5] = 1.0
     y = apply_rope_bf16(e, np.array([77]), c32, s32)
     assert y[0, 0, 5] == _bf16(c32[77, 5]) and y[0, 0, 37] == _bf16(s32[77, 5])
+
+
+def test_bf16_rotation_where_two_fp32_roundings_would_differ():
+    """x_i = 0x1.66p-6, x_(i+32) = -0x1.4ap+0, c = 0x1.58b9p+0,
+    s = 0x1.670b4cp-10: the exact value x_i c - x_(i+32) s lies just below the
+    bf16 midpoint 0x1.ffp-6, so it rounds to 0x1.fep-6; rounding x_i c to fp32
+    first carries it past the midpoint (to 0x1.00p-5).  The oracle must give
+    the single rounding."""
+    x1, x2 = float.fromhex("0x1.66p-6"), float.fromhex("-0x1.4ap+0")
+    c, s = float.fromhex("0x1.58b9p+0"), float.fromhex("0x1.670b4cp-10")
+    exact = Fraction(x1) * Fraction(c) - Fraction(x2) * Fraction(s)
+    mid = Fraction(float.fromhex("0x1.ffp-6"))
+    assert exact < mid and mid - exact < Fraction(1, 2 ** 29)
+    x = np.zeros((1, 1, 64))
+    x[0, 0, 0], x[0, 0, 32] = x1, x2
+    c32 = np.ones((1, 32), np.float32)
+    s32 = np.zeros((1, 32), np.float32)
+    c32[0, 0], s32[0, 0] = c, s
+    y = apply_rope_bf16(x, np.array([0]), c32, s32)
+    assert y[0, 0, 0] == float.fromhex("0x1.fep-6")
+    assert float(np.float32(np.float32(x1 * c) - np.float32(x2 * s))) >= float(mid)
+
+
+def test_round_bf16_ties_and_pairs():
+    one, step = 1.0, 2.0 ** -7            # bf16 neighbours 1 and 1 + 2^-7
+    midpoint = one + step / 2
+    assert round_bf16(np.array([midpoint]))[0] == one                    # tie: even (1.0000000)
+    assert round_bf16(np.array([midpoint + step]))[0] == one + 2 * step  # tie: even (1.0000010)
+    assert round_bf16(np.array([midpoint]), np.array([2.0 ** -60]))[0] == one + step   # just above
+    assert round_bf16(np.array([midpoint]), np.array([-2.0 ** -60]))[0] == one         # just below
+    assert round_bf16(np.array([-midpoint]), np.array([-2.0 ** -60]))[0] == -(one + step)
+    assert round_bf16(np.array([-midpoint]), np.array([2.0 ** -60]))[0] == -one
+    assert round_bf16(np.array([0.0, 3.0, 255.0, 511.0])).tolist() == [0.0, 3.0, 255.0, 512.0]  # 8 bits exact; 9 bits a tie
+    assert round_bf16(np.array([257.0]))[0] == 256.0                     # 257 = 256 + half a step: even
+    assert round_bf16(np.array([259.0]))[0] == 260.0
+    with pytest.raises(ValueError):
+        round_bf16(np.array([1e-40]))
+
+
+def test_yarn_mscale_hand_values():
+    """The temperature 0.1 ln(s) + 1 at points where the logarithm is known
+    exactly: s = e gives 1.1, s = e^10 gives 2.0; no scaling (s <= 1) gives 1."""
+    assert abs(yarn_mscale(math.e) - 1.1) < 1e-15
+    assert abs(yarn_mscale(math.exp(10.0)) - 2.0) < 1e-15
+    assert yarn_mscale(0.5) == 1.0
+    assert yarn_mscale(1.0) == 1.0
+    assert abs(yarn_mscale(32.0) - 1.3465735902799727) < 1e-15   # 0.1 * 5 ln 2 + 1
 
 
 def test_identity_table_is_attention_without_rope():
