@@ -35,7 +35,19 @@ gptoss_status ok() {
     return GPTOSS_OK;
 }
 
-constexpr long long kIndexLimit = (1LL << 31) - 1;  // kernels index rows in int32
+// Kernels index token rows in int32 and round row counts up to whole tiles
+// (at most 256 rows), so row counts stay 2^16 below 2^31.
+constexpr long long kIndexLimit = (1LL << 31) - (1LL << 16);
+// Decode: the longest sequence a call may name (2^30 tokens; one KV head of
+// it alone is 256 GB of bf16 K and V), so that chunk arithmetic fits int32.
+constexpr int kMaxDecodeSeqlen = 1 << 30;
+
+gptoss_status check_decode_seqlen(int max_seqlen) {
+    if (max_seqlen < 1) return fail(GPTOSS_ERR_INVALID_ARGUMENT, "max_seqlen (%d) must be >= 1", max_seqlen);
+    if (max_seqlen > kMaxDecodeSeqlen)
+        return fail(GPTOSS_ERR_INVALID_ARGUMENT, "max_seqlen (%d) exceeds 2^30", max_seqlen);
+    return GPTOSS_OK;
+}
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -101,7 +113,7 @@ gptoss_status gptoss_attn_fwd(const void* q, const void* k, const void* v, const
     if (st != GPTOSS_OK) return st;
     if (B == 0 || S == 0) return ok();
     if ((long long)B * S > kIndexLimit)
-        return fail(GPTOSS_ERR_INVALID_ARGUMENT, "B*S = %lld exceeds 2^31-1", (long long)B * S);
+        return fail(GPTOSS_ERR_INVALID_ARGUMENT, "B*S = %lld exceeds 2^31 - 2^16", (long long)B * S);
     CHECK_PTR(q, 16);
     CHECK_PTR(k, 16);
     CHECK_PTR(v, 16);
@@ -143,7 +155,7 @@ gptoss_status gptoss_attn_bwd(const void* q, const void* k, const void* v, const
     if (st != GPTOSS_OK) return st;
     if (B == 0 || S == 0) return ok();
     if ((long long)B * S > kIndexLimit)
-        return fail(GPTOSS_ERR_INVALID_ARGUMENT, "B*S = %lld exceeds 2^31-1", (long long)B * S);
+        return fail(GPTOSS_ERR_INVALID_ARGUMENT, "B*S = %lld exceeds 2^31 - 2^16", (long long)B * S);
     CHECK_PTR(q, 16);
     CHECK_PTR(k, 16);
     CHECK_PTR(v, 16);
@@ -190,6 +202,8 @@ static gptoss_status check_varlen(int N, int T, int max_seqlen) {
     if (N < 0 || T < 0) return fail(GPTOSS_ERR_INVALID_ARGUMENT, "N (%d) and T (%d) must be >= 0", N, T);
     if (max_seqlen < 1) return fail(GPTOSS_ERR_INVALID_ARGUMENT, "max_seqlen (%d) must be >= 1", max_seqlen);
     if (N > 65535) return fail(GPTOSS_ERR_INVALID_ARGUMENT, "N (%d) exceeds 65535 documents per call", N);
+    if ((long long)T > kIndexLimit)
+        return fail(GPTOSS_ERR_INVALID_ARGUMENT, "T = %d exceeds 2^31 - 2^16", T);
     return GPTOSS_OK;
 }
 
@@ -220,7 +234,7 @@ gptoss_status gptoss_attn_fwd_varlen(const void* q, const void* k, const void* v
     a.cu = cu_seqlens;
     a.rope = nullptr;
     a.B = N;
-    a.S = max_seqlen;
+    a.S = max_seqlen < T ? max_seqlen : T;  // no document is longer than the T rows
     a.T = T;
     a.Hq = Hq;
     a.Hkv = Hkv;
@@ -277,7 +291,7 @@ gptoss_status gptoss_attn_bwd_varlen(const void* q, const void* k, const void* v
     a.workspace = workspace;
     a.cu = cu_seqlens;
     a.B = N;
-    a.S = max_seqlen;
+    a.S = max_seqlen < T ? max_seqlen : T;  // no document is longer than the T rows
     a.T = T;
     a.Hq = Hq;
     a.Hkv = Hkv;
@@ -288,6 +302,7 @@ gptoss_status gptoss_attn_bwd_varlen(const void* q, const void* k, const void* v
 
 size_t gptoss_attn_decode_workspace_size(int N, int Hq, int Hkv, int D, int max_seqlen, int window) {
     if (N <= 0 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || D != 64 || max_seqlen < 1 || window < 0) return 0;
+    if (max_seqlen > kMaxDecodeSeqlen) return 0;
     return gptoss::decode_workspace_bytes(N, Hq, Hkv, max_seqlen, window);
 }
 
@@ -296,8 +311,9 @@ gptoss_status gptoss_attn_decode(const void* q, const void* k_cache, const void*
                                  float softmax_scale, void* out, float* lse, void* workspace,
                                  size_t workspace_bytes, void* stream) {
     if (N < 0) return fail(GPTOSS_ERR_INVALID_ARGUMENT, "N (%d) must be >= 0", N);
-    if (max_seqlen < 1) return fail(GPTOSS_ERR_INVALID_ARGUMENT, "max_seqlen (%d) must be >= 1", max_seqlen);
-    gptoss_status st = check_common(Hq, Hkv, D, window, softmax_scale);
+    gptoss_status st = check_decode_seqlen(max_seqlen);
+    if (st != GPTOSS_OK) return st;
+    st = check_common(Hq, Hkv, D, window, softmax_scale);
     if (st != GPTOSS_OK) return st;
     if (N == 0) return ok();
     if ((long long)N > 65535)
@@ -347,8 +363,9 @@ gptoss_status gptoss_attn_decode_paged(const void* q, const void* k_pages, const
                                        int max_seqlen, int window, float softmax_scale, void* out, float* lse,
                                        void* workspace, size_t workspace_bytes, void* stream) {
     if (N < 0) return fail(GPTOSS_ERR_INVALID_ARGUMENT, "N (%d) must be >= 0", N);
-    if (max_seqlen < 1) return fail(GPTOSS_ERR_INVALID_ARGUMENT, "max_seqlen (%d) must be >= 1", max_seqlen);
-    gptoss_status st = check_common(Hq, Hkv, D, window, softmax_scale);
+    gptoss_status st = check_decode_seqlen(max_seqlen);
+    if (st != GPTOSS_OK) return st;
+    st = check_common(Hq, Hkv, D, window, softmax_scale);
     if (st != GPTOSS_OK) return st;
     if (!is_pow2(page_size) || page_size > 65536)
         return fail(GPTOSS_ERR_INVALID_ARGUMENT, "page_size (%d) must be a power of two in [1, 65536]", page_size);
@@ -480,7 +497,7 @@ gptoss_status gptoss_attn_fwd_rope(const void* q, const void* k, const void* v, 
     if (st != GPTOSS_OK) return st;
     if (B == 0 || S == 0) return ok();
     if ((long long)B * S > kIndexLimit)
-        return fail(GPTOSS_ERR_INVALID_ARGUMENT, "B*S = %lld exceeds 2^31-1", (long long)B * S);
+        return fail(GPTOSS_ERR_INVALID_ARGUMENT, "B*S = %lld exceeds 2^31 - 2^16", (long long)B * S);
     if (table_positions < S)
         return fail(GPTOSS_ERR_INVALID_ARGUMENT, "rope table holds %d positions, S is %d", table_positions, S);
     CHECK_PTR(q, 16);
@@ -523,8 +540,9 @@ gptoss_status gptoss_attn_decode_rope(const void* q, const void* k_cache, const 
                                       int Hkv, int D, int max_seqlen, int window, float softmax_scale, void* out,
                                       float* lse, void* workspace, size_t workspace_bytes, void* stream) {
     if (N < 0) return fail(GPTOSS_ERR_INVALID_ARGUMENT, "N (%d) must be >= 0", N);
-    if (max_seqlen < 1) return fail(GPTOSS_ERR_INVALID_ARGUMENT, "max_seqlen (%d) must be >= 1", max_seqlen);
-    gptoss_status st = check_common(Hq, Hkv, D, window, softmax_scale);
+    gptoss_status st = check_decode_seqlen(max_seqlen);
+    if (st != GPTOSS_OK) return st;
+    st = check_common(Hq, Hkv, D, window, softmax_scale);
     if (st != GPTOSS_OK) return st;
     if (table_positions < max_seqlen)
         return fail(GPTOSS_ERR_INVALID_ARGUMENT, "rope table holds %d positions, max_seqlen is %d", table_positions,
@@ -590,7 +608,7 @@ gptoss_status gptoss_attn_bwd_rope(const void* q, const void* k_rot, const void*
     if (st != GPTOSS_OK) return st;
     if (B == 0 || S == 0) return ok();
     if ((long long)B * S > kIndexLimit)
-        return fail(GPTOSS_ERR_INVALID_ARGUMENT, "B*S = %lld exceeds 2^31-1", (long long)B * S);
+        return fail(GPTOSS_ERR_INVALID_ARGUMENT, "B*S = %lld exceeds 2^31 - 2^16", (long long)B * S);
     if ((long long)B * S * Hq > kIndexLimit)
         return fail(GPTOSS_ERR_INVALID_ARGUMENT, "B*S*Hq = %lld rows exceeds 2^31-1", (long long)B * S * Hq);
     if (table_positions < S)

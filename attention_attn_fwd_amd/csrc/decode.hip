@@ -393,14 +393,17 @@ decode_merge_kernel(DecParams p) {
 // workload cost more than they gain.
 struct ChunkPlan { int keys, n; };
 ChunkPlan chunk_plan(int N, int Hkv, int G, int max_seqlen, int window) {
-    const int vis = window > 0 ? std::min(max_seqlen, window) : max_seqlen;
+    // 64-bit throughout: max_seqlen may be up to 2^30 (the entry points
+    // refuse more), and the rounding below must not wrap
+    const long long vis = window > 0 ? std::min<long long>(max_seqlen, window) : (long long)max_seqlen;
     const long long groups = (long long)N * ((Hkv + kWaves - 1) / kWaves) * ((G + 31) / 32);
     const long long want = std::max(1LL, (kTargetWorkgroups + groups - 1) / groups);
-    const int max_chunks = std::max(1, (vis + kTileKeys - 1) / kTileKeys);
-    const int n = (int)std::min<long long>(want, max_chunks);
-    int keys = (vis + n - 1) / n;
-    keys = std::max(kTileKeys, (keys + kTileKeys - 1) / kTileKeys * kTileKeys);
-    return ChunkPlan{keys, std::max(1, (vis + keys - 1) / keys)};
+    const long long max_chunks = std::max(1LL, (vis + kTileKeys - 1) / kTileKeys);
+    const long long n = std::min(want, max_chunks);
+    long long keys = (vis + n - 1) / n;
+    keys = std::max<long long>(kTileKeys, (keys + kTileKeys - 1) / kTileKeys * kTileKeys);
+    const long long chunks = std::max(1LL, (vis + keys - 1) / keys);
+    return ChunkPlan{(int)keys, (int)chunks};
 }
 
 }  // namespace
@@ -427,6 +430,9 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
     p.window = a.window;
     p.max_seqlen = a.max_seqlen;
     const ChunkPlan cp = chunk_plan(a.N, a.Hkv, p.G, a.max_seqlen, a.window);
+    // every visible key of the longest allowed sequence lies in some chunk
+    const long long vis = a.window > 0 ? std::min(a.max_seqlen, a.window) : a.max_seqlen;
+    if (cp.keys < kTileKeys || (long long)cp.keys * cp.n < vis) return hipErrorInvalidValue;
     p.n_splits = cp.n;
     p.chunk_keys = cp.keys;
     p.n_hblk = (p.G + 31) / 32;

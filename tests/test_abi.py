@@ -130,6 +130,8 @@ def _dec(lib, **kw):
 @pytest.mark.parametrize("kw,frag", [
     (dict(cu=None), "cu_seqlens is NULL"),
     (dict(max_seqlen=0), "max_seqlen"),
+    (dict(max_seqlen=(1 << 30) + 1), "exceeds 2^30"),
+    (dict(max_seqlen=2 ** 31 - 1), "exceeds 2^30"),
     (dict(N=-1), "N"),
     (dict(N=70000), "exceeds"),
     (dict(window=-2), "window"),
@@ -151,6 +153,22 @@ def test_workspace_size_queries(lib):
     assert lib.gptoss_attn_decode_workspace_size(128, 64, 8, 128, 1024, 0) == 0  # unsupported D
     assert lib.gptoss_attn_bwd_workspace_size(4, 4096, 64, 8, 64, 0) >= 0
     assert lib.gptoss_attn_bwd_workspace_size(4, 4096, 64, 7, 64, 0) == 0
+
+
+def test_decode_workspace_size_near_the_int32_limit(lib):
+    """The chunk plan is computed in 64 bits: up to the largest allowed
+    max_seqlen (2^30) the workspace grows with the sequence and never wraps;
+    beyond it the size query returns 0 and the entry points refuse the call."""
+    sizes = [lib.gptoss_attn_decode_workspace_size(1, 64, 8, 64, L, 0)
+             for L in (1 << 16, 1 << 20, 1 << 26, (1 << 30) - 63, 1 << 30)]
+    assert all(x > 0 for x in sizes) and sizes == sorted(sizes), sizes
+    for L in ((1 << 30) + 1, 2 ** 31 - 64, 2 ** 31 - 63, 2 ** 31 - 1):
+        assert lib.gptoss_attn_decode_workspace_size(1, 64, 8, 64, L, 0) == 0
+        assert _dec(lib, N=1, max_seqlen=L, ws_bytes=1 << 40) == 1
+        assert "exceeds 2^30" in lib.gptoss_attn_last_error().decode()
+    # a window bounds the visible keys whatever max_seqlen says
+    assert lib.gptoss_attn_decode_workspace_size(1, 64, 8, 64, 1 << 30, 128) == \
+        lib.gptoss_attn_decode_workspace_size(1, 64, 8, 64, 128, 128)
 
 
 def test_error_message_cleared_on_success(lib):
@@ -231,6 +249,7 @@ VARLEN_BAD = [
     (dict(T=-5), "must be >= 0"),
     (dict(max_seqlen=0), "max_seqlen"),
     (dict(N=65536), "exceeds"),
+    (dict(T=2 ** 31 - 1), "exceeds 2^31 - 2^16"),
     (dict(Hq=64, Hkv=6), "multiple"),
     (dict(window=-1), "window"),
     (dict(scale=math.nan), "softmax_scale"),

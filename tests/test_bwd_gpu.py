@@ -11,7 +11,7 @@ import attention_attn_fwd_amd as attn
 from attention_attn_fwd_amd import synth
 from oracle import ref_bwd
 
-from _util import seed_of, GRAD_REL_L2, f64, need_gpu, rel_l2
+from _util import GRAD_REL_L2, check_grads_by_group, f64, nan_grads, need_gpu, ref_bwd_groups, rel_l2, seed_of
 
 pytestmark = pytest.mark.gpu
 
@@ -50,6 +50,7 @@ SMALL = [  # B, S, Hq, Hkv  (S = 1 over 4 batches: one key per head makes a sing
            # batch's relative L2 hinge on one possibly cancelling dS sum)
     (4, 1, 8, 1), (1, 17, 8, 1), (2, 129, 8, 1), (1, 300, 8, 8), (1, 700, 8, 1), (2, 77, 16, 2),
     (1, 200, 6, 2), (1, 333, 1, 1), (1, 260, 4, 4),
+    (2, 200, 16, 8), (3, 150, 24, 8),  # B * Hkv = 16, 24: the XCD-aware order with 2, 3 groups per XCD
 ]
 
 
@@ -62,7 +63,7 @@ def test_bwd_small_shapes(shape, window):
     dout = synth.make_dout(tuple(case.q.shape), seed=S + window)
     print(f"bwd shape={shape} window={window}", flush=True)
     grads = _run(case, dout, window, dev)
-    _check(grads, _oracle(case, dout, window), f"{shape} W={window}")
+    check_grads_by_group([f64(t) for t in grads], _oracle(case, dout, window), Hkv, f"{shape} W={window}")
 
 
 @pytest.mark.parametrize("heads", [(16, 1), (32, 1), (64, 1), (128, 1), (12, 1), (80, 2)], ids=lambda h: "H%dx%d" % h)
@@ -107,16 +108,19 @@ def test_bwd_is_deterministic():
 
 
 @pytest.mark.parametrize("window", [128, 0])
-def test_bwd_c3_sampled_group(window):
-    """The full training shape (B=4, S=4096, 64q/8kv) in the launch
-    configuration bench.py times; the oracle computes every gradient of KV
-    group 0 (query heads 0..7, all batches) exactly."""
+def test_bwd_training_workload_whole(window):
+    """The training shape (B=4, S=4096, 64q/8kv) in the launch configuration
+    bench.py times: every gradient element of all eight KV groups against the
+    oracle (run per batch and KV group on the host's cores), into NaN-filled
+    gradient buffers."""
     dev = need_gpu()
     case, dout = synth.config_inputs("c3_bwd_b4_s4096_h64x8")
-    print(f"bwd C3 W={window}", flush=True)
-    grads = _run(case, dout, window, dev)
+    print(f"bwd B4 S4096 W={window}", flush=True)
+    q, k, v, s = (t.to(dev) for t in (case.q, case.k, case.v, case.sinks))
+    out, lse = attn.fwd(q, k, v, s, window, case.scale)
+    grads = attn.bwd(q, k, v, s, out, lse, dout.to(dev), window, case.scale, grads=nan_grads(q, k, v, q.shape[2]))
+    torch.cuda.synchronize()
     for t in grads:
         assert torch.isfinite(t.float()).all()
-    heads = list(range(8))
-    ref = _oracle(case, dout, window, heads=heads)
-    _check(grads, ref, f"C3 W={window}", heads=heads, kv_heads=[0])
+    ref = ref_bwd_groups(f64(case.q), f64(case.k), f64(case.v), f64(case.sinks), f64(dout), window, case.scale)
+    check_grads_by_group([f64(t) for t in grads], ref, k.shape[2], f"B4 S4096 W={window}")

@@ -155,3 +155,34 @@ def test_decode_is_deterministic():
     a = _run(case, 0, dev)
     b = _run(case, 0, dev)
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+@pytest.mark.parametrize("window", [0, 128])
+@pytest.mark.parametrize("workload", ["n128_l1024", "n8_l1024", "one_65536"])
+def test_decode_split_count_invariance(workload, window):
+    """The result must not depend on how a sequence's keys are cut into
+    chunks: the same inputs decoded under the chunk plans of max_seqlen =
+    the longest sequence, 4x and 64x it (the plan follows max_seqlen and the
+    number of sequences) match the oracle each, and agree with one another
+    within one bf16 ulp (out) and 2e-5 (lse)."""
+    dev = need_gpu()
+    if workload == "n128_l1024":
+        case = synth.config_inputs("c4_decode_n128_l1024_h64x8")
+    elif workload == "n8_l1024":
+        case = synth.make_decode(8, 64, 8, max_len=1024, seed=seed_of("t3", window))
+    else:
+        case = synth.make_decode(1, 64, 8, lengths=[65536], seed=seed_of("t3long", window))
+    Lmax = int(np.diff(case.cu_seqlens.numpy()).max())
+    ro, rl = _oracle(case, window)
+    results = []
+    for ms in (Lmax, 4 * Lmax, 64 * Lmax):
+        ws = attn.decode_workspace_size(case.q.shape[0], 64, 8, 64, ms, window)
+        print(f"decode T3 {workload} W={window} max_seqlen={ms} workspace={ws}", flush=True)
+        out, lse = _run(case, window, dev, max_seqlen=ms)
+        check_out_lse(f64(out), f64(lse), ro, rl, f"{workload} W={window} max_seqlen={ms}")
+        results.append((f64(out), f64(lse)))
+    (o0, l0) = results[0]
+    for o, l in results[1:]:
+        ulp = np.exp2(np.floor(np.log2(np.maximum(np.maximum(np.abs(o), np.abs(o0)), 2.0 ** -126))) - 7)
+        assert (np.abs(o - o0) <= ulp).all()
+        assert np.abs(l - l0).max() <= 2e-5

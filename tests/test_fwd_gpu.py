@@ -8,7 +8,7 @@ import attention_attn_fwd_amd as attn
 from attention_attn_fwd_amd import synth
 from oracle import ref_fwd
 
-from _util import seed_of, check_out_lse, f64, need_gpu, out_bar
+from _util import check_out_lse, f64, nan_like, need_gpu, out_bar, ref_fwd_groups, seed_of
 
 pytestmark = pytest.mark.gpu
 
@@ -27,6 +27,7 @@ def _oracle(case, window, **kw):
 SMALL = [  # B, S, Hq, Hkv
     (1, 1, 8, 1), (1, 17, 8, 1), (2, 129, 8, 1), (1, 300, 8, 8), (1, 1000, 8, 1), (2, 77, 16, 2),
     (1, 200, 6, 2), (1, 333, 1, 1), (1, 260, 4, 4),
+    (2, 200, 16, 8), (3, 150, 24, 8),  # B * Hkv = 16, 24: the XCD-aware order with 2, 3 groups per XCD
 ]
 
 
@@ -110,30 +111,53 @@ def test_fwd_c0_both_layers():
         check_out_lse(f64(out), f64(lse), ro, rl, f"C0 W={window}")
 
 
-def _sample_rows(S, rng, n_rand=24):
-    rows = set(range(0, 20)) | {126, 127, 128, 129, 255, 256} | set(range(S - 16, S))
-    rows |= set(rng.integers(0, S, n_rand).tolist())
-    return np.array(sorted(r for r in rows if 0 <= r < S))
-
-
-@pytest.mark.parametrize("name", ["c1_b4_s4096_h64x8", "c2_b1_s65536_h64x8"])
-@pytest.mark.parametrize("window", [128, 0])
-def test_fwd_full_size_sampled_rows(name, window):
-    """The workload shapes, in the launch configuration bench.py times; the
-    oracle computes a sample of rows (each sampled row is exact)."""
-    dev = need_gpu()
-    case = synth.config_inputs(name)
-    print(f"fwd {name} W={window}", flush=True)
-    out, lse = _run(case, window, dev)
-    B, S, Hq, _ = case.q.shape
-    rng = np.random.default_rng(S + window)
-    rows = _sample_rows(S, rng)
-    heads = list(range(Hq)) if S <= 4096 else list(range(0, Hq, 3))
-    batches = list(range(B))
-    ro, rl = _oracle(case, window, rows=rows, heads=heads, batches=batches)
-    sel_o = f64(out[:, rows])
-    check_out_lse(sel_o, f64(lse)[:, :, rows], ro[:, rows], rl[:, :, rows], f"{name} W={window}")
-    # every output element is finite and every lse is >= the sink (sink is in the sum)
+def _run_poisoned(case, window, dev):
+    """The forward into NaN-filled out and lse buffers."""
+    q, k, v, s = (t.to(dev) for t in (case.q, case.k, case.v, case.sinks))
+    B, S, Hq, D = q.shape
+    out = nan_like((B, S, Hq, D), torch.bfloat16, dev)
+    lse = nan_like((B, Hq, S), torch.float32, dev)
+    attn.fwd(q, k, v, s, window, case.scale, out=out, lse=lse)
+    torch.cuda.synchronize()
+    # every element written: finite, and every lse at least the sink (it is in the sum)
     assert torch.isfinite(out.float()).all() and torch.isfinite(lse).all()
-    sinks = case.sinks.to(dev)
-    assert (lse >= sinks.view(1, -1, 1) - 1e-4).all()
+    assert (lse >= s.view(1, -1, 1) - 1e-4).all()
+    return out, lse
+
+
+@pytest.mark.parametrize("window", [128, 0])
+def test_fwd_prefill_workload_whole(window):
+    """B=4, S=4096, 64q/8kv in the launch configuration bench.py times:
+    every output and lse element against the oracle (run per batch and KV
+    group on the host's cores)."""
+    dev = need_gpu()
+    case = synth.config_inputs("c1_b4_s4096_h64x8")
+    print(f"fwd B4 S4096 W={window}", flush=True)
+    out, lse = _run_poisoned(case, window, dev)
+    ro, rl = ref_fwd_groups(f64(case.q), f64(case.k), f64(case.v), f64(case.sinks), window, case.scale)
+    check_out_lse(f64(out), f64(lse), ro, rl, f"B4 S4096 W={window}")
+
+
+def _long_context_rows(S, W, rng):
+    """512 query rows: the first 128, W - 1 .. W + 1, the last 64, and random
+    rows to make up 512."""
+    rows = set(range(128)) | {W - 1, W, W + 1} | set(range(S - 64, S))
+    while len(rows) < 512:
+        rows.add(int(rng.integers(0, S)))
+    return np.array(sorted(rows))
+
+
+@pytest.mark.parametrize("window", [128, 0])
+def test_fwd_long_context_sampled_rows(window):
+    """B=1, S=65536, 64q/8kv in the launch configuration bench.py times:
+    all 64 heads at 512 query rows (each row exact over all its keys), and
+    every element of the output written and finite."""
+    dev = need_gpu()
+    case = synth.config_inputs("c2_b1_s65536_h64x8")
+    print(f"fwd B1 S65536 W={window}", flush=True)
+    out, lse = _run_poisoned(case, window, dev)
+    S = case.q.shape[1]
+    rows = _long_context_rows(S, 128, np.random.default_rng(S + window))
+    ro, rl = ref_fwd_groups(f64(case.q), f64(case.k), f64(case.v), f64(case.sinks), window, case.scale, rows=rows)
+    ri = torch.from_numpy(rows).to(dev)
+    check_out_lse(f64(out[:, ri]), f64(lse[:, :, ri]), ro, rl, f"B1 S65536 W={window}")

@@ -11,7 +11,7 @@ import attention_attn_fwd_amd as attn
 from attention_attn_fwd_amd import synth
 from oracle import apply_rope_bf16, ref_bwd_rope, ref_decode_rope, ref_fwd_rope, rope_table
 
-from _util import check_out_lse, f64, need_gpu, seed_of
+from _util import check_grads_by_group, check_out_lse, f64, nan_grads, nan_like, need_gpu, oracle_map, seed_of
 
 pytestmark = pytest.mark.gpu
 
@@ -52,9 +52,23 @@ def test_table_matches_oracle(params):
         assert (got == ref).mean() > 0.999
 
 
-def test_rows_bitwise_with_the_oracle_table():
-    """Given the oracle's fp32 table, the kernel's rotation is the same fp32
-    operations and bf16 rounding as the oracle's: bit-identical."""
+def _kernel_rotation_recipe(x, pos, c, s):
+    """The kernel's own evaluation order (not the oracle): each product and
+    the difference rounded to fp32, no fused multiply-add, then bf16."""
+    xt = torch.from_numpy(np.asarray(x, dtype=np.float32))
+    ct = torch.from_numpy(c[pos])[:, None, :]
+    st = torch.from_numpy(s[pos])[:, None, :]
+    a, b = xt[..., :32], xt[..., 32:]
+    y = torch.cat([(a * ct) - (b * st), (b * ct) + (a * st)], -1)
+    return y.to(torch.bfloat16).to(torch.float64).numpy()
+
+
+def test_rows_match_the_oracle():
+    """Rotated rows against the oracle's bf16 rotation (the exact value
+    rounded once): within one bf16 ulp everywhere and equal almost
+    everywhere (the kernel rounds its two products and their difference to
+    fp32 first, which lands on the other side of a bf16 midpoint about once
+    in 1e5 elements); in place the same."""
     dev = need_gpu()
     rng = np.random.default_rng(1)
     P, T, H = 5000, 700, 8
@@ -64,12 +78,26 @@ def test_rows_bitwise_with_the_oracle_table():
     y = attn.rope_rows(x.to(dev), torch.from_numpy(pos).to(dev), _as_device_table(c, s, dev))
     torch.cuda.synchronize()
     ref = apply_rope_bf16(f64(x), pos, c, s)
-    np.testing.assert_array_equal(f64(y), ref)
-    # in place
+    d = np.abs(f64(y) - ref)
+    assert (d <= _bf16_ulp(ref)).all() and (d == 0).mean() > 0.999
     xd = x.to(dev)
     attn.rope_rows(xd, torch.from_numpy(pos).to(dev), _as_device_table(c, s, dev), out=xd)
     torch.cuda.synchronize()
-    np.testing.assert_array_equal(f64(xd), ref)
+    assert torch.equal(xd, y)
+
+
+def test_rows_follow_the_kernel_recipe():
+    """Self-consistency of the kernel (not oracle parity): given the same
+    fp32 table, its rotation is exactly its stated fp32 evaluation order."""
+    dev = need_gpu()
+    rng = np.random.default_rng(2)
+    P, T, H = 5000, 700, 8
+    c, s = _oracle_table(P, GPTOSS_LIKE)
+    x = synth.make_dout((T, H, 64), seed=6)
+    pos = rng.integers(0, P, T).astype(np.int32)
+    y = attn.rope_rows(x.to(dev), torch.from_numpy(pos).to(dev), _as_device_table(c, s, dev))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(f64(y), _kernel_rotation_recipe(f64(x), pos, c, s))
 
 
 SMALL = [(1, 200, 8, 1), (2, 333, 16, 2), (1, 130, 6, 2), (1, 77, 1, 1)]
@@ -108,27 +136,43 @@ def test_fwd_rope_identity_table_is_fwd():
 
 
 @pytest.mark.parametrize("window", [128, 0])
-def test_fwd_rope_workload_sampled_rows(window):
+def test_fwd_rope_workload_whole(window):
     """B=4, S=4096, 64q/8kv with a YaRN table (factor 32 over a 4096-token
-    original context), in the launch configuration bench.py times; every
-    rotated key and a sample of output rows against the oracle."""
+    original context), in the launch configuration bench.py times: every
+    rotated key, output and lse element against the oracle (per batch and KV
+    group on the host's cores), into NaN-filled buffers."""
     dev = need_gpu()
     case = synth.config_inputs("c1_b4_s4096_h64x8")
     print(f"fwd_rope workload W={window}", flush=True)
-    B, S, Hq, _ = case.q.shape
+    B, S, Hq, D = case.q.shape
+    Hkv = case.k.shape[2]
+    G = Hq // Hkv
     tab = attn.rope_table(S, **GPTOSS_LIKE)
     q, k, v, sk = (t.to(dev) for t in (case.q, case.k, case.v, case.sinks))
-    out, lse, k_rot = attn.fwd_rope(q, k, v, sk, tab, window, case.scale)
+    out = nan_like((B, S, Hq, D), torch.bfloat16, dev)
+    lse = nan_like((B, Hq, S), torch.float32, dev)
+    k_rot = nan_like((B, S, Hkv, D), torch.bfloat16, dev)
+    attn.fwd_rope(q, k, v, sk, tab, window, case.scale, out=out, lse=lse, k_rot=k_rot)
     torch.cuda.synchronize()
+    for t in (out, lse, k_rot):
+        assert torch.isfinite(t.float()).all()
     c, s = _oracle_table(S, GPTOSS_LIKE)
-    rng = np.random.default_rng(S + window)
-    rows = np.array(sorted(set(range(0, 8)) | {127, 128, 2047, 4095} | set(rng.integers(0, S, 12).tolist())))
-    ro, rl, rk = ref_fwd_rope(f64(case.q), f64(case.k), f64(case.v), f64(case.sinks), window, case.scale, c, s,
-                              rows=rows, heads=list(range(0, Hq, 4)))
-    ri = torch.from_numpy(rows).to(dev)
-    check_out_lse(f64(out[:, ri]), f64(lse[:, :, ri]), ro[:, rows], rl[:, :, rows], f"fwd_rope C1 W={window}")
+    qo, ko, vo, so = f64(case.q), f64(case.k), f64(case.v), f64(case.sinks)
+    tasks = [(b, g) for b in range(B) for g in range(Hkv)]
+
+    def one(t):
+        b, g = t
+        hs = slice(g * G, (g + 1) * G)
+        return ref_fwd_rope(qo[b:b + 1, :, hs], ko[b:b + 1, :, g:g + 1], vo[b:b + 1, :, g:g + 1], so[hs], window,
+                            case.scale, c, s)
+
+    ro, rl, rk = np.zeros((B, S, Hq, D)), np.zeros((B, Hq, S)), np.zeros((B, S, Hkv, D))
+    for (b, g), (o, l, kr) in zip(tasks, oracle_map(one, tasks)):
+        hs = slice(g * G, (g + 1) * G)
+        ro[b, :, hs], rl[b, hs], rk[b, :, g] = o[0], l[0], kr[0, :, 0]
+    check_out_lse(f64(out), f64(lse), ro, rl, f"fwd_rope B4 S4096 W={window}")
     d = np.abs(f64(k_rot) - rk)
-    assert (d <= _bf16_ulp(rk)).all()
+    assert (d <= _bf16_ulp(rk)).all() and (d == 0).mean() > 0.999
 
 
 @pytest.mark.parametrize("window", [0, 128])
@@ -210,29 +254,40 @@ def test_bwd_rope_small(shape, window):
 
 
 @pytest.mark.parametrize("window", [128, 0])
-def test_bwd_rope_workload_group(window):
+def test_bwd_rope_workload_whole(window):
     """The training shape (B=4, S=4096, 64q/8kv) with the YaRN table, in the
-    configuration bench.py times; every gradient of KV group 0 (query heads
-    0..7, all batches) against the oracle."""
-    from _util import GRAD_REL_L2
+    configuration bench.py times: every gradient element of all eight KV
+    groups against the oracle, into NaN-filled gradient buffers."""
     dev = need_gpu()
     case, dout = synth.config_inputs("c3_bwd_b4_s4096_h64x8")
     print(f"bwd_rope workload W={window}", flush=True)
-    S = case.q.shape[1]
+    B, S, Hq, D = case.q.shape
+    Hkv = case.k.shape[2]
+    G = Hq // Hkv
     tab = attn.rope_table(S, **GPTOSS_LIKE)
     q, k, v, sk = (t.to(dev) for t in (case.q, case.k, case.v, case.sinks))
     out, lse, k_rot = attn.fwd_rope(q, k, v, sk, tab, window, case.scale)
-    grads = attn.bwd_rope(q, k_rot, v, sk, tab, out, lse, dout.to(dev), window, case.scale)
+    grads = attn.bwd_rope(q, k_rot, v, sk, tab, out, lse, dout.to(dev), window, case.scale,
+                          grads=nan_grads(q, k, v, Hq))
     torch.cuda.synchronize()
     for t in grads:
         assert torch.isfinite(t.float()).all()
     c, s = _oracle_table(S, GPTOSS_LIKE)
-    heads = list(range(8))
-    ref = ref_bwd_rope(f64(case.q), f64(case.k), f64(case.v), f64(case.sinks), f64(dout), window, case.scale, c, s,
-                       heads=heads)
-    errs = _rel_errs(grads, ref, heads=heads, kv_heads=[0])
-    print(errs, flush=True)
-    assert all(e <= GRAD_REL_L2 for e in errs.values()), errs
+    qo, ko, vo, so, do = f64(case.q), f64(case.k), f64(case.v), f64(case.sinks), f64(dout)
+    tasks = [(b, g) for b in range(B) for g in range(Hkv)]
+
+    def one(t):
+        b, g = t
+        hs = slice(g * G, (g + 1) * G)
+        return ref_bwd_rope(qo[b:b + 1, :, hs], ko[b:b + 1, :, g:g + 1], vo[b:b + 1, :, g:g + 1], so[hs],
+                            do[b:b + 1, :, hs], window, case.scale, c, s)
+
+    rdq, rdk, rdv, rds = np.zeros(qo.shape), np.zeros(ko.shape), np.zeros(vo.shape), np.zeros(Hq)
+    for (b, g), (gq, gk, gv, gs) in zip(tasks, oracle_map(one, tasks)):
+        hs = slice(g * G, (g + 1) * G)
+        rdq[b, :, hs], rdk[b, :, g], rdv[b, :, g] = gq[0], gk[0, :, 0], gv[0, :, 0]
+        rds[hs] += gs
+    check_grads_by_group([f64(t) for t in grads], (rdq, rdk, rdv, rds), Hkv, f"bwd_rope B4 S4096 W={window}")
 
 
 def test_autograd_rope_matches_entry_points():

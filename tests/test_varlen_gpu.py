@@ -14,7 +14,8 @@ import attention_attn_fwd_amd as attn
 from attention_attn_fwd_amd import synth
 from oracle import ref_bwd_varlen, ref_fwd_varlen
 
-from _util import GRAD_REL_L2, check_out_lse, f64, need_gpu, rel_l2, seed_of
+from _util import (GRAD_REL_L2, check_grads_by_group, check_out_lse, f64, nan_grads, need_gpu, oracle_map, rel_l2,
+                   seed_of)
 
 pytestmark = pytest.mark.gpu
 
@@ -142,29 +143,55 @@ def test_varlen_no_document_rows():
 
 
 @pytest.mark.parametrize("window", [128, 0])
-def test_varlen_workload_sampled_documents(window):
+def test_varlen_workload_whole(window):
     """The packed-document workload bench.py times (16384 tokens in
     documents of U{1..4096} tokens, 64q/8kv heads), in the same launch
-    configuration; the oracle computes the forward of the shortest, the
-    longest and one more document over all heads, and the backward of every
-    document for KV group 0 (query heads 0..7, dsinks included)."""
+    configuration: every output, lse and gradient element of every document
+    and KV group against the oracle (run per document and KV group on the
+    host's cores), into NaN-filled gradient buffers."""
     dev = need_gpu()
     case, dout = synth.varlen_workload()
     cu = case.cu_seqlens.numpy()
-    lens = np.diff(cu)
-    docs = sorted({int(np.argmin(lens)), int(np.argmax(lens)), len(lens) // 2})
-    print(f"varlen workload W={window} docs={docs} lens={lens[docs].tolist()}", flush=True)
+    T, Hq, D = case.q.shape
+    Hkv = case.k.shape[1]
+    G = Hq // Hkv
+    print(f"varlen workload W={window} docs={len(cu) - 1}", flush=True)
+    assert _inside(cu, T).all()  # the documents tile the token rows
     out, lse = _fwd(case, window, dev)
     assert torch.isfinite(out.float()).all() and torch.isfinite(lse).all()
-    ro, rl = ref_fwd_varlen(f64(case.q), f64(case.k), f64(case.v), cu, f64(case.sinks), window, case.scale,
-                            docs=docs)
-    sel = ~np.isnan(rl[0])
-    check_out_lse(f64(out)[sel], f64(lse)[:, sel], ro[sel], rl[:, sel], f"varlen workload W={window}")
-    grads = _bwd(case, out, lse, dout, window, dev)
+    q, k, v, sk, do = f64(case.q), f64(case.k), f64(case.v), f64(case.sinks), f64(dout)
+    tasks = [(b, c) for b in range(len(cu) - 1) for c in range(Hkv) if cu[b + 1] > cu[b]]
+
+    def fwd_one(t):
+        b, c = t
+        a, e, hs = int(cu[b]), int(cu[b + 1]), slice(c * G, (c + 1) * G)
+        return ref_fwd_varlen(q[a:e, hs], k[a:e, c:c + 1], v[a:e, c:c + 1], np.array([0, e - a]), sk[hs], window,
+                              case.scale)
+
+    ro, rl = np.full((T, Hq, D), np.nan), np.full((Hq, T), np.nan)
+    for (b, c), (o, l) in zip(tasks, oracle_map(fwd_one, tasks)):
+        a, e, hs = int(cu[b]), int(cu[b + 1]), slice(c * G, (c + 1) * G)
+        ro[a:e, hs], rl[hs, a:e] = o, l
+    check_out_lse(f64(out), f64(lse), ro, rl, f"varlen workload W={window}")
+
+    q_, k_, v_, cu_, s_ = _dev(case, dev)
+    grads = attn.bwd_varlen(q_, k_, v_, cu_, s_, out, lse, dout.to(dev), case.max_seqlen, window, case.scale,
+                            grads=nan_grads(q_, k_, v_, Hq))
+    torch.cuda.synchronize()
     for t in grads:
         assert torch.isfinite(t.float()).all()
-    heads = list(range(8))
-    ref = ref_bwd_varlen(f64(case.q), f64(case.k), f64(case.v), cu, f64(case.sinks), f64(dout), window,
-                         case.scale, heads=heads)
-    _check_grads(grads, ref, _inside(cu, case.q.shape[0]), f"varlen workload bwd W={window}", heads=heads,
-                 kv_heads=[0])
+
+    def bwd_one(t):
+        b, c = t
+        a, e, hs = int(cu[b]), int(cu[b + 1]), slice(c * G, (c + 1) * G)
+        return ref_bwd_varlen(q[a:e, hs], k[a:e, c:c + 1], v[a:e, c:c + 1], np.array([0, e - a]), sk[hs],
+                              do[a:e, hs], window, case.scale)
+
+    rdq, rdk, rdv, rds = np.zeros(q.shape), np.zeros(k.shape), np.zeros(v.shape), np.zeros(Hq)
+    for (b, c), (gq, gk, gv, gs) in zip(tasks, oracle_map(bwd_one, tasks)):
+        a, e, hs = int(cu[b]), int(cu[b + 1]), slice(c * G, (c + 1) * G)
+        rdq[a:e, hs], rdk[a:e, c], rdv[a:e, c] = gq, gk[:, 0], gv[:, 0]
+        rds[hs] += gs
+    got = [f64(t) for t in grads]
+    check_grads_by_group([got[0][None], got[1][None], got[2][None], got[3]],
+                         [rdq[None], rdk[None], rdv[None], rds], Hkv, f"varlen workload bwd W={window}")
