@@ -28,7 +28,7 @@ from . import _lib
 from ._lib import AttnError
 
 __all__ = ["fwd", "bwd", "decode", "decode_paged", "fwd_varlen", "bwd_varlen", "bwd_workspace_size",
-           "bwd_varlen_workspace_size", "decode_workspace_size", "rope_table", "rope_rows", "fwd_rope", "decode_rope",
+           "bwd_varlen_workspace_size", "decode_workspace_size", "decode_workspace", "rope_table", "rope_rows", "fwd_rope", "decode_rope",
            "bwd_rope", "bwd_rope_workspace_size",
            "AttnError", "abi_version"]
 
@@ -159,6 +159,13 @@ def _decode_outputs(out, lse, q):
 
 def decode_workspace_size(N, Hq, Hkv, D=64, max_seqlen=1, window=0):
     return int(_lib.load().gptoss_attn_decode_workspace_size(N, Hq, Hkv, D, max_seqlen, int(window)))
+
+
+def decode_workspace(N, Hq, Hkv, max_seqlen, window=0, D=64, device=None):
+    """A decode workspace for these sizes (reusable by later calls on one
+    stream with the same or smaller sizes)."""
+    need = decode_workspace_size(N, Hq, Hkv, D, max_seqlen, window)
+    return torch.empty(max(need, 1), dtype=torch.uint8, device=device or torch.device("cuda"))
 
 
 def decode(q, k_cache, v_cache, cu_seqlens, sinks, max_seqlen, window=0, scale=None, out=None, lse=None,

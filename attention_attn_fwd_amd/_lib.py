@@ -36,11 +36,13 @@ class AttnError(RuntimeError):
 
 
 def load(path=None):
-    """Load (once) and return the ctypes library handle."""
+    """Load (once) and return the ctypes library handle.  GPTOSS_ATTN_LIBRARY,
+    when set, names another build of the same ABI to load instead (the CPU
+    tests use it for a sanitizer build of the host layer)."""
     global _lib
     if _lib is not None and path is None:
         return _lib
-    path = path or LIB_PATH
+    path = path or os.environ.get("GPTOSS_ATTN_LIBRARY") or LIB_PATH
     if not os.path.exists(path):
         raise RuntimeError(f"HIP library {path} is not built; run "
                            "`python -m attention_attn_fwd_amd.build` first")
@@ -86,7 +88,7 @@ def load(path=None):
     lib.gptoss_attn_bwd_rope.restype = c_int
     lib.gptoss_attn_bwd_rope.argtypes = [c_void_p] * 5 + [c_int] + [c_void_p] * 3 + [c_int] * 6 + [c_float] + \
         [c_void_p] * 5 + [c_size_t, c_void_p]
-    if path == LIB_PATH:
+    if path in (LIB_PATH, os.environ.get("GPTOSS_ATTN_LIBRARY")):
         _lib = lib
     return lib
 

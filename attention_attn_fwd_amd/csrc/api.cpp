@@ -4,7 +4,7 @@
 // plus a per-thread message.
 #include "gptoss_attn.h"
 
-#include <hip/hip_runtime.h>
+#include <hip/hip_runtime_api.h>
 
 #include <atomic>
 #include <cmath>

@@ -152,7 +152,7 @@ bwd_dkdv_kernel(BwdParams p, int n_kt) {
     // K is multiplied by c = scale * log2(e) once here (and rounded to bf16),
     // so that S' = Q (c K)^T is the score in log2 units; with the
     // accumulator started at -lse * log2(e), P = exp2(S') needs no further
-    // arithmetic.  (The rounding of c K perturbs P by ~2^-9 relative, far
+    // arithmetic.  (The rounding of c K perturbs P by up to 2^-8 relative, far
     // inside the gradients' tolerance; dK uses Q and dS, not K.)
     const size_t kv_stride = (size_t)p.Hkv * kHeadDim;
     bf16x8 kb[4], vb[4];
@@ -651,16 +651,6 @@ bwd_dq_kernel(BwdParams p, int n_qt, int pos_per_block) {
 
 }  // namespace
 
-// Workspace: {lse * log2(e), Dvec} per row, then (256-byte aligned) one
-// dsink term per row.
-static size_t ld_region_bytes(long long total_rows, int Hq) {
-    return ((size_t)total_rows * Hq * sizeof(float2) + 255) / 256 * 256;
-}
-
-size_t bwd_workspace_bytes(long long total_rows, int Hq) {
-    return ld_region_bytes(total_rows, Hq) + (size_t)total_rows * Hq * sizeof(float);
-}
-
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
     BwdParams p;
     p.q = a.q;
@@ -675,7 +665,7 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
     p.dv = a.dv;
     p.dsinks = a.dsinks;
     p.ld = static_cast<float2*>(a.workspace);
-    p.dsterm = reinterpret_cast<float*>(static_cast<char*>(a.workspace) + ld_region_bytes(a.T, a.Hq));
+    p.dsterm = reinterpret_cast<float*>(static_cast<char*>(a.workspace) + bwd_ld_region_bytes(a.T, a.Hq));
     p.cu = a.cu;
     p.rope = a.rope;
     p.q_rot = a.q_rot;

@@ -127,33 +127,42 @@ __device__ __forceinline__ bf16x8 tile_read_tr8(const uint4* tile, int r0, int c
 // register can alias a load still in flight, which costs a full wait.)
 __device__ __forceinline__ size_t row_off(int row, uint32_t stride) { return (size_t)(uint32_t)row * stride; }
 
+// Nearest bf16 (8 significant bits, ties to even) of an fp64 value, as the
+// 16-bit pattern: the fp64 significand is rounded at its 8th bit by integer
+// addition on the bit pattern (a carry moves into the exponent as it
+// should), and the result, exact in fp32, gives its top half.
+__device__ __forceinline__ uint32_t bf16_bits_of(double d) {
+    uint64_t b = (uint64_t)__double_as_longlong(d);
+    b += ((1ull << 44) - 1) + ((b >> 45) & 1);
+    b &= ~((1ull << 45) - 1);
+    return __float_as_uint((float)__longlong_as_double((long long)b)) >> 16;
+}
+
 // Rotary embedding of 8 element pairs: a holds elements i .. i+7 and b their
 // partners i+32 .. i+39 (half-split pairing of a 64-wide head), cs the
 // (cos, sin) pairs of i .. i+7 as four float4 {c_i, s_i, c_{i+1}, s_{i+1}}.
 //   a' = a c - b s,  b' = b c + a s            (the rotation R)
 // or, with transpose, the adjoint R^T that carries gradients back:
 //   a' = a c + b s,  b' = b c - a s
-// Each product and the sum are rounded once to fp32 (no fused multiply-add),
-// then the results to bf16 (nearest even).
+// Each result is the exact value rounded once to bf16 (nearest even): with
+// bf16 a, b (8 significant bits) and fp32 c, s (24 bits) every product is
+// exact in fp64 (32 bits), the fused multiply-add rounds the difference
+// once to fp64, and that value is rounded to bf16.  The fp64 rounding is
+// exact unless the two products' exponents differ by more than 21, and can
+// change the bf16 result only if it lands exactly on a bf16 midpoint.
 __device__ __forceinline__ void rope8(uint4& a, uint4& b, const float4 (&cs)[4], bool transpose = false) {
-#pragma clang fp contract(off)
     const uint32_t aw[4] = {a.x, a.y, a.z, a.w}, bw[4] = {b.x, b.y, b.z, b.w};
     uint32_t ra[4], rb[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-        const float a0 = __uint_as_float(aw[u] << 16), a1 = __uint_as_float(aw[u] & 0xffff0000u);
-        const float b0 = __uint_as_float(bw[u] << 16), b1 = __uint_as_float(bw[u] & 0xffff0000u);
-        const float c0 = cs[u].x, c1 = cs[u].z;
-        const float s0 = transpose ? -cs[u].y : cs[u].y, s1 = transpose ? -cs[u].w : cs[u].w;
-        const float ya0 = a0 * c0 - b0 * s0, ya1 = a1 * c1 - b1 * s1;
-        const float yb0 = b0 * c0 + a0 * s0, yb1 = b1 * c1 + a1 * s1;
-        bf16x2 pa, pb;
-        pa[0] = (__bf16)ya0;
-        pa[1] = (__bf16)ya1;
-        pb[0] = (__bf16)yb0;
-        pb[1] = (__bf16)yb1;
-        ra[u] = __builtin_bit_cast(uint32_t, pa);
-        rb[u] = __builtin_bit_cast(uint32_t, pb);
+        const double a0 = bf16_lo(aw[u]), a1 = bf16_hi(aw[u]);
+        const double b0 = bf16_lo(bw[u]), b1 = bf16_hi(bw[u]);
+        const double c0 = cs[u].x, c1 = cs[u].z;
+        const double s0 = transpose ? -cs[u].y : cs[u].y, s1 = transpose ? -cs[u].w : cs[u].w;
+        const double ya0 = fma(a0, c0, -(b0 * s0)), ya1 = fma(a1, c1, -(b1 * s1));
+        const double yb0 = fma(b0, c0, a0 * s0), yb1 = fma(b1, c1, a1 * s1);
+        ra[u] = bf16_bits_of(ya0) | (bf16_bits_of(ya1) << 16);
+        rb[u] = bf16_bits_of(yb0) | (bf16_bits_of(yb1) << 16);
     }
     a = make_uint4(ra[0], ra[1], ra[2], ra[3]);
     b = make_uint4(rb[0], rb[1], rb[2], rb[3]);

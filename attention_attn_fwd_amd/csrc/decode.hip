@@ -36,13 +36,10 @@
 namespace gptoss {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kWaves = 4;         // KV heads per workgroup, one per wave
-constexpr int kTileKeys = 64;     // keys per wave step
-constexpr int kPartStride = 68;   // floats per partial: O[64], m, l, pad
-// Workgroups the chunking aims for: one per CU.  Cutting the 128 x 1024
-// workload finer (512 or more workgroups, merged afterwards) measured slower.
-constexpr long long kTargetWorkgroups = 256;
+constexpr int kWaves = kDecodeKvPerBlock;  // KV heads per workgroup, one per wave
+constexpr int kThreads = 64 * kWaves;
+constexpr int kTileKeys = kDecodeKeyTile;  // keys per wave step
+constexpr int kPartStride = kDecodePartStride;
 
 
 struct DecParams {
@@ -386,33 +383,7 @@ decode_merge_kernel(DecParams p) {
     if (lane == 0) p.lse[(size_t)n * p.Hq + head] = (mtot + fast_log2(l)) * kLn2;
 }
 
-// Chunking plan: about one workgroup per CU over the whole grid.  A sequence
-// is cut into chunks only when there are too few (sequence, KV-head group)
-// pairs to fill the chip; every chunk but the last per sequence costs a
-// partial write and read plus the merge launch, which on the 128 x 1024
-// workload cost more than they gain.
-struct ChunkPlan { int keys, n; };
-ChunkPlan chunk_plan(int N, int Hkv, int G, int max_seqlen, int window) {
-    // 64-bit throughout: max_seqlen may be up to 2^30 (the entry points
-    // refuse more), and the rounding below must not wrap
-    const long long vis = window > 0 ? std::min<long long>(max_seqlen, window) : (long long)max_seqlen;
-    const long long groups = (long long)N * ((Hkv + kWaves - 1) / kWaves) * ((G + 31) / 32);
-    const long long want = std::max(1LL, (kTargetWorkgroups + groups - 1) / groups);
-    const long long max_chunks = std::max(1LL, (vis + kTileKeys - 1) / kTileKeys);
-    const long long n = std::min(want, max_chunks);
-    long long keys = (vis + n - 1) / n;
-    keys = std::max<long long>(kTileKeys, (keys + kTileKeys - 1) / kTileKeys * kTileKeys);
-    const long long chunks = std::max(1LL, (vis + keys - 1) / keys);
-    return ChunkPlan{(int)keys, (int)chunks};
-}
-
 }  // namespace
-
-size_t decode_workspace_bytes(int N, int Hq, int Hkv, int max_seqlen, int window) {
-    const ChunkPlan cp = chunk_plan(N, Hkv, Hq / Hkv, max_seqlen, window);
-    if (cp.n <= 1) return 0;
-    return (size_t)N * Hq * cp.n * kPartStride * sizeof(float);
-}
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
     DecParams p;
@@ -429,12 +400,13 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
     p.G = a.Hq / a.Hkv;
     p.window = a.window;
     p.max_seqlen = a.max_seqlen;
-    const ChunkPlan cp = chunk_plan(a.N, a.Hkv, p.G, a.max_seqlen, a.window);
+    const DecodePlan cp = decode_plan(a.N, a.Hq, a.Hkv, a.max_seqlen, a.window);
     // every visible key of the longest allowed sequence lies in some chunk
     const long long vis = a.window > 0 ? std::min(a.max_seqlen, a.window) : a.max_seqlen;
-    if (cp.keys < kTileKeys || (long long)cp.keys * cp.n < vis) return hipErrorInvalidValue;
-    p.n_splits = cp.n;
-    p.chunk_keys = cp.keys;
+    if (cp.chunk_keys < kTileKeys || (long long)cp.chunk_keys * cp.n_splits < vis) return hipErrorInvalidValue;
+    if (cp.n_splits > 1 && a.workspace == nullptr) return hipErrorInvalidValue;
+    p.n_splits = cp.n_splits;
+    p.chunk_keys = cp.chunk_keys;
     p.n_hblk = (p.G + 31) / 32;
     p.c = a.scale * kLog2e;
     p.bt = a.block_table;

@@ -73,7 +73,7 @@ constexpr float kRescaleBound = 4096.0f;
 // p = exp2(s * c - m) for the 32 scores of one column held by this lane
 // (two 32-key blocks), packed into the bf16 B operands of the four 16-key
 // P.V steps; returns the fp32 sum of the unrounded values (summing the bf16
-// values would cost lse up to 2^-9 relative when one key dominates).
+// values would cost lse up to 2^-8 relative when one key dominates).
 __device__ __forceinline__ float exp_pack(const f32x16& s0, const f32x16& s1, float c, float m, bf16x8* pb,
                                           int stride) {
     float la = 0.0f, lb = 0.0f;

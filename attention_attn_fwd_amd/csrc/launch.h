@@ -2,7 +2,7 @@
 // Arguments are validated by the caller; launchers only plan grids and launch.
 #pragma once
 
-#include <hip/hip_runtime.h>
+#include <hip/hip_runtime_api.h>
 #include <stddef.h>
 #include <stdint.h>
 
@@ -66,9 +66,25 @@ struct DecodeArgs {
 
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
 
+// Backward workspace: {lse * log2(e), Dvec} per (token row, head) as float2,
+// then (256-byte aligned) one fp32 dsink term per (head, token row).
+size_t bwd_ld_region_bytes(long long total_rows, int Hq);
 size_t bwd_workspace_bytes(long long total_rows, int Hq);
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream);
 
+// Decode split plan (host side, no device access).  A split workgroup
+// covers kDecodeKvPerBlock KV heads (one wave each) of one sequence's chunk
+// of chunk_keys visible keys (a multiple of kDecodeKeyTile); a sequence has
+// at most n_splits chunks.  With more than one chunk the workspace holds one
+// partial of kDecodePartStride floats per (sequence, query head, chunk).
+constexpr int kDecodeKvPerBlock = 4;
+constexpr int kDecodeKeyTile = 64;
+constexpr int kDecodePartStride = 68;  // O[64], m, l, pad
+struct DecodePlan {
+    int chunk_keys, n_splits;
+    size_t workspace_bytes;
+};
+DecodePlan decode_plan(int N, int Hq, int Hkv, int max_seqlen, int window);
 size_t decode_workspace_bytes(int N, int Hq, int Hkv, int max_seqlen, int window);
 
 hipError_t launch_rope_table(float2* tab, int P, double base, double factor, double orig_ctx, double alpha,

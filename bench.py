@@ -142,8 +142,7 @@ def main():
             dec_out={w: (torch.empty_like(dec.q, device=dev), torch.empty(N, Hq, device=dev)) for w in WINDOWS}))
     q, k = sets[0]["q"], sets[0]["k"]
     bws = torch.empty(attn.bwd_workspace_size(B, S, Hq, Hkv, D, 0), dtype=torch.uint8, device=dev)
-    dws = torch.empty(max(1, attn.decode_workspace_size(N, Hq, Hkv, D, dec.max_seqlen, 0)),
-                      dtype=torch.uint8, device=dev)
+    dws = attn.decode_workspace(N, Hq, Hkv, dec.max_seqlen, 0, device=dev)
 
     def fwd(w, i=0):
         x = sets[i % NSETS]

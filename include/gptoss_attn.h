@@ -123,8 +123,10 @@ gptoss_status gptoss_attn_bwd(const void* q, const void* k, const void* v,
  *               caller error whose keys beyond max_seqlen are ignored.
  *   out         bf16 [N, Hq, D]   written;  lse fp32 [N, Hq] written.
  *               An empty sequence (L_n = 0) gives out = 0, lse = sinks[h].
+ *   max_seqlen  at most 2^30 (INVALID_ARGUMENT above).
  *   workspace   at least gptoss_attn_decode_workspace_size() bytes,
- *               256-byte aligned (split partials); contents on entry ignored.
+ *               256-byte aligned (split partials; 0 bytes: may be NULL);
+ *               contents on entry ignored.
  */
 size_t gptoss_attn_decode_workspace_size(int N, int Hq, int Hkv, int D, int max_seqlen,
                                          int window);
@@ -236,8 +238,8 @@ gptoss_status gptoss_attn_bwd_varlen(const void* q, const void* k, const void* v
  * Element i of a q or k row at position p is rotated with element i + 32:
  *   y_i = x_i c - x_{i+32} s,  y_{i+32} = x_{i+32} c + x_i s,
  *   c = m cos(p h_i), s = m sin(p h_i)  (fp32, from the table below);
- * each product and the sum are rounded once to fp32 and the result to bf16
- * (nearest even): the attention consumes bf16 q and k.
+ * y is the exact value of that expression (bf16 x, fp32 c and s) rounded
+ * once to bf16, nearest even: the attention consumes bf16 q and k.
  *
  * gptoss_attn_rope_table: fills table, fp32 [positions][32][2] = (c, s),
  *   evaluated in fp64.  Requires D == 64, positions >= 1, base > 1,

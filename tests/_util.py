@@ -25,20 +25,23 @@ def f64(t):
     return t.detach().to("cpu", torch.float64).numpy()
 
 
-def check_out_lse(out, lse, ref_out, ref_lse, what=""):
+def check_out_lse(out, lse, ref_out, ref_lse, what="", ref_abs=None):
     """out/ref_out [..., D] and lse/ref_lse arrays; NaN entries of the
-    reference (rows the oracle did not compute) are ignored."""
+    reference (rows the oracle did not compute) are ignored.  ref_abs, when
+    given, is sum_j P_ij |v_j| per output element (the oracle's forward of
+    |v|), which bounds what the rounding of P to bf16 can cost (out_bar);
+    without it |ref_out| stands in, a smaller and so stricter bound."""
     out, lse = np.asarray(out), np.asarray(lse)
     sel = ~np.isnan(ref_lse)
     assert sel.any(), "nothing to compare"
     osel = ~np.isnan(ref_out)
     d_out = np.abs(out[osel] - ref_out[osel])
     d_lse = np.abs(lse[sel] - ref_lse[sel])
-    bar = out_bar(ref_out[osel])
+    bar = out_bar(ref_out[osel], None if ref_abs is None else np.asarray(ref_abs)[osel])
     wide = int((bar > OUT_MAX_ABS).sum())
     msg = (f"{what}: out max {d_out.max():.3e} mean {d_out.mean():.3e} (worst vs its bar "
-           f"{(d_out / bar).max():.3f}; {wide} of {bar.size} elements above |out| = 4 carry the "
-           f"rounding-widened bar); lse max {d_lse.max():.3e}")
+           f"{(d_out / bar).max():.3f}; {wide} of {bar.size} elements carry the rounding-derived bar above "
+           f"1e-2); lse max {d_lse.max():.3e}")
     print(msg, flush=True)
     assert np.isfinite(out[osel]).all() and np.isfinite(lse[sel]).all(), msg
     assert (d_out <= bar).all(), msg
@@ -53,13 +56,19 @@ def bf16_ulp(x):
     return np.exp2(e - 7)
 
 
-def out_bar(ref):
-    """Per-element bar of the bf16 output: OUT_MAX_ABS wherever that is
-    attainable, else half a bf16 ulp of the exact value (the cost of rounding
-    it to bf16 at all) plus 1e-3 of fp32 accumulation slack.  Half an ulp
-    exceeds 9e-3 only from |out| = 4 on (0.0156 there), e.g. a window-1 row
-    whose output is one value row."""
-    return np.maximum(OUT_MAX_ABS, 0.5 * bf16_ulp(ref) + 1e-3)
+def out_bar(ref, ref_abs=None):
+    """Per-element bar of the bf16 output: OUT_MAX_ABS wherever a bf16 MFMA
+    path can attain it, else the error its arithmetic admits.  The P.V
+    product consumes probabilities rounded to bf16 (8 significant bits), each
+    off by up to 2^-8 of itself, which moves out_i by at most
+    2^-8 sum_j P_ij |v_j| (ref_abs; |ref| when not given); the result is
+    rounded to bf16 (half an ulp of |out| <= |ref| (1 + 2^-7)); 1e-3 covers
+    the fp32 accumulation.  This exceeds 1e-2 only where sum_j P_ij |v_j| is
+    above about 1.3 (a row dominated by one key with a large value, e.g. a
+    window-1 row)."""
+    ref = np.abs(ref)
+    a = ref if ref_abs is None else np.maximum(np.abs(ref_abs), ref)
+    return np.maximum(OUT_MAX_ABS, 2.0 ** -8 * a + 0.5 * bf16_ulp(ref * (1 + 2.0 ** -7)) + 1e-3)
 
 
 def rel_l2(x, ref):

@@ -163,8 +163,11 @@ def test_decode_split_count_invariance(workload, window):
     """The result must not depend on how a sequence's keys are cut into
     chunks: the same inputs decoded under the chunk plans of max_seqlen =
     the longest sequence, 4x and 64x it (the plan follows max_seqlen and the
-    number of sequences) match the oracle each, and agree with one another
-    within one bf16 ulp (out) and 2e-5 (lse)."""
+    number of sequences) each match the oracle, and agree with one another
+    within 3e-3 (max) and 3e-4 (mean) on out and 2e-5 on lse.  (Plans do
+    differ beyond one bf16 ulp: each chunk rounds its probabilities to bf16
+    against its own running maximum, an error of the size the oracle bar
+    already admits for each plan, ~1e-3 here.)"""
     dev = need_gpu()
     if workload == "n128_l1024":
         case = synth.config_inputs("c4_decode_n128_l1024_h64x8")
@@ -183,6 +186,27 @@ def test_decode_split_count_invariance(workload, window):
         results.append((f64(out), f64(lse)))
     (o0, l0) = results[0]
     for o, l in results[1:]:
-        ulp = np.exp2(np.floor(np.log2(np.maximum(np.maximum(np.abs(o), np.abs(o0)), 2.0 ** -126))) - 7)
-        assert (np.abs(o - o0) <= ulp).all()
+        d = np.abs(o - o0)
+        print(f"plans differ: out max {d.max():.2e} mean {d.mean():.2e}, lse max {np.abs(l - l0).max():.2e}")
+        assert d.max() <= 3e-3 and d.mean() <= 3e-4
         assert np.abs(l - l0).max() <= 2e-5
+
+
+def test_decode_reuses_one_workspace():
+    """One workspace serves a run of calls with different plans, windows and
+    sequence counts: every call matches the one with a fresh workspace bit
+    for bit (the kernels are deterministic and overwrite what they read)."""
+    dev = need_gpu()
+    cases = [synth.make_decode(128, 64, 8, max_len=1024, seed=61),
+             synth.make_decode(8, 64, 8, max_len=1024, seed=62),
+             synth.make_decode(3, 64, 8, lengths=[3000, 1, 2049], seed=63)]
+    need = max(attn.decode_workspace_size(c.q.shape[0], 64, 8, 64, c.max_seqlen, w) for c in cases for w in (0, 128))
+    ws = torch.full((need,), 0xA5, dtype=torch.uint8, device=dev)  # stale bytes must not matter
+    for rep in range(2):
+        for ci, case in enumerate(cases):
+            for window in (0, 128):
+                t = [x.to(dev) for x in (case.q, case.k_cache, case.v_cache, case.cu_seqlens, case.sinks)]
+                ref = attn.decode(*t, case.max_seqlen, window, case.scale)
+                got = attn.decode(*t, case.max_seqlen, window, case.scale, workspace=ws)
+                torch.cuda.synchronize()
+                assert torch.equal(got[0], ref[0]) and torch.equal(got[1], ref[1]), (rep, ci, window)
