@@ -27,7 +27,7 @@ import torch
 from . import _lib
 from ._lib import AttnError
 
-__all__ = ["fwd", "bwd", "decode", "decode_paged", "fwd_varlen", "bwd_varlen", "bwd_workspace_size",
+__all__ = ["fwd", "bwd", "decode", "decode_noalloc", "decode_paged", "fwd_varlen", "bwd_varlen", "bwd_workspace_size",
            "bwd_varlen_workspace_size", "decode_workspace_size", "decode_workspace", "rope_table", "rope_rows", "fwd_rope", "decode_rope",
            "bwd_rope", "bwd_rope_workspace_size",
            "AttnError", "abi_version"]
@@ -191,6 +191,31 @@ def decode(q, k_cache, v_cache, cu_seqlens, sinks, max_seqlen, window=0, scale=N
                                 sinks.data_ptr(), N, Hq, Hkv, D, int(max_seqlen), int(window), scale,
                                 out.data_ptr(), lse.data_ptr(), workspace.data_ptr(), ws_bytes,
                                 _stream(q.device))
+    _lib.check(st, lib)
+    return out, lse
+
+
+def decode_noalloc(q, k_cache, v_cache, cu_seqlens, sinks, max_seqlen, window=0, scale=None, out=None, lse=None):
+    """decode() through gptoss_attn_decode_noalloc: no workspace; the split
+    partials live in the library's per-GPU scratch array (calls that may
+    overlap on one GPU race on it)."""
+    _need(q, "q", torch.bfloat16, 3)
+    _need(k_cache, "k_cache", torch.bfloat16, 3)
+    _need(v_cache, "v_cache", torch.bfloat16, 3)
+    _need(cu_seqlens, "cu_seqlens", torch.int32, 1)
+    _need(sinks, "sinks", torch.float32, 1)
+    N, Hq, D = q.shape
+    Hkv = k_cache.shape[1]
+    if (v_cache.shape != k_cache.shape or k_cache.shape[2] != D or cu_seqlens.shape != (N + 1,)
+            or sinks.shape != (Hq,)):
+        raise ValueError("shape mismatch among decode inputs")
+    _on(q.device, (k_cache, "k_cache"), (v_cache, "v_cache"), (cu_seqlens, "cu_seqlens"), (sinks, "sinks"))
+    scale = (1.0 / D ** 0.5) if scale is None else float(scale)
+    out, lse = _decode_outputs(out, lse, q)
+    lib = _lib.load()
+    st = lib.gptoss_attn_decode_noalloc(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), cu_seqlens.data_ptr(),
+                                        sinks.data_ptr(), N, Hq, Hkv, D, int(max_seqlen), int(window), scale,
+                                        out.data_ptr(), lse.data_ptr(), _stream(q.device))
     _lib.check(st, lib)
     return out, lse
 

@@ -306,10 +306,12 @@ size_t gptoss_attn_decode_workspace_size(int N, int Hq, int Hkv, int D, int max_
     return gptoss::decode_workspace_bytes(N, Hq, Hkv, max_seqlen, window);
 }
 
-gptoss_status gptoss_attn_decode(const void* q, const void* k_cache, const void* v_cache, const int* cu_seqlens,
-                                 const float* sinks, int N, int Hq, int Hkv, int D, int max_seqlen, int window,
-                                 float softmax_scale, void* out, float* lse, void* workspace,
-                                 size_t workspace_bytes, void* stream) {
+// The packed-cache decode, with the caller's workspace or (noalloc) the
+// library's per-GPU scratch array.
+static gptoss_status decode_entry(const void* q, const void* k_cache, const void* v_cache, const int* cu_seqlens,
+                                  const float* sinks, int N, int Hq, int Hkv, int D, int max_seqlen, int window,
+                                  float softmax_scale, void* out, float* lse, bool noalloc, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
     if (N < 0) return fail(GPTOSS_ERR_INVALID_ARGUMENT, "N (%d) must be >= 0", N);
     gptoss_status st = check_decode_seqlen(max_seqlen);
     if (st != GPTOSS_OK) return st;
@@ -326,9 +328,17 @@ gptoss_status gptoss_attn_decode(const void* q, const void* k_cache, const void*
     CHECK_PTR(out, 16);
     CHECK_PTR(lse, 4);
     const size_t need = gptoss::decode_workspace_bytes(N, Hq, Hkv, max_seqlen, window);
-    if (workspace_bytes < need)
-        return fail(GPTOSS_ERR_INVALID_ARGUMENT, "workspace_bytes %zu < required %zu", workspace_bytes, need);
-    if (need > 0) CHECK_PTR(workspace, 256);
+    if (noalloc) {
+        if (need > gptoss::kDecodeNoAllocScratchBytes)
+            return fail(GPTOSS_ERR_INVALID_ARGUMENT,
+                        "this decode needs %zu bytes of split partials; the no-allocation entry point holds %zu "
+                        "(use gptoss_attn_decode with a workspace)",
+                        need, gptoss::kDecodeNoAllocScratchBytes);
+    } else {
+        if (workspace_bytes < need)
+            return fail(GPTOSS_ERR_INVALID_ARGUMENT, "workspace_bytes %zu < required %zu", workspace_bytes, need);
+        if (need > 0) CHECK_PTR(workspace, 256);
+    }
     st = check_device();
     if (st != GPTOSS_OK) return st;
     gptoss::DecodeArgs a;
@@ -341,7 +351,7 @@ gptoss_status gptoss_attn_decode(const void* q, const void* k_cache, const void*
     a.sinks = sinks;
     a.out = static_cast<uint16_t*>(out);
     a.lse = lse;
-    a.workspace = workspace;
+    a.workspace = noalloc ? nullptr : workspace;
     a.N = N;
     a.Hq = Hq;
     a.Hkv = Hkv;
@@ -352,7 +362,25 @@ gptoss_status gptoss_attn_decode(const void* q, const void* k_cache, const void*
     a.ring_tokens = 0;
     a.rope = nullptr;
     a.scale = softmax_scale;
-    return launched(gptoss::launch_decode(a, static_cast<hipStream_t>(stream)), "decode");
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    if (noalloc) return launched(gptoss::launch_decode_noalloc(a, s), "decode (no allocation)");
+    return launched(gptoss::launch_decode(a, s), "decode");
+}
+
+gptoss_status gptoss_attn_decode(const void* q, const void* k_cache, const void* v_cache, const int* cu_seqlens,
+                                 const float* sinks, int N, int Hq, int Hkv, int D, int max_seqlen, int window,
+                                 float softmax_scale, void* out, float* lse, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+    return decode_entry(q, k_cache, v_cache, cu_seqlens, sinks, N, Hq, Hkv, D, max_seqlen, window, softmax_scale,
+                        out, lse, false, workspace, workspace_bytes, stream);
+}
+
+gptoss_status gptoss_attn_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                         const int* cu_seqlens, const float* sinks, int N, int Hq, int Hkv, int D,
+                                         int max_seqlen, int window, float softmax_scale, void* out, float* lse,
+                                         void* stream) {
+    return decode_entry(q, k_cache, v_cache, cu_seqlens, sinks, N, Hq, Hkv, D, max_seqlen, window, softmax_scale,
+                        out, lse, true, nullptr, 0, stream);
 }
 
 static bool is_pow2(long long x) { return x > 0 && (x & (x - 1)) == 0; }

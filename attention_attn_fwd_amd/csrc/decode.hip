@@ -32,6 +32,7 @@
 #include "launch.h"
 
 #include <algorithm>
+#include <mutex>
 
 namespace gptoss {
 namespace {
@@ -429,6 +430,55 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
     else
         hipLaunchKernelGGL(decode_merge_kernel, dim3(a.Hq, a.N), dim3(256), 0, stream, p);
     return hipGetLastError();
+}
+
+
+// ---------------------------------------------------------------------------
+// Decode without a caller workspace, for callers that cannot allocate device
+// memory (code under graph capture, tight serving loops).  The split
+// partials live in this file-scope array instead: every GPU holds its own
+// copy for the life of the process, and every call on that GPU shares it
+// (calls that may overlap on one GPU race on it).  The kernels overwrite
+// every partial they read in the same call, so nothing needs clearing.
+namespace {
+
+static __device__ __align__(256) float scratch[kDecodeNoAllocScratchBytes / sizeof(float)];
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices] = {};
+
+// The device address of this GPU's scratch array, looked up once per device
+// with that device current (the array's name in host code is only a
+// stand-in for the symbol, not an address a kernel may use).
+hipError_t scratch_for_current_device(void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return hipSuccess;
+}
+
+}  // namespace
+
+hipError_t launch_decode_noalloc(const DecodeArgs& args, hipStream_t stream) {
+    const DecodePlan cp = decode_plan(args.N, args.Hq, args.Hkv, args.max_seqlen, args.window);
+    if (cp.workspace_bytes > kDecodeNoAllocScratchBytes) return hipErrorInvalidValue;  // checked by the caller
+    DecodeArgs a = args;
+    a.workspace = nullptr;
+    if (cp.workspace_bytes > 0) {
+        const hipError_t e = scratch_for_current_device(&a.workspace);
+        if (e != hipSuccess) return e;
+    }
+    return launch_decode(a, stream);
 }
 
 }  // namespace gptoss

@@ -93,4 +93,10 @@ hipError_t launch_rope_rows(const uint16_t* x, uint16_t* y, const int* positions
                             long long rows, int H, int S, bool transpose, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 
+// Decode with the split partials in a library-owned device array of
+// kDecodeNoAllocScratchBytes per GPU instead of a.workspace (ignored);
+// plans needing more must be refused by the caller.
+constexpr size_t kDecodeNoAllocScratchBytes = 4u << 20;
+hipError_t launch_decode_noalloc(const DecodeArgs& a, hipStream_t stream);
+
 }  // namespace gptoss

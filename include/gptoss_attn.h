@@ -137,6 +137,24 @@ gptoss_status gptoss_attn_decode(const void* q, const void* k_cache, const void*
                                  void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * gptoss_attn_decode without a workspace, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation.  Same operation, arguments (minus the workspace)
+ * and outputs as gptoss_attn_decode.  The split partials live in a
+ * library-owned array of 4 MiB in each GPU's memory (held until the process
+ * ends; its address is looked up once per device); a call whose plan needs
+ * more (gptoss_attn_decode_workspace_size() > 4 MiB) returns
+ * GPTOSS_ERR_INVALID_ARGUMENT before any HIP call.  The call allocates nothing.  Every call on a
+ * GPU shares that GPU's array: calls that may overlap on one GPU (different
+ * streams, concurrent host threads) race and must be serialised by the
+ * caller.
+ */
+gptoss_status gptoss_attn_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                         const int* cu_seqlens, const float* sinks, int N, int Hq,
+                                         int Hkv, int D, int max_seqlen, int window,
+                                         float softmax_scale, void* out, float* lse, void* stream);
+
+/*
  * Decode against a paged KV cache (HF blog "Tricks from OpenAI gpt-oss YOU
  * can use with transformers", items "Continuous Batching & Paged Attention"
  * and "Dynamic Sliding Window Layer & Cache": the cache lives in fixed-size

@@ -9,6 +9,7 @@ namespace gptoss {
 hipError_t launch_fwd(const FwdArgs&, hipStream_t) { return hipErrorNoDevice; }
 hipError_t launch_bwd(const BwdArgs&, hipStream_t) { return hipErrorNoDevice; }
 hipError_t launch_decode(const DecodeArgs&, hipStream_t) { return hipErrorNoDevice; }
+hipError_t launch_decode_noalloc(const DecodeArgs&, hipStream_t) { return hipErrorNoDevice; }
 hipError_t launch_rope_table(float2*, int, double, double, double, double, double, hipStream_t) {
     return hipErrorNoDevice;
 }

@@ -363,3 +363,20 @@ def test_missing_library_fails_loudly(tmp_path):
     from attention_attn_fwd_amd import _lib
     with pytest.raises(RuntimeError, match="is not built"):
         _lib.load(str(tmp_path / "libgptoss_attn.so"))
+
+
+def test_decode_noalloc_refuses_plans_beyond_its_scratch(lib):
+    """The no-allocation decode holds 4 MiB of split partials per GPU; a call
+    whose plan needs more is refused on the host, before any HIP call."""
+    N, Hq, Hkv, L = 129, 128, 4, 1024
+    need = lib.gptoss_attn_decode_workspace_size(N, Hq, Hkv, 64, L, 0)
+    assert need > 4 << 20
+    st = lib.gptoss_attn_decode_noalloc(P, P, P, P, P, N, Hq, Hkv, 64, L, 0, 0.125, P, P, None)
+    assert st == 1 and "no-allocation" in lib.gptoss_attn_last_error().decode()
+    # the same argument checks as gptoss_attn_decode
+    st = lib.gptoss_attn_decode_noalloc(P, P, P, None, P, 2, 64, 8, 64, 1024, 0, 0.125, P, P, None)
+    assert st == 1 and "cu_seqlens is NULL" in lib.gptoss_attn_last_error().decode()
+    st = lib.gptoss_attn_decode_noalloc(P, P, P, P, P, 2, 64, 8, 64, 2 ** 31 - 1, 0, 0.125, P, P, None)
+    assert st == 1 and "exceeds 2^30" in lib.gptoss_attn_last_error().decode()
+    assert lib.gptoss_attn_decode_noalloc(None, None, None, None, None, 0, 64, 8, 64, 1, 0, 0.125, None, None,
+                                          None) == 0
