@@ -42,7 +42,13 @@
 namespace gptoss {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 256;  // dsink kernel
+#ifndef GPTOSS_DKDV_WAVES
+#define GPTOSS_DKDV_WAVES 4
+#endif
+#ifndef GPTOSS_DQ_WAVES
+#define GPTOSS_DQ_WAVES 4
+#endif
 
 struct BwdParams {
     const uint16_t* q;
@@ -104,8 +110,12 @@ bwd_dsink_kernel(BwdParams p) {
 
 // ---------------------------------------------------------------------------
 // dkdv: key-outer.
-constexpr int kKeysPerBlock = 128;
+constexpr int kKvWaves = GPTOSS_DKDV_WAVES;
+constexpr int kKvThreads = 64 * kKvWaves;
+constexpr int kKeysPerBlock = 32 * kKvWaves;  // 32 keys per wave
 constexpr int kColsPerStep = 64;
+constexpr int kKvStRows = kKvThreads / 8;            // columns staged per pass
+constexpr int kKvStPasses = kColsPerStep / kKvStRows;
 
 __device__ __forceinline__ void dkdv_coords(const BwdParams& p, int n_kt, int bid, int& grp, int& kt) {
     const int n_groups = p.B * p.Hkv;
@@ -125,7 +135,7 @@ __device__ __forceinline__ void dkdv_coords(const BwdParams& p, int n_kt, int bi
     }
 }
 
-__global__ void __launch_bounds__(kThreads, 2)
+__global__ void __launch_bounds__(kKvThreads, 2)
 bwd_dkdv_kernel(BwdParams p, int n_kt) {
     __shared__ uint4 sQ[2][kTileUnits];
     __shared__ uint4 sO[2][kTileUnits];
@@ -187,7 +197,7 @@ bwd_dkdv_kernel(BwdParams p, int n_kt) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) dkacc[db][r] = dvacc[db][r] = 0.0f;
 
-    // staging: thread stages rows (columns) st_row and st_row + 32 (unit
+    // staging: thread stages rows (columns) st_row + kKvStRows j (unit
     // st_unit) of each 64-column step, and threads 0..63 the per-column
     // scalars.  A column c maps to (pos_lo + c / G, kvh * G + c % G); when G
     // divides 64 a step advances every staged column by 64 / G positions.
@@ -198,32 +208,31 @@ bwd_dkdv_kernel(BwdParams p, int n_kt) {
     const uint16_t* qcol_base = qsrc + ((size_t)sr.row0 * Hq + (size_t)kvh * G) * kHeadDim + 8 * st_unit;
     const uint16_t* ocol_base = p.dout + ((size_t)sr.row0 * Hq + (size_t)kvh * G) * kHeadDim + 8 * st_unit;
     const float2* ld_base = p.ld + (size_t)sr.row0 * Hq + (size_t)kvh * G;
-    uint4 rq[2], ro[2];
+    uint4 rq[kKvStPasses], ro[kKvStPasses];
     float2 rld = make_float2(INFINITY, 0.0f);
     int rpos = 0x3fffffff;
     // per-thread column offsets within a step (constant across steps when G divides 64)
-    int st_pos[2], st_head[2];
+    int st_pos[kKvStPasses], st_head[kKvStPasses];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        st_pos[j] = (st_row + 32 * j) / G;
-        st_head[j] = (st_row + 32 * j) % G;
+    for (int j = 0; j < kKvStPasses; ++j) {
+        st_pos[j] = (st_row + kKvStRows * j) / G;
+        st_head[j] = (st_row + kKvStRows * j) % G;
     }
     const int ld_pos = tid / G, ld_head = tid % G;
     const int pos_per_step = kColsPerStep / G;
     auto load_step = [&](int st) {
         const int c0 = st * kColsPerStep;
+        // columns past the last one re-read the last column's rows: their
+        // lse is staged as +inf below, so P = dS = 0 for them
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int c = c0 + st_row + 32 * j;
-            rq[j] = make_uint4(0, 0, 0, 0);
-            ro[j] = make_uint4(0, 0, 0, 0);
-            if (c < n_cols) {
-                const int pos = pos_lo + (g64 ? st * pos_per_step + st_pos[j] : c / G);
-                const int head = g64 ? st_head[j] : c % G;
-                const size_t off = (size_t)pos * pos_stride + (size_t)head * kHeadDim;
-                rq[j] = ld16(qcol_base + off);
-                ro[j] = ld16(ocol_base + off);
-            }
+        for (int j = 0; j < kKvStPasses; ++j) {
+            const int c = min(c0 + st_row + kKvStRows * j, n_cols - 1);
+            const bool fast = g64 && c0 + kColsPerStep <= n_cols;
+            const int pos = pos_lo + (fast ? st * pos_per_step + st_pos[j] : c / G);
+            const int head = fast ? st_head[j] : c % G;
+            const size_t off = (size_t)pos * pos_stride + (size_t)head * kHeadDim;
+            rq[j] = ld16(qcol_base + off);
+            ro[j] = ld16(ocol_base + off);
         }
         if (tid < kColsPerStep) {
             const int c = c0 + tid;
@@ -238,8 +247,8 @@ bwd_dkdv_kernel(BwdParams p, int n_kt) {
     };
     auto store_step = [&](int buf) {
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int row = st_row + 32 * j;
+        for (int j = 0; j < kKvStPasses; ++j) {
+            const int row = st_row + kKvStRows * j;
             sQ[buf][tile_unit(row, st_unit)] = rq[j];
             sO[buf][tile_unit(row, st_unit)] = ro[j];
         }
@@ -387,8 +396,12 @@ bwd_dkdv_kernel(BwdParams p, int n_kt) {
 
 // ---------------------------------------------------------------------------
 // dq: query-outer; 4 waves x 32 columns per workgroup, 64-key tiles.
-constexpr int kDqCols = 128;
+constexpr int kDqWaves = GPTOSS_DQ_WAVES;
+constexpr int kDqThreads = 64 * kDqWaves;
+constexpr int kDqCols = 32 * kDqWaves;  // 32 columns per wave
 constexpr int kBk = 64;
+constexpr int kDqStRows = kDqThreads / 8;   // key rows staged per pass
+constexpr int kDqStPasses = kBk / kDqStRows;
 
 __device__ __forceinline__ void dq_coords(const BwdParams& p, int n_qt, int bid, int& grp, int& qt) {
     const int n_groups = p.B * p.Hkv;
@@ -404,7 +417,7 @@ __device__ __forceinline__ void dq_coords(const BwdParams& p, int n_qt, int bid,
     qt = n_qt - 1 - qt;  // latest positions (most keys) first
 }
 
-__global__ void __launch_bounds__(kThreads, 2)
+__global__ void __launch_bounds__(kDqThreads, 2)
 bwd_dq_kernel(BwdParams p, int n_qt, int pos_per_block) {
     __shared__ uint4 sK[2][kTileUnits];
     __shared__ uint4 sV[2][kTileUnits];
@@ -441,24 +454,22 @@ bwd_dq_kernel(BwdParams p, int n_qt, int pos_per_block) {
     const uint16_t* kbase = p.k + ((size_t)sr.row0 * p.Hkv + kvh) * kHeadDim;
     const uint16_t* vbase = p.v + ((size_t)sr.row0 * p.Hkv + kvh) * kHeadDim;
     const int st_row = tid >> 3, st_unit = tid & 7;
-    uint4 rk[2], rv[2];
+    uint4 rk[kDqStPasses], rv[kDqStPasses];
+    // rows past the sequence end re-read its last row: no query row sees
+    // them, and the tile holding them is an edge tile, whose scores are masked
     auto load_tile = [&](int t) {
         const int kt0 = t * kBk;
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int key = kt0 + st_row + 32 * j;
-            rk[j] = make_uint4(0, 0, 0, 0);
-            rv[j] = make_uint4(0, 0, 0, 0);
-            if (key < S) {
-                rk[j] = ld16(kbase + row_off(key, (uint32_t)kv_stride) + 8 * st_unit);
-                rv[j] = ld16(vbase + row_off(key, (uint32_t)kv_stride) + 8 * st_unit);
-            }
+        for (int j = 0; j < kDqStPasses; ++j) {
+            const int key = min(kt0 + st_row + kDqStRows * j, S - 1);
+            rk[j] = ld16(kbase + row_off(key, (uint32_t)kv_stride) + 8 * st_unit);
+            rv[j] = ld16(vbase + row_off(key, (uint32_t)kv_stride) + 8 * st_unit);
         }
     };
     auto store_tile = [&](int buf) {
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int row = st_row + 32 * j;
+        for (int j = 0; j < kDqStPasses; ++j) {
+            const int row = st_row + kDqStRows * j;
             sK[buf][tile_unit(row, st_unit)] = rk[j];
             sV[buf][tile_unit(row, st_unit)] = rv[j];
         }
@@ -684,10 +695,11 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
     const int n_qt = (a.S + ppb - 1) / ppb;
     if ((long long)n_qt * a.B * a.Hkv > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     // dq first: it also stores {lse log2(e), Dvec} per row for dkdv
-    hipLaunchKernelGGL(bwd_dq_kernel, dim3((unsigned)(n_qt * a.B * a.Hkv)), dim3(kThreads), 0, stream, p, n_qt, ppb);
+    hipLaunchKernelGGL(bwd_dq_kernel, dim3((unsigned)(n_qt * a.B * a.Hkv)), dim3(kDqThreads), 0, stream, p, n_qt,
+                       ppb);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(bwd_dkdv_kernel, dim3((unsigned)(n_kt * a.B * a.Hkv)), dim3(kThreads), 0, stream, p, n_kt);
+    hipLaunchKernelGGL(bwd_dkdv_kernel, dim3((unsigned)(n_kt * a.B * a.Hkv)), dim3(kKvThreads), 0, stream, p, n_kt);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(bwd_dsink_kernel, dim3(a.Hq), dim3(kThreads), 0, stream, p);
     return hipGetLastError();

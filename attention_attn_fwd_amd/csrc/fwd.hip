@@ -42,9 +42,15 @@
 namespace gptoss {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kCols = 256;        // columns per workgroup
-constexpr int kBk = 64;           // keys per LDS tile
+#ifndef GPTOSS_FWD_WAVES
+#define GPTOSS_FWD_WAVES 4
+#endif
+constexpr int kWaves = GPTOSS_FWD_WAVES;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kCols = 64 * kWaves;  // columns per workgroup
+constexpr int kBk = 64;             // keys per LDS tile
+constexpr int kStRows = kThreads / 8;       // key rows staged per pass (8 threads per 128-byte row)
+constexpr int kStPasses = kBk / kStRows;    // passes per tile
 
 struct FwdParams {
     const uint16_t* q;
@@ -122,7 +128,7 @@ fwd_kernel(FwdParams p) {
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: the wave's tile tests are scalar
     const int g = lane >> 5;     // slot group / lane half
     const int l32 = lane & 31;
 
@@ -189,10 +195,12 @@ fwd_kernel(FwdParams p) {
     float m_run[2], l_run[2];
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
-        const float sink = col_ok[nb] ? p.sinks[col_head[nb]] : -INFINITY;
+        // (a padding column -- no query row -- starts at m = 0: its scores are
+        // finite and its results are never stored)
+        const float sink = col_ok[nb] ? p.sinks[col_head[nb]] : 0.0f;
         const bool has_sink = sink != -INFINITY;
         m_run[nb] = has_sink ? sink * kLog2e : -INFINITY;
-        l_run[nb] = (has_sink && g == 0) ? 1.0f : 0.0f;
+        l_run[nb] = (has_sink && g == 0 && col_ok[nb]) ? 1.0f : 0.0f;
     }
     f32x16 oacc[2][2];
 #pragma unroll
@@ -211,27 +219,26 @@ fwd_kernel(FwdParams p) {
     const uint32_t kv_row_stride = (uint32_t)p.Hkv * kHeadDim;
     const uint16_t* kbase = p.k + ((size_t)sr.row0 * p.Hkv + kvh) * kHeadDim;
     const uint16_t* vbase = p.v + ((size_t)sr.row0 * p.Hkv + kvh) * kHeadDim;
-    const int st_key = tid >> 3, st_unit = tid & 7;  // rows st_key, st_key + 32; 16-byte unit
-    uint4 kreg[2], vreg[2];
+    const int st_key = tid >> 3, st_unit = tid & 7;  // rows st_key + kStRows j; 16-byte unit
+    uint4 kreg[kStPasses], vreg[kStPasses];
 
+    // Rows past the sequence end re-read its last row: no valid query row can
+    // see them (they lie past every position), and the tile that holds them
+    // is an edge tile, whose scores are masked.
     auto load_tile = [&](int t) {
         const int kt0 = t * kBk;
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int key = kt0 + st_key + 32 * j;
-            kreg[j] = make_uint4(0, 0, 0, 0);
-            vreg[j] = make_uint4(0, 0, 0, 0);
-            if (key < S) {
-                kreg[j] = ld16(kbase + row_off(key, kv_row_stride) + 8 * st_unit);
-                vreg[j] = ld16(vbase + row_off(key, kv_row_stride) + 8 * st_unit);
-            }
+        for (int j = 0; j < kStPasses; ++j) {
+            const int key = min(kt0 + st_key + kStRows * j, S - 1);
+            kreg[j] = ld16(kbase + row_off(key, kv_row_stride) + 8 * st_unit);
+            vreg[j] = ld16(vbase + row_off(key, kv_row_stride) + 8 * st_unit);
         }
     };
     auto store_tile = [&](int buf) {
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            smem[buf][0][tile_unit(st_key + 32 * j, st_unit)] = kreg[j];
-            smem[buf][1][tile_unit(st_key + 32 * j, st_unit)] = vreg[j];
+        for (int j = 0; j < kStPasses; ++j) {
+            smem[buf][0][tile_unit(st_key + kStRows * j, st_unit)] = kreg[j];
+            smem[buf][1][tile_unit(st_key + kStRows * j, st_unit)] = vreg[j];
         }
     };
 
@@ -250,7 +257,13 @@ fwd_kernel(FwdParams p) {
     if (t_begin <= t_end) store_tile(0);
     __syncthreads();
 
-    bool fresh[2] = {true, true};  // row has not seen a key yet
+    // The tile in which each of this lane's rows first sees a key (with W = 0
+    // every row sees key 0, in tile t_begin = 0), and whether any row of the
+    // wave can still sit at m = -inf (a sink of -inf) before that tile.
+    int first_tile[2];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) first_tile[nb] = W > 0 ? max(0, col_pos[nb] - W + 1) / kBk : 0;
+    const bool any_ninf = __any(m_run[0] == -INFINITY || m_run[1] == -INFINITY);
     for (int t = t_begin; t <= t_end; ++t) {
         const int buf = (t - t_begin) & 1;
         const bool has_next = t < t_end;
@@ -308,15 +321,8 @@ fwd_kernel(FwdParams p) {
             // rounding on it).
             bf16x8 pb[4][2];
             float lt[2] = {0.0f, 0.0f};
-            bool first = false;
-#pragma unroll
-            for (int nb = 0; nb < 2; ++nb) {
-                const int pos = col_pos[nb];
-                const bool sees = kt0 <= pos && (W == 0 || kt0 + kBk - 1 > pos - W);
-                first |= fresh[nb] && sees;
-                fresh[nb] = fresh[nb] && !sees;
-            }
-            bool slow = __any(first || m_run[0] == -INFINITY || m_run[1] == -INFINITY);
+            bool slow = W > 0 ? __any(first_tile[0] == t || first_tile[1] == t) : t == t_begin;
+            if (any_ninf) slow = slow || __any(m_run[0] == -INFINITY || m_run[1] == -INFINITY);
             if (!slow) {
                 f32x16 sacc[2][2];
                 scores(sacc);
