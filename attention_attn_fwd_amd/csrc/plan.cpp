@@ -15,6 +15,11 @@ constexpr size_t align256(size_t n) { return (n + 255) / 256 * 256; }
 // and read plus the merge launch, which on the 128 x U{1..1024} workload
 // cost more than they gain.
 constexpr long long kDecodeTargetWorkgroups = 256;
+// Shortest chunk the plan cuts (a multiple of the key tile).  Two tiles:
+// a one-tile chunk saves less than the merge launch it brings (a sliding
+// layer's 128 visible keys decode fastest unsplit).
+constexpr long long kDecodeMinChunkKeys = 2 * kDecodeKeyTile;
+static_assert(kDecodeMinChunkKeys % kDecodeKeyTile == 0, "chunks hold whole key tiles");
 }  // namespace
 
 size_t bwd_ld_region_bytes(long long total_rows, int Hq) {
@@ -33,10 +38,10 @@ DecodePlan decode_plan(int N, int Hq, int Hkv, int max_seqlen, int window) {
     const long long groups =
         (long long)N * ((Hkv + kDecodeKvPerBlock - 1) / kDecodeKvPerBlock) * ((G + 31) / 32);
     const long long want = std::max(1LL, (kDecodeTargetWorkgroups + groups - 1) / std::max(1LL, groups));
-    const long long max_chunks = std::max(1LL, (vis + kDecodeKeyTile - 1) / kDecodeKeyTile);
+    const long long max_chunks = std::max(1LL, (vis + kDecodeMinChunkKeys - 1) / kDecodeMinChunkKeys);
     const long long n = std::min(want, max_chunks);
     long long keys = (vis + n - 1) / n;
-    keys = std::max<long long>(kDecodeKeyTile, (keys + kDecodeKeyTile - 1) / kDecodeKeyTile * kDecodeKeyTile);
+    keys = std::max<long long>(kDecodeMinChunkKeys, (keys + kDecodeKeyTile - 1) / kDecodeKeyTile * kDecodeKeyTile);
     const long long chunks = std::max(1LL, (vis + keys - 1) / keys);
     DecodePlan p;
     p.chunk_keys = (int)keys;

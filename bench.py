@@ -22,8 +22,8 @@ step through the autograd wrapper, and prefill of packed documents (16384
 tokens in documents of U{1..4096} tokens, same heads; FLOPs over the pairs
 visible inside each document), and prefill and decode with the YaRN rotary
 embedding fused in (the same FLOPs; bytes add the rotated-key write; the
-backward counts the plain backward's bytes), and
-the forward of the small (B=1, S=512, 8q/1kv) and long-context (B=1,
+backward counts the plain backward's bytes), decode of one 65536-key
+sequence (the long-context workload's next token), and the forward of the small (B=1, S=512, 8q/1kv) and long-context (B=1,
 S=65536) workloads.
 """
 
@@ -42,29 +42,37 @@ NSETS = 4                      # input/output buffer sets used in rotation
 ROOT = os.path.dirname(os.path.abspath(__file__))
 
 
-def source_digest():
-    """sha256 over the library sources; measured traffic is only reported
-    while it matches the digest recorded with the counters."""
+# the sources each part's kernels and launch come from (measured traffic of a
+# part stays valid while these files are unchanged)
+PART_SOURCES = {"fwd": ("fwd.hip", "common.h", "launch.h"),
+                "bwd": ("bwd.hip", "common.h", "launch.h", "plan.cpp"),
+                "decode": ("decode.hip", "common.h", "launch.h", "plan.cpp")}
+
+
+def source_digest(part):
+    """sha256 over the library sources of `part` (fwd, bwd or decode, the
+    packed-document parts as their dense kind)."""
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "attention_attn_fwd_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
+    for name in PART_SOURCES[part.replace("varlen_", "")]:
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()
 
 
 def measured_traffic(key):
-    """HBM bytes per launch of `key` from profiles/traffic.json (FETCH_SIZE +
-    WRITE_SIZE, calibrated against a plain copy), or None if absent or taken
-    on different kernel sources."""
+    """HBM bytes per launch of `key` (e.g. "bwd_full") from
+    profiles/traffic.json (FETCH_SIZE + WRITE_SIZE, calibrated against a
+    plain copy), or None if absent or taken on different kernel sources."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     try:
         with open(path) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("source_sha256") != source_digest():
+    part = key.rsplit("_", 1)[0]
+    if t.get("source_sha256", {}).get(part) != source_digest(part):
         return None
     v = t.get("bytes_per_launch", {}).get(key)
     return None if v is None else float(v)
@@ -88,12 +96,19 @@ def parse():
                          "copies 1 GiB once per step, to calibrate HBM byte counters")
     ap.add_argument("--window", type=int, default=None, choices=list(WINDOWS),
                     help="with --only: run that part for this layer's window only")
+    ap.add_argument("--digest-traffic", metavar="DIR", default=None,
+                    help="write profiles/traffic.json from the rocprofv3 FETCH_SIZE / WRITE_SIZE csv runs under DIR "
+                         "(DIR/<part>_<window>_<counter>/run_counter_collection.csv, one run per part, layer and "
+                         "counter, plus DIR/copy_<counter>) and exit; runs no GPU code")
     ap.add_argument("--verbose", action="store_true")
     return ap.parse_args()
 
 
 def main():
     args = parse()
+    if args.digest_traffic:
+        digest_traffic(args.digest_traffic)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the path is "
               "single-GPU by design, see DESIGN.md for how it would shard", file=sys.stderr)
@@ -326,6 +341,28 @@ def main():
         parts[label] = {"ms": round(ms, 4), "gbs": round(gbs, 1), "bound": "hbm",
                         "frac_of_roof": round(gbs / HBM_PEAK_GBS, 4)}
     del pg_sets, rg_sets
+    # decode of the long-context workload's next token: one sequence of
+    # 65536 keys, 64q/8kv, both layers (the full layer's chunk plan cuts the
+    # sequence into 128 chunks of 512 keys and merges their partials)
+    lc = synth.make_decode(1, Hq, Hkv, lengths=[65536], seed=1005)
+    lcu, lsk = lc.cu_seqlens.to(dev), lc.sinks.to(dev)
+    lsets = [(lc.q.to(dev), lc.k_cache.to(dev), lc.v_cache.to(dev), torch.empty(1, Hq, D, dtype=torch.bfloat16,
+              device=dev), torch.empty(1, Hq, device=dev)) for _ in range(NSETS)]
+    lws = attn.decode_workspace(1, Hq, Hkv, lc.max_seqlen, 0, device=dev)
+    for w in WINDOWS:
+        def lfn(i, w=w):
+            lq, lk, lv, lo, ll = lsets[i % NSETS]
+            attn.decode(lq, lk, lv, lcu, lsk, lc.max_seqlen, w, lc.scale, out=lo, lse=ll, workspace=lws)
+        g = capture(lambda: [lfn(i) for i in range(reps)])
+        g.replay()
+        ms = median_replay(g) / reps
+        del g
+        vis = min(65536, w) if w else 65536
+        by = 2 * 2 * vis * Hkv * D + 2 * 2 * Hq * D + 4 * Hq + 4 * Hq + 8
+        gbs = by / (ms * 1e-3) / 1e9
+        parts[f"decode_one65536_{'full' if w == 0 else 'w%d' % w}"] = {
+            "ms": round(ms, 4), "gbs": round(gbs, 1), "bound": "hbm", "frac_of_roof": round(gbs / HBM_PEAK_GBS, 4)}
+    del lsets, lws
     # packed-document prefill (not part of the step): forward and backward
     # per layer, each timed like the parts above
     for w in WINDOWS:
@@ -482,6 +519,65 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
+
+
+PART_KERNELS = {"fwd": ("fwd_kernel",), "varlen_fwd": ("fwd_kernel",),
+                "bwd": ("bwd_dq_kernel", "bwd_dkdv_kernel", "bwd_dsink_kernel"),
+                "varlen_bwd": ("bwd_dq_kernel", "bwd_dkdv_kernel", "bwd_dsink_kernel"),
+                "decode": ("decode_split_kernel", "decode_merge_few_kernel", "decode_merge_kernel")}
+
+
+def read_counter(path, counter):
+    """{kernel: [values per dispatch]} of one rocprofv3 counter csv (KiB)."""
+    import csv
+    import re
+    out = {}
+    with open(path) as f:
+        for row in csv.DictReader(f):
+            if row["Counter_Name"] != counter:
+                continue
+            m = re.search(r"(\w+_kernel)(<[^>]*>)?\(", row["Kernel_Name"])
+            name = m.group(1) if m else row["Kernel_Name"]
+            out.setdefault(name, []).append(float(row["Counter_Value"]))
+    return out
+
+
+def digest_traffic(d):
+    """profiles/traffic.json from counter runs of `bench.py --only <part>
+    --window <w>` (each of the part's kernels averaged over its dispatches),
+    scaled by what the counters read for a plain copy of COPY_BYTES: reads
+    by COPY_BYTES / FETCH_SIZE of the copy, writes by COPY_BYTES /
+    WRITE_SIZE of the copy."""
+    def copy_kib(counter):
+        v = read_counter(os.path.join(d, f"copy_{counter}", "run_counter_collection.csv"), counter)
+        big = [x for vals in v.values() for x in vals if x * 1024 > COPY_BYTES / 8]
+        return sum(big) / len(big)
+    rk, wk = copy_kib("FETCH_SIZE"), copy_kib("WRITE_SIZE")
+    rcal, wcal = COPY_BYTES / (rk * 1024), COPY_BYTES / (wk * 1024)
+    per_launch, per_kernel = {}, {}
+    for part, kernels in PART_KERNELS.items():
+        for w in WINDOWS:
+            key = f"{part}_{'full' if w == 0 else 'w%d' % w}"
+            vals = [read_counter(os.path.join(d, f"{part}_{w}_{c}", "run_counter_collection.csv"), c)
+                    for c in ("FETCH_SIZE", "WRITE_SIZE")]
+            total = 0.0
+            for kname in kernels:
+                if kname not in vals[0]:  # (the forward calls in a backward run are not the part's)
+                    continue
+                r = sum(vals[0][kname]) / len(vals[0][kname]) * 1024 * rcal
+                wb = sum(vals[1][kname]) / len(vals[1][kname]) * 1024 * wcal
+                per_kernel[f"{key}:{kname}"] = [round(r), round(wb)]
+                total += r + wb
+            per_launch[key] = round(total)
+    out = {"source_sha256": {part: source_digest(part) for part in PART_KERNELS},
+           "read_calibration": rcal, "write_calibration": wcal,
+           "calibration": f"plain device copy of {COPY_BYTES} bytes: FETCH_SIZE {rk:.0f} KiB, "
+                          f"WRITE_SIZE {wk:.0f} KiB",
+           "bytes_per_launch": per_launch, "per_kernel_bytes": per_kernel}
+    with open(os.path.join(ROOT, "profiles", "traffic.json"), "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    print(json.dumps(out, indent=1))
 
 
 def capture(fn):

@@ -135,12 +135,14 @@ def test_decode_matches_prefill_last_row():
         assert (lse_d[0] - lse_p[0, :, S - 1]).abs().max().item() <= 1e-3
 
 
-@pytest.mark.parametrize("window", [0, 128])
+@pytest.mark.parametrize("window", [0, 128, 1000])
 @pytest.mark.parametrize("lengths", [[65536], [1024] * 31 + [700], [3000, 1, 64, 2049]],
                          ids=["one_long", "n32", "mixed"])
 def test_decode_chunked(window, lengths):
     """Few (sequence, KV group) pairs: sequences are cut into chunks, each
-    chunk walked by one or two waves per KV head, and merged afterwards."""
+    chunk walked by one wave per KV head, and merged afterwards (window
+    1000: the visible range starts inside the sequence and is cut too;
+    window 128 is decoded unsplit)."""
     dev = need_gpu()
     case = synth.make_decode(len(lengths), 64, 8, lengths=lengths, seed=seed_of(lengths, window))
     print(f"decode chunked n={len(lengths)} max={max(lengths)} W={window}", flush=True)
