@@ -220,17 +220,42 @@ bwd_dkdv_kernel(BwdParams p, int n_kt) {
     }
     const int ld_pos = tid / G, ld_head = tid % G;
     const int pos_per_step = kColsPerStep / G;
+    // Whole steps with G dividing 64 (all but possibly the first one
+    // processed): the rows a thread stages in step st lie st * pos_per_step
+    // positions above its rows of step 0, so their addresses are one
+    // multiply-add from these step-0 addresses.
+    const char* q_row0[kKvStPasses];
+    const char* o_row0[kKvStPasses];
+#pragma unroll
+    for (int j = 0; j < kKvStPasses; ++j) {
+        const size_t off = (size_t)(pos_lo + st_pos[j]) * pos_stride + (size_t)st_head[j] * kHeadDim;
+        q_row0[j] = reinterpret_cast<const char*>(qcol_base + off);
+        o_row0[j] = reinterpret_cast<const char*>(ocol_base + off);
+    }
+    const char* ld_row0 = reinterpret_cast<const char*>(ld_base + (size_t)(pos_lo + ld_pos) * Hq + ld_head);
+    const uint32_t step_bytes = (uint32_t)(pos_per_step * pos_stride * sizeof(uint16_t));  // <= 1 MiB
+    const uint32_t ld_step_bytes = (uint32_t)(pos_per_step * Hq * sizeof(float2));
     auto load_step = [&](int st) {
         const int c0 = st * kColsPerStep;
+        if (g64 && c0 + kColsPerStep <= n_cols) {  // wave-uniform
+            const uint64_t dq = (uint64_t)(uint32_t)st * step_bytes;
+#pragma unroll
+            for (int j = 0; j < kKvStPasses; ++j) {
+                rq[j] = ld16(q_row0[j] + dq);
+                ro[j] = ld16(o_row0[j] + dq);
+            }
+            if (tid < kColsPerStep) {
+                rld = *reinterpret_cast<const float2*>(ld_row0 + (uint64_t)(uint32_t)st * ld_step_bytes);
+                rpos = pos_lo + st * pos_per_step + ld_pos;
+            }
+            return;
+        }
         // columns past the last one re-read the last column's rows: their
         // lse is staged as +inf below, so P = dS = 0 for them
 #pragma unroll
         for (int j = 0; j < kKvStPasses; ++j) {
             const int c = min(c0 + st_row + kKvStRows * j, n_cols - 1);
-            const bool fast = g64 && c0 + kColsPerStep <= n_cols;
-            const int pos = pos_lo + (fast ? st * pos_per_step + st_pos[j] : c / G);
-            const int head = fast ? st_head[j] : c % G;
-            const size_t off = (size_t)pos * pos_stride + (size_t)head * kHeadDim;
+            const size_t off = (size_t)(pos_lo + c / G) * pos_stride + (size_t)(c % G) * kHeadDim;
             rq[j] = ld16(qcol_base + off);
             ro[j] = ld16(ocol_base + off);
         }
@@ -239,8 +264,8 @@ bwd_dkdv_kernel(BwdParams p, int n_kt) {
             rld = make_float2(INFINITY, 0.0f);
             rpos = 0x3fffffff;
             if (c < n_cols) {
-                const int pos = pos_lo + (g64 ? st * pos_per_step + ld_pos : c / G);
-                rld = ld_base[(size_t)pos * Hq + (g64 ? ld_head : c % G)];
+                const int pos = pos_lo + c / G;
+                rld = ld_base[(size_t)pos * Hq + c % G];
                 rpos = pos;
             }
         }
@@ -341,8 +366,10 @@ bwd_dkdv_kernel(BwdParams p, int n_kt) {
         if (has_next) load_step(st - 1);
 
         const int c0 = st * kColsPerStep;
-        const int tp_min = pos_lo + c0 / G;
-        const int tp_max = min(pos_lo + (min(c0 + kColsPerStep, n_cols) - 1) / G, S - 1);
+        const bool whole = g64 && c0 + kColsPerStep <= n_cols;  // no scalar divisions by G then
+        const int tp_min = pos_lo + (whole ? st * pos_per_step : c0 / G);
+        const int tp_max = min(whole ? tp_min + pos_per_step - 1 : pos_lo + (min(c0 + kColsPerStep, n_cols) - 1) / G,
+                               S - 1);
         const bool skip = !wave_active || tp_max < kw0 || (W > 0 && tp_min - kw1 >= W);
         if (!skip) {
             const bool need_mask = !(tp_min >= kw1 && (W == 0 || tp_max - kw0 < W));
