@@ -127,15 +127,27 @@ __device__ __forceinline__ bf16x8 tile_read_tr8(const uint4* tile, int r0, int c
 // register can alias a load still in flight, which costs a full wait.)
 __device__ __forceinline__ size_t row_off(int row, uint32_t stride) { return (size_t)(uint32_t)row * stride; }
 
-// Nearest bf16 (8 significant bits, ties to even) of an fp64 value, as the
-// 16-bit pattern: the fp64 significand is rounded at its 8th bit by integer
-// addition on the bit pattern (a carry moves into the exponent as it
-// should), and the result, exact in fp32, gives its top half.
-__device__ __forceinline__ uint32_t bf16_bits_of(double d) {
-    uint64_t b = (uint64_t)__double_as_longlong(d);
+// Nearest bf16 (8 significant bits, ties to even) of the exact value
+// hi + lo, as the 16-bit pattern, where lo is the exact remainder of an fp64
+// sum hi (|lo| at most half an ulp of hi).  The fp64 significand is rounded
+// at its 8th bit by integer addition on the bit pattern (a carry moves into
+// the exponent as it should); when hi sits exactly on a bf16 midpoint, the
+// sign of lo says on which side the exact value lies.
+__device__ __forceinline__ uint32_t bf16_bits_of(double hi, double lo) {
+    uint64_t b = (uint64_t)__double_as_longlong(hi);
+    if ((b & ((1ull << 45) - 1)) == (1ull << 44) && lo != 0.0)
+        b += ((lo > 0.0) == (hi > 0.0)) ? 1 : ~0ull;  // off the midpoint, towards the exact value
     b += ((1ull << 44) - 1) + ((b >> 45) & 1);
     b &= ~((1ull << 45) - 1);
     return __float_as_uint((float)__longlong_as_double((long long)b)) >> 16;
+}
+
+// x + y as an fp64 value and its exact remainder (Knuth's two-sum).
+__device__ __forceinline__ void two_sum(double x, double y, double& hi, double& lo) {
+#pragma clang fp contract(off)
+    hi = x + y;
+    const double yv = hi - x;
+    lo = (x - (hi - yv)) + (y - yv);
 }
 
 // Rotary embedding of 8 element pairs: a holds elements i .. i+7 and b their
@@ -146,23 +158,31 @@ __device__ __forceinline__ uint32_t bf16_bits_of(double d) {
 //   a' = a c + b s,  b' = b c - a s
 // Each result is the exact value rounded once to bf16 (nearest even): with
 // bf16 a, b (8 significant bits) and fp32 c, s (24 bits) every product is
-// exact in fp64 (32 bits), the fused multiply-add rounds the difference
-// once to fp64, and that value is rounded to bf16.  The fp64 rounding is
-// exact unless the two products' exponents differ by more than 21, and can
-// change the bf16 result only if it lands exactly on a bf16 midpoint.
+// exact in fp64 (32 bits), and the sum of the two products is carried as an
+// fp64 value plus its exact remainder, so the one rounding sees the exact
+// value.
 __device__ __forceinline__ void rope8(uint4& a, uint4& b, const float4 (&cs)[4], bool transpose = false) {
+#pragma clang fp contract(off)
     const uint32_t aw[4] = {a.x, a.y, a.z, a.w}, bw[4] = {b.x, b.y, b.z, b.w};
     uint32_t ra[4], rb[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-        const double a0 = bf16_lo(aw[u]), a1 = bf16_hi(aw[u]);
-        const double b0 = bf16_lo(bw[u]), b1 = bf16_hi(bw[u]);
-        const double c0 = cs[u].x, c1 = cs[u].z;
-        const double s0 = transpose ? -cs[u].y : cs[u].y, s1 = transpose ? -cs[u].w : cs[u].w;
-        const double ya0 = fma(a0, c0, -(b0 * s0)), ya1 = fma(a1, c1, -(b1 * s1));
-        const double yb0 = fma(b0, c0, a0 * s0), yb1 = fma(b1, c1, a1 * s1);
-        ra[u] = bf16_bits_of(ya0) | (bf16_bits_of(ya1) << 16);
-        rb[u] = bf16_bits_of(yb0) | (bf16_bits_of(yb1) << 16);
+        uint32_t ya[2], yb[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const double ax = e ? bf16_hi(aw[u]) : bf16_lo(aw[u]);
+            const double bx = e ? bf16_hi(bw[u]) : bf16_lo(bw[u]);
+            const double c = e ? cs[u].z : cs[u].x;
+            const double sn = e ? cs[u].w : cs[u].y;
+            const double s = transpose ? -sn : sn;
+            double hi, lo;
+            two_sum(ax * c, -(bx * s), hi, lo);
+            ya[e] = bf16_bits_of(hi, lo);
+            two_sum(bx * c, ax * s, hi, lo);
+            yb[e] = bf16_bits_of(hi, lo);
+        }
+        ra[u] = ya[0] | (ya[1] << 16);
+        rb[u] = yb[0] | (yb[1] << 16);
     }
     a = make_uint4(ra[0], ra[1], ra[2], ra[3]);
     b = make_uint4(rb[0], rb[1], rb[2], rb[3]);
