@@ -541,11 +541,28 @@ bwd_dq_kernel(BwdParams p, int n_qt, int pos_per_block) {
             }
         }
         if (col_ok) lse2 = p.lse[sr.lse_base + col_head * sr.lse_hstride + col_pos] * kLog2e;
-        if (rope && col_ok) {
+        if (rope) {
+            bool mid = false;
+            if (col_ok) {
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) rope8(xq[ks], xq[ks + 2], rcs[ks]);
+                for (int ks = 0; ks < 2; ++ks) mid = rope8(xq[ks], xq[ks + 2], rcs[ks]) || mid;
+            }
+            if (__any(mid) && col_ok) {
+                // (rare) an fp64 sum on a bf16 midpoint: reload q (the loads
+                // above are complete, q_rot not yet written) and rotate with
+                // exact remainders
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) *reinterpret_cast<uint4*>(p.q_rot + off + 16 * ks + 8 * g) = xq[ks];
+                for (int ks = 0; ks < 2; ++ks) {
+                    uint4 x0 = ld16(p.q + off + 16 * ks + 8 * g), x1 = ld16(p.q + off + 16 * (ks + 2) + 8 * g);
+                    rope8_exact(x0, x1, rcs[ks]);
+                    xq[ks] = x0;
+                    xq[ks + 2] = x1;
+                }
+            }
+            if (col_ok) {
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks) *reinterpret_cast<uint4*>(p.q_rot + off + 16 * ks + 8 * g) = xq[ks];
+            }
         }
         float dot = 0.0f;
 #pragma unroll

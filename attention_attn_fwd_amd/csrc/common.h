@@ -156,36 +156,59 @@ __device__ __forceinline__ void two_sum(double x, double y, double& hi, double& 
 //   a' = a c - b s,  b' = b c + a s            (the rotation R)
 // or, with transpose, the adjoint R^T that carries gradients back:
 //   a' = a c + b s,  b' = b c - a s
-// Each result is the exact value rounded once to bf16 (nearest even): with
+// Each result is the exact value rounded once to bf16 (nearest even).  With
 // bf16 a, b (8 significant bits) and fp32 c, s (24 bits) every product is
-// exact in fp64 (32 bits), and the sum of the two products is carried as an
-// fp64 value plus its exact remainder, so the one rounding sees the exact
-// value.
-__device__ __forceinline__ void rope8(uint4& a, uint4& b, const float4 (&cs)[4], bool transpose = false) {
+// exact in fp64 (32 bits); rope8 rounds their sum once to fp64 (a fused
+// multiply-add) and that value to bf16, which is the exact value's rounding
+// unless the fp64 value sits exactly on a bf16 midpoint.  rope8 returns
+// true if that happened for some element; the caller then reloads a, b and
+// cs and calls rope8_exact, which carries the sum with its exact remainder
+// (two-sum) so that the remainder decides.  (The remainder is not formed
+// always: its fp64 additions cost more than the rest of the rotation.)
+__device__ __forceinline__ void rope_elem(const uint32_t (&aw)[4], const uint32_t (&bw)[4], const float4 (&cs)[4],
+                                          bool transpose, int k, double& x0, double& x1, double& c, double& s) {
+    const int u = k >> 1, e = k & 1;
+    x0 = e ? bf16_hi(aw[u]) : bf16_lo(aw[u]);
+    x1 = e ? bf16_hi(bw[u]) : bf16_lo(bw[u]);
+    c = e ? cs[u].z : cs[u].x;
+    const double sn = e ? cs[u].w : cs[u].y;
+    s = transpose ? -sn : sn;
+}
+
+__device__ __forceinline__ bool rope8(uint4& a, uint4& b, const float4 (&cs)[4], bool transpose = false) {
+    const uint32_t aw[4] = {a.x, a.y, a.z, a.w}, bw[4] = {b.x, b.y, b.z, b.w};
+    uint32_t w[2][4] = {};
+    bool mid = false;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        double x0, x1, c, s;
+        rope_elem(aw, bw, cs, transpose, k, x0, x1, c, s);
+        const double h0 = fma(x0, c, -(x1 * s)), h1 = fma(x1, c, x0 * s);
+        mid = mid || ((uint64_t)__double_as_longlong(h0) & ((1ull << 45) - 1)) == (1ull << 44) ||
+              ((uint64_t)__double_as_longlong(h1) & ((1ull << 45) - 1)) == (1ull << 44);
+        w[0][k >> 1] |= bf16_bits_of(h0, 0.0) << (16 * (k & 1));
+        w[1][k >> 1] |= bf16_bits_of(h1, 0.0) << (16 * (k & 1));
+    }
+    a = make_uint4(w[0][0], w[0][1], w[0][2], w[0][3]);
+    b = make_uint4(w[1][0], w[1][1], w[1][2], w[1][3]);
+    return mid;
+}
+
+__device__ __forceinline__ void rope8_exact(uint4& a, uint4& b, const float4 (&cs)[4], bool transpose = false) {
 #pragma clang fp contract(off)
     const uint32_t aw[4] = {a.x, a.y, a.z, a.w}, bw[4] = {b.x, b.y, b.z, b.w};
-    uint32_t ra[4], rb[4];
+    uint32_t w[2][4] = {};
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        uint32_t ya[2], yb[2];
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-            const double ax = e ? bf16_hi(aw[u]) : bf16_lo(aw[u]);
-            const double bx = e ? bf16_hi(bw[u]) : bf16_lo(bw[u]);
-            const double c = e ? cs[u].z : cs[u].x;
-            const double sn = e ? cs[u].w : cs[u].y;
-            const double s = transpose ? -sn : sn;
-            double hi, lo;
-            two_sum(ax * c, -(bx * s), hi, lo);
-            ya[e] = bf16_bits_of(hi, lo);
-            two_sum(bx * c, ax * s, hi, lo);
-            yb[e] = bf16_bits_of(hi, lo);
-        }
-        ra[u] = ya[0] | (ya[1] << 16);
-        rb[u] = yb[0] | (yb[1] << 16);
+    for (int k = 0; k < 8; ++k) {
+        double x0, x1, c, s, h, lo;
+        rope_elem(aw, bw, cs, transpose, k, x0, x1, c, s);
+        two_sum(x0 * c, -(x1 * s), h, lo);
+        w[0][k >> 1] |= bf16_bits_of(h, lo) << (16 * (k & 1));
+        two_sum(x1 * c, x0 * s, h, lo);
+        w[1][k >> 1] |= bf16_bits_of(h, lo) << (16 * (k & 1));
     }
-    a = make_uint4(ra[0], ra[1], ra[2], ra[3]);
-    b = make_uint4(rb[0], rb[1], rb[2], rb[3]);
+    a = make_uint4(w[0][0], w[0][1], w[0][2], w[0][3]);
+    b = make_uint4(w[1][0], w[1][1], w[1][2], w[1][3]);
 }
 
 // The adjoint rotation R^T on fp32 values: a[j] holds element i + j and b[j]

@@ -181,8 +181,23 @@ decode_split_kernel(DecParams p) {
         load_tile(0);  // n_tiles >= 1 here
     }
     if (p.rope != nullptr) {
+        bool mid = false;
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) rope8(qraw[ks], qraw[ks + 2], rcs[ks]);
+        for (int ks = 0; ks < 2; ++ks) mid = rope8(qraw[ks], qraw[ks + 2], rcs[ks]) || mid;
+        if (__any(mid) && col_ok) {
+            // (rare) an fp64 sum on a bf16 midpoint: reload q and its table
+            // entries and rotate with exact remainders
+            const uint16_t* qrow = p.q + ((size_t)n * p.Hq + head) * kHeadDim;
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                uint4 x0 = ld16(qrow + 16 * ks + 8 * g), x1 = ld16(qrow + 16 * (ks + 2) + 8 * g);
+                float4 cs[4];
+                load_rope8(p.rope, L - 1, 16 * ks + 8 * g, cs);
+                rope8_exact(x0, x1, cs);
+                qraw[ks] = x0;
+                qraw[ks + 2] = x1;
+            }
+        }
     }
     bf16x8 qf[4];
 #pragma unroll

@@ -257,10 +257,29 @@ fwd_kernel(FwdParams p) {
 
     if (t_begin <= t_end) load_tile(t_begin);
     if (rope) {
+        bool mid = false;
 #pragma unroll
         for (int nb = 0; nb < kNb; ++nb)
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) rope8(qraw[nb][ks], qraw[nb][ks + 2], rcs[nb][ks]);
+            for (int ks = 0; ks < 2; ++ks) mid = rope8(qraw[nb][ks], qraw[nb][ks + 2], rcs[nb][ks]) || mid;
+        if (__any(mid)) {
+            // (rare) an fp64 sum on a bf16 midpoint: reload q and its table
+            // entries and rotate with exact remainders
+#pragma unroll
+            for (int nb = 0; nb < kNb; ++nb) {
+                if (!col_ok[nb]) continue;
+                const uint16_t* qrow = p.q + ((size_t)(sr.row0 + col_pos[nb]) * p.Hq + col_head[nb]) * kHeadDim;
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) {
+                    uint4 x0 = ld16(qrow + 16 * ks + 8 * g), x1 = ld16(qrow + 16 * (ks + 2) + 8 * g);
+                    float4 cs[4];
+                    load_rope8(p.rope, col_pos[nb], 16 * ks + 8 * g, cs);
+                    rope8_exact(x0, x1, cs);
+                    qraw[nb][ks] = x0;
+                    qraw[nb][ks + 2] = x1;
+                }
+            }
+        }
     }
     bf16x8 qf[kNb][4];
 #pragma unroll

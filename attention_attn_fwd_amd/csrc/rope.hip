@@ -58,7 +58,13 @@ __global__ void __launch_bounds__(256) rope_rows_kernel(const uint16_t* x, uint1
     uint4 a = ld16(src), b = ld16(src + kPairs);
     float4 cs[4];
     load_rope8(tab, pos, 8 * o, cs);
-    rope8(a, b, cs, transpose != 0);
+    if (__any(rope8(a, b, cs, transpose != 0))) {
+        // (rare) an fp64 sum on a bf16 midpoint: rotate again from the
+        // inputs with exact remainders (before any store: y may be x)
+        a = ld16(src);
+        b = ld16(src + kPairs);
+        rope8_exact(a, b, cs, transpose != 0);
+    }
     uint16_t* dst = y + row * kHeadDim + 8 * o;
     st16(dst, a);
     st16(dst + kPairs, b);

@@ -74,6 +74,82 @@ def test_rows_match_the_oracle():
     assert torch.equal(xd, y)
 
 
+def test_rows_on_bf16_midpoints():
+    """Rotations whose fp64 sum lands exactly on a bf16 midpoint although
+    the exact value does not: a = +-2^e with cos = 1 + 2^-8 puts a c on the
+    midpoint above a, and a sine of ~2^-62 moves the exact value off it by
+    far less than an fp64 ulp.  The exact value's side of the midpoint
+    decides (the oracle's rounding), not ties-to-even; both the rotation and
+    its adjoint, bit for bit."""
+    dev = need_gpu()
+    rng = np.random.default_rng(11)
+    P, T, H = 64, 512, 4
+    c = np.full((P, 32), 1.0 + 2.0 ** -8, dtype=np.float32)
+    s = (rng.choice([-1.0, 1.0], (P, 32)) * 2.0 ** -62 * rng.integers(1, 9, (P, 32))).astype(np.float32)
+    a = rng.choice([-1.0, 1.0], (T, H, 32)) * np.exp2(rng.integers(-6, 7, (T, H, 32)))
+    b = f64(synth.make_dout((T, H, 32), seed=6))
+    x = torch.from_numpy(np.concatenate([a, b], axis=-1)).to(torch.bfloat16)
+    pos = rng.integers(0, P, T).astype(np.int32)
+    pd, tab = torch.from_numpy(pos).to(dev), _as_device_table(c, s, dev)
+    y = attn.rope_rows(x.to(dev), pd, tab)
+    yt = attn.rope_rows(x.to(dev), pd, tab, transpose=True)
+    torch.cuda.synchronize()
+    want = apply_rope_bf16(f64(x), pos, c, s)
+    # the case is real: ties-to-even on the fp64 sum would round every a c - b s down to |a|
+    assert (np.abs(want[..., :32]) > np.abs(a)).mean() > 0.3
+    np.testing.assert_array_equal(f64(y), want)
+    np.testing.assert_array_equal(f64(yt), apply_rope_bf16(f64(x), pos, c, -s))
+
+
+def _midpoint_case(B, S, Hq, Hkv, seed):
+    """q and k whose first-half elements are +-2^e (e in -3..0) and a table
+    with cos = 1 + 2^-8 and sines of ~2^-62: most rotated first-half
+    elements have an fp64 sum exactly on a bf16 midpoint."""
+    rng = np.random.default_rng(seed)
+    case = synth.make_prefill(B, S, Hq, Hkv, seed=seed)
+    def pow2_half(t):
+        x = f64(t)
+        x[..., :32] = rng.choice([-1.0, 1.0], x[..., :32].shape) * np.exp2(rng.integers(-3, 1, x[..., :32].shape))
+        return torch.from_numpy(x).to(torch.bfloat16)
+    c = np.full((S, 32), 1.0 + 2.0 ** -8, dtype=np.float32)
+    s = (rng.choice([-1.0, 1.0], (S, 32)) * 2.0 ** -62 * rng.integers(1, 9, (S, 32))).astype(np.float32)
+    return pow2_half(case.q), pow2_half(case.k), case.v, case.sinks, case.scale, c, s
+
+
+@pytest.mark.parametrize("window", [0, 128])
+def test_fused_rotations_on_bf16_midpoints(window):
+    """The fused rotations of q (forward, decode, backward) take their exact
+    path when an fp64 sum lands on a bf16 midpoint: the backward's rotated q
+    (the first part of its workspace) equals the oracle's bit for bit, and
+    the forward and decode results match the oracle over the same rotation."""
+    dev = need_gpu()
+    B, S, Hq, Hkv = 1, 200, 8, 1
+    q, k, v, sk, scale, c, s = _midpoint_case(B, S, Hq, Hkv, seed=17 + window)
+    tab = _as_device_table(c, s, dev)
+    qd, kd, vd, skd = (t.to(dev) for t in (q, k, v, sk))
+    out, lse, k_rot = attn.fwd_rope(qd, kd, vd, skd, tab, window, scale)
+    dout = synth.make_dout(tuple(q.shape), seed=23)
+    ws = torch.empty(attn.bwd_rope_workspace_size(B, S, Hq, Hkv), dtype=torch.uint8, device=dev)
+    attn.bwd_rope(qd, k_rot, vd, skd, tab, out, lse, dout.to(dev), window, scale, workspace=ws)
+    torch.cuda.synchronize()
+    ro, rl, rk = ref_fwd_rope(f64(q), f64(k), f64(v), f64(sk), window, scale, c, s)
+    ra, _, _ = ref_fwd_rope(f64(q), f64(k), np.abs(f64(v)), f64(sk), window, scale, c, s)
+    np.testing.assert_array_equal(f64(k_rot), rk)
+    check_out_lse(f64(out), f64(lse), ro, rl, f"fwd_rope on midpoints W={window}", ref_abs=ra)
+    q_rot = ws[:B * S * Hq * 64 * 2].view(torch.bfloat16).view(B, S, Hq, 64)
+    want = apply_rope_bf16(f64(q[0]), np.arange(S), c, s)
+    assert (np.abs(want[..., :32]) > np.abs(f64(q[0])[..., :32])).mean() > 0.3  # the midpoints are there
+    np.testing.assert_array_equal(f64(q_rot[0]), want)
+    # decode of the last row, the query rotated at S - 1 in the decode kernel
+    cu = torch.tensor([0, S], dtype=torch.int32)
+    do_, dl = attn.decode_rope(qd[0, S - 1:S].contiguous(), k_rot[0].contiguous(), vd[0].contiguous(), cu.to(dev), skd,
+                               tab, S, window, scale)
+    torch.cuda.synchronize()
+    rdo, rdl = ref_decode_rope(f64(q[0, S - 1:S]), rk[0], f64(v[0]), cu.numpy(), f64(sk), window, scale, c, s)
+    rda, _ = ref_decode_rope(f64(q[0, S - 1:S]), rk[0], np.abs(f64(v[0])), cu.numpy(), f64(sk), window, scale, c, s)
+    check_out_lse(f64(do_), f64(dl), rdo, rdl, f"decode_rope on midpoints W={window}", ref_abs=rda)
+
+
 SMALL = [(1, 200, 8, 1), (2, 333, 16, 2), (1, 130, 6, 2), (1, 77, 1, 1)]
 
 
