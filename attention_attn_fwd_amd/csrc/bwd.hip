@@ -42,7 +42,6 @@
 namespace gptoss {
 namespace {
 
-constexpr int kThreads = 256;  // dsink kernel
 #ifndef GPTOSS_DKDV_WAVES
 #define GPTOSS_DKDV_WAVES 4
 #endif
@@ -73,37 +72,46 @@ struct BwdParams {
     float c;  // scale * log2(e)
 };
 
-// dsink: one workgroup per head sums the rows' exp(sink - lse) r terms
-// (contiguous per head and sequence; four independent partial sums).
-__global__ void __launch_bounds__(kThreads)
+// dsink: one workgroup of 1024 threads per head sums the rows'
+// exp(sink - lse) r terms (contiguous per head and sequence).  Each thread
+// keeps 16 loads in flight (16 partial sums), so the 16384 rows of a head
+// take one round trip instead of one per 1024 rows.
+constexpr int kDsinkThreads = 1024;
+constexpr int kDsinkUnroll = 16;
+__global__ void __launch_bounds__(kDsinkThreads)
 bwd_dsink_kernel(BwdParams p) {
-    __shared__ float red[kThreads / 64];
+    __shared__ float red[kDsinkThreads / 64];
     const int h = blockIdx.x;
-    const long long n = p.T;
-    const float* src = p.dsterm + (size_t)h * n;
-    float a0 = 0.0f, a1 = 0.0f, a2 = 0.0f, a3 = 0.0f;
+    const float* src = p.dsterm + (size_t)h * p.T;
+    float a[kDsinkUnroll];
+#pragma unroll
+    for (int k = 0; k < kDsinkUnroll; ++k) a[k] = 0.0f;
     // the rows of each sequence (for packed documents, only rows inside a
-    // document hold a term: the dq kernel wrote those), four partial sums
+    // document hold a term: the dq kernel wrote those)
     for (int b = 0; b < p.B; ++b) {
         const SeqRows sr = seq_rows(p.cu, p.S, p.Hq, p.T, b);
         const float* seg = src + sr.row0;
-        int i = threadIdx.x;
-        for (; i + 3 * kThreads < sr.len; i += 4 * kThreads) {
-            a0 += seg[i];
-            a1 += seg[i + kThreads];
-            a2 += seg[i + 2 * kThreads];
-            a3 += seg[i + 3 * kThreads];
+        for (int i = threadIdx.x; i < sr.len; i += kDsinkUnroll * kDsinkThreads) {
+#pragma unroll
+            for (int k = 0; k < kDsinkUnroll; ++k) {
+                const int j = i + k * kDsinkThreads;
+                const float x = seg[min(j, sr.len - 1)];  // in range; past the end counts 0
+                a[k] += j < sr.len ? x : 0.0f;
+            }
         }
-        for (; i < sr.len; i += kThreads) a0 += seg[i];
     }
-    float acc = (a0 + a1) + (a2 + a3);
+#pragma unroll
+    for (int w = kDsinkUnroll / 2; w > 0; w >>= 1)
+#pragma unroll
+        for (int k = 0; k < w; ++k) a[k] += a[k + w];
+    float acc = a[0];
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = acc;
     __syncthreads();
     if (threadIdx.x == 0) {
         float t = 0.0f;
-        for (int w = 0; w < kThreads / 64; ++w) t += red[w];
+        for (int w = 0; w < kDsinkThreads / 64; ++w) t += red[w];
         p.dsinks[h] = -t;
     }
 }
@@ -745,7 +753,7 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(bwd_dkdv_kernel, dim3((unsigned)(n_kt * a.B * a.Hkv)), dim3(kKvThreads), 0, stream, p, n_kt);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(bwd_dsink_kernel, dim3(a.Hq), dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL(bwd_dsink_kernel, dim3(a.Hq), dim3(kDsinkThreads), 0, stream, p);
     return hipGetLastError();
 }
 
