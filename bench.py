@@ -110,8 +110,9 @@ def main():
         digest_traffic(args.digest_traffic)
         return
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the path is "
-              "single-GPU by design, see DESIGN.md for how it would shard", file=sys.stderr)
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}): the kernels run on one GPU's share "
+              "of the work (KV heads, sequences and batch rows shard across GPUs without communication)",
+              file=sys.stderr)
         sys.exit(2)
 
     import torch
