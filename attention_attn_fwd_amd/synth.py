@@ -180,12 +180,12 @@ def make_varlen(Hq, Hkv, D=64, lengths=None, total=None, max_len=None, std=1.0, 
 # The five workloads.  Each prefill config runs one sliding-window-128 layer
 # and one full-causal layer (window 0) over the same tensors.
 CONFIGS = {
-    "c0_b1_s512_h8x1": dict(kind="fwd", B=1, S=512, Hq=8, Hkv=1, std=1.0, seed=1000),
-    "c1_b4_s4096_h64x8": dict(kind="fwd", B=4, S=4096, Hq=64, Hkv=8, std=1.0, seed=1001),
-    "c2_b1_s65536_h64x8": dict(kind="fwd", B=1, S=65536, Hq=64, Hkv=8, std=0.5, seed=1002),
-    "c3_bwd_b4_s4096_h64x8": dict(kind="bwd", B=4, S=4096, Hq=64, Hkv=8, std=1.0, seed=1001,
+    "small_b1_s512_h8x1": dict(kind="fwd", B=1, S=512, Hq=8, Hkv=1, std=1.0, seed=1000),
+    "prefill_b4_s4096_h64x8": dict(kind="fwd", B=4, S=4096, Hq=64, Hkv=8, std=1.0, seed=1001),
+    "long_b1_s65536_h64x8": dict(kind="fwd", B=1, S=65536, Hq=64, Hkv=8, std=0.5, seed=1002),
+    "train_b4_s4096_h64x8": dict(kind="bwd", B=4, S=4096, Hq=64, Hkv=8, std=1.0, seed=1001,
                                   dout_seed=1003),
-    "c4_decode_n128_l1024_h64x8": dict(kind="decode", N=128, Hq=64, Hkv=8, max_len=1024,
+    "decode_n128_l1024_h64x8": dict(kind="decode", N=128, Hq=64, Hkv=8, max_len=1024,
                                        seed=1004),
 }
 

@@ -136,11 +136,11 @@ def main():
     # NSETS copies of every input and output, used in rotation, so that
     # consecutive launches never find their working set in the 256 MB
     # last-level cache (MALL) that the previous launch filled.
-    case, dout_cpu = synth.config_inputs("c3_bwd_b4_s4096_h64x8")
+    case, dout_cpu = synth.config_inputs("train_b4_s4096_h64x8")
     B, S, Hq, _ = case.q.shape
     Hkv = case.k.shape[2]
     sinks = case.sinks.to(dev)
-    dec = synth.config_inputs("c4_decode_n128_l1024_h64x8")
+    dec = synth.config_inputs("decode_n128_l1024_h64x8")
     N = dec.q.shape[0]
     dcu, dsinks_ = dec.cu_seqlens.to(dev), dec.sinks.to(dev)
     lengths = (dec.cu_seqlens[1:] - dec.cu_seqlens[:-1]).tolist()
@@ -445,7 +445,7 @@ def main():
     del krots, rws
     # the small workload (B=1, S=512, 8q/1kv) and the long-context workload
     # (B=1, S=65536, 64q/8kv, values ~ N(0, 0.5^2)): forward of both layers
-    for cname, label in (("c0_b1_s512_h8x1", "c0"), ("c2_b1_s65536_h64x8", "c2")):
+    for cname, label in (("small_b1_s512_h8x1", "small"), ("long_b1_s65536_h64x8", "long")):
         cc = synth.config_inputs(cname)
         cB, cS, cHq, _ = cc.q.shape
         csets = []

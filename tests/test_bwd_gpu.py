@@ -114,7 +114,7 @@ def test_bwd_training_workload_whole(window):
     oracle (run per batch and KV group on the host's cores), into NaN-filled
     gradient buffers."""
     dev = need_gpu()
-    case, dout = synth.config_inputs("c3_bwd_b4_s4096_h64x8")
+    case, dout = synth.config_inputs("train_b4_s4096_h64x8")
     print(f"bwd B4 S4096 W={window}", flush=True)
     q, k, v, s = (t.to(dev) for t in (case.q, case.k, case.v, case.sinks))
     out, lse = attn.fwd(q, k, v, s, window, case.scale)

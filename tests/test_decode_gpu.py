@@ -26,13 +26,13 @@ def _oracle(case, window):
 
 
 @pytest.mark.parametrize("window", [128, 0])
-def test_decode_c4(window):
+def test_decode_workload(window):
     dev = need_gpu()
-    case = synth.config_inputs("c4_decode_n128_l1024_h64x8")
-    print(f"decode C4 W={window}", flush=True)
+    case = synth.config_inputs("decode_n128_l1024_h64x8")
+    print(f"decode workload W={window}", flush=True)
     out, lse = _run(case, window, dev)
     ro, rl = _oracle(case, window)
-    check_out_lse(f64(out), f64(lse), ro, rl, f"C4 W={window}")
+    check_out_lse(f64(out), f64(lse), ro, rl, f"decode workload W={window}")
 
 
 EDGE_LENGTHS = [1, 2, 63, 64, 65, 127, 128, 129, 255, 256, 257, 511, 512, 513, 1000, 1024]
@@ -172,7 +172,7 @@ def test_decode_split_count_invariance(workload, window):
     already admits for each plan, ~1e-3 here.)"""
     dev = need_gpu()
     if workload == "n128_l1024":
-        case = synth.config_inputs("c4_decode_n128_l1024_h64x8")
+        case = synth.config_inputs("decode_n128_l1024_h64x8")
     elif workload == "n8_l1024":
         case = synth.make_decode(8, 64, 8, max_len=1024, seed=seed_of("t3", window))
     else:

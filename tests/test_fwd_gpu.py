@@ -102,13 +102,13 @@ def test_fwd_row0_closed_form_on_gpu_output():
         assert abs(f64(lse)[0, h, 0] - np.logaddexp(s00, s[h])) <= 1e-3
 
 
-def test_fwd_c0_both_layers():
+def test_fwd_small_workload_both_layers():
     dev = need_gpu()
-    case = synth.config_inputs("c0_b1_s512_h8x1")
+    case = synth.config_inputs("small_b1_s512_h8x1")
     for window in (128, 0):
         out, lse = _run(case, window, dev)
         ro, rl = _oracle(case, window)
-        check_out_lse(f64(out), f64(lse), ro, rl, f"C0 W={window}")
+        check_out_lse(f64(out), f64(lse), ro, rl, f"small workload W={window}")
 
 
 def _run_poisoned(case, window, dev):
@@ -131,7 +131,7 @@ def test_fwd_prefill_workload_whole(window):
     every output and lse element against the oracle (run per batch and KV
     group on the host's cores)."""
     dev = need_gpu()
-    case = synth.config_inputs("c1_b4_s4096_h64x8")
+    case = synth.config_inputs("prefill_b4_s4096_h64x8")
     print(f"fwd B4 S4096 W={window}", flush=True)
     out, lse = _run_poisoned(case, window, dev)
     ro, rl = ref_fwd_groups(f64(case.q), f64(case.k), f64(case.v), f64(case.sinks), window, case.scale)
@@ -153,7 +153,7 @@ def test_fwd_long_context_sampled_rows(window):
     all 64 heads at 512 query rows (each row exact over all its keys), and
     every element of the output written and finite."""
     dev = need_gpu()
-    case = synth.config_inputs("c2_b1_s65536_h64x8")
+    case = synth.config_inputs("long_b1_s65536_h64x8")
     print(f"fwd B1 S65536 W={window}", flush=True)
     out, lse = _run_poisoned(case, window, dev)
     S = case.q.shape[1]

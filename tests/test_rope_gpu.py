@@ -193,7 +193,7 @@ def test_fwd_rope_workload_whole(window):
     rotated key, output and lse element against the oracle (per batch and KV
     group on the host's cores), into NaN-filled buffers."""
     dev = need_gpu()
-    case = synth.config_inputs("c1_b4_s4096_h64x8")
+    case = synth.config_inputs("prefill_b4_s4096_h64x8")
     print(f"fwd_rope workload W={window}", flush=True)
     B, S, Hq, D = case.q.shape
     Hkv = case.k.shape[2]
@@ -234,7 +234,7 @@ def test_decode_rope(window):
     """The 128-sequence decode workload with the query rotated at L - 1; the
     cache holds keys rotated by the oracle (positions 0 .. L - 1)."""
     dev = need_gpu()
-    dec = synth.config_inputs("c4_decode_n128_l1024_h64x8")
+    dec = synth.config_inputs("decode_n128_l1024_h64x8")
     cu = dec.cu_seqlens.numpy()
     c, s = _oracle_table(1024, GPTOSS_LIKE)
     pos = np.concatenate([np.arange(int(cu[i + 1] - cu[i])) for i in range(len(cu) - 1)]).astype(np.int64)
@@ -314,7 +314,7 @@ def test_bwd_rope_workload_whole(window):
     configuration bench.py times: every gradient element of all eight KV
     groups against the oracle, into NaN-filled gradient buffers."""
     dev = need_gpu()
-    case, dout = synth.config_inputs("c3_bwd_b4_s4096_h64x8")
+    case, dout = synth.config_inputs("train_b4_s4096_h64x8")
     print(f"bwd_rope workload W={window}", flush=True)
     B, S, Hq, D = case.q.shape
     Hkv = case.k.shape[2]

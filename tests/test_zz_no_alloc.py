@@ -67,7 +67,7 @@ def test_noalloc_workload_without_partials():
     array is not needed) gives the workspace entry point's result."""
     dev = need_gpu()
     lib = _lib.load()
-    case = synth.config_inputs("c4_decode_n128_l1024_h64x8")
+    case = synth.config_inputs("decode_n128_l1024_h64x8")
     for window in (0, 128):
         (o1, l1), (o2, l2) = _both(lib, case, window, dev)
         assert torch.equal(o1, o2) and torch.equal(l1, l2)
