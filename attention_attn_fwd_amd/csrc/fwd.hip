@@ -11,15 +11,15 @@
 // reaches HBM.
 //
 // Work decomposition
-//   One workgroup = 4 waves = 256 "columns".  A column is one (query position,
-//   query head) pair; the G = Hq / Hkv heads of one KV head are packed next to
-//   each other, so every K/V tile staged in LDS serves all G heads (GQA
-//   sharing) and the workgroup covers floor(256 / G) positions.
-//   Each wave owns 64 columns (kNb = 2 32-column MFMA N-blocks), two
-//   workgroups per CU.  (Eight waves of 32 columns, at most 128 registers and
-//   two workgroups per CU, measure the same on the full-causal layer and 4%
-//   faster on the sliding-window layer; four waves of 32 columns, three
-//   workgroups per CU, 8% slower on the full-causal layer.)
+//   One workgroup = 256 "columns".  A column is one (query position, query
+//   head) pair; the G = Hq / Hkv heads of one KV head are packed next to each
+//   other, so every K/V tile staged in LDS serves all G heads (GQA sharing)
+//   and the workgroup covers floor(256 / G) positions.  Full-causal layers:
+//   4 waves of 64 columns (kNb = 2 32-column MFMA N-blocks), two workgroups
+//   per CU.  Sliding-window layers: 8 waves of 32 columns (at most 128
+//   registers), two workgroups per CU, 4-5% faster there and the same on the
+//   full-causal layer.  (4 waves of 32 columns at three workgroups per CU
+//   ran 8% slower on the full-causal layer.)
 //   Key tiles of 64 rows are staged HBM -> LDS with 16-byte coalesced loads,
 //   double buffered, K and V both row-major (144-byte padded rows); the P.V
 //   contraction over keys reads V^T through transposing LDS reads
@@ -46,24 +46,8 @@
 namespace gptoss {
 namespace {
 
-#ifndef GPTOSS_FWD_WAVES
-#define GPTOSS_FWD_WAVES 4
-#endif
-#ifndef GPTOSS_FWD_NB
-#define GPTOSS_FWD_NB 2
-#endif
-constexpr int kWaves = GPTOSS_FWD_WAVES;
-constexpr int kNb = GPTOSS_FWD_NB;         // 32-column MFMA N-blocks per wave
-constexpr int kWaveCols = 32 * kNb;        // columns per wave
-constexpr int kThreads = 64 * kWaves;
-constexpr int kCols = kWaveCols * kWaves;  // columns per workgroup
-#ifndef GPTOSS_FWD_OCC
-#define GPTOSS_FWD_OCC (kNb == 1 ? 4 : 2)
-#endif
-constexpr int kWavesPerSimd = GPTOSS_FWD_OCC;  // occupancy the register budget is set for
-constexpr int kBk = 64;             // keys per LDS tile
-constexpr int kStRows = kThreads / 8;       // key rows staged per pass (8 threads per 128-byte row)
-constexpr int kStPasses = kBk / kStRows;    // passes per tile
+constexpr int kCols = 256;  // columns per workgroup (both layouts)
+constexpr int kBk = 64;     // keys per LDS tile
 
 struct FwdParams {
     const uint16_t* q;
@@ -135,8 +119,17 @@ __device__ __forceinline__ void block_coords(const FwdParams& p, int bid, int& g
     qt = nq - 1 - qt;
 }
 
-__global__ void __launch_bounds__(kThreads, kWavesPerSimd)
+// kWaves waves of kNb 32-column MFMA N-blocks each (kWaves * 32 * kNb =
+// kCols); 64-column waves need up to 256 registers (two waves per SIMD),
+// 32-column waves at most 128 (four).
+template <int kWaves, int kNb>
+__global__ void __launch_bounds__(64 * kWaves, kNb == 1 ? 4 : 2)
 fwd_kernel(FwdParams p) {
+    static_assert(kWaves * 32 * kNb == kCols, "a workgroup holds kCols columns");
+    constexpr int kWaveCols = 32 * kNb;           // columns per wave
+    constexpr int kThreads = 64 * kWaves;
+    constexpr int kStRows = kThreads / 8;         // key rows staged per pass (8 threads per 128-byte row)
+    constexpr int kStPasses = kBk / kStRows;      // passes per tile
     __shared__ uint4 smem[2][2][kTileUnits];  // [buffer][K | V][unit], both row-major
 
     const int tid = threadIdx.x;
@@ -479,7 +472,13 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {
     p.c = a.scale * kLog2e;
     const long long blocks = (long long)p.n_groups * p.n_qtiles;
     if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(fwd_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream, p);
+    // the sliding layer (three key tiles per workgroup, mostly edge tiles)
+    // runs 4-5% faster with 32-column waves; the full-causal layer runs the
+    // same with either and takes the 64-column layout
+    if (p.window > 0)
+        hipLaunchKernelGGL((fwd_kernel<8, 1>), dim3((unsigned)blocks), dim3(512), 0, stream, p);
+    else
+        hipLaunchKernelGGL((fwd_kernel<4, 2>), dim3((unsigned)blocks), dim3(256), 0, stream, p);
     return hipGetLastError();
 }
 
