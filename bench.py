@@ -72,6 +72,8 @@ def measured_traffic(key):
     except (OSError, ValueError):
         return None
     part = key.rsplit("_", 1)[0]
+    if part.replace("varlen_", "") not in PART_SOURCES:
+        return None
     if t.get("source_sha256", {}).get(part) != source_digest(part):
         return None
     v = t.get("bytes_per_launch", {}).get(key)
