@@ -49,6 +49,18 @@ gptoss_status check_decode_seqlen(int max_seqlen) {
     return GPTOSS_OK;
 }
 
+// Decode launches ceil(Hkv / 4) * ceil(G / 32) workgroup rows per sequence
+// chunk, at most 65535; the bound also keeps a K/V tile's row offsets (64
+// rows of Hkv * 128 bytes) below 2^32, which the split kernel relies on.
+gptoss_status check_decode_heads(int Hq, int Hkv) {
+    const long long rows = (long long)((Hkv + gptoss::kDecodeKvPerBlock - 1) / gptoss::kDecodeKvPerBlock) *
+                           ((Hq / Hkv + 31) / 32);
+    if (rows > 65535)
+        return fail(GPTOSS_ERR_UNSUPPORTED, "decode of %d KV heads needs %lld workgroup rows, more than 65535",
+                    Hkv, rows);
+    return GPTOSS_OK;
+}
+
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 #define CHECK_PTR(p, align)                                                                  \
@@ -317,6 +329,8 @@ static gptoss_status decode_entry(const void* q, const void* k_cache, const void
     if (st != GPTOSS_OK) return st;
     st = check_common(Hq, Hkv, D, window, softmax_scale);
     if (st != GPTOSS_OK) return st;
+    st = check_decode_heads(Hq, Hkv);
+    if (st != GPTOSS_OK) return st;
     if (N == 0) return ok();
     if ((long long)N > 65535)
         return fail(GPTOSS_ERR_INVALID_ARGUMENT, "N (%d) exceeds 65535 sequences per call", N);
@@ -394,6 +408,8 @@ gptoss_status gptoss_attn_decode_paged(const void* q, const void* k_pages, const
     gptoss_status st = check_decode_seqlen(max_seqlen);
     if (st != GPTOSS_OK) return st;
     st = check_common(Hq, Hkv, D, window, softmax_scale);
+    if (st != GPTOSS_OK) return st;
+    st = check_decode_heads(Hq, Hkv);
     if (st != GPTOSS_OK) return st;
     if (!is_pow2(page_size) || page_size > 65536)
         return fail(GPTOSS_ERR_INVALID_ARGUMENT, "page_size (%d) must be a power of two in [1, 65536]", page_size);
@@ -571,6 +587,8 @@ gptoss_status gptoss_attn_decode_rope(const void* q, const void* k_cache, const 
     gptoss_status st = check_decode_seqlen(max_seqlen);
     if (st != GPTOSS_OK) return st;
     st = check_common(Hq, Hkv, D, window, softmax_scale);
+    if (st != GPTOSS_OK) return st;
+    st = check_decode_heads(Hq, Hkv);
     if (st != GPTOSS_OK) return st;
     if (table_positions < max_seqlen)
         return fail(GPTOSS_ERR_INVALID_ARGUMENT, "rope table holds %d positions, max_seqlen is %d", table_positions,

@@ -75,11 +75,20 @@ __device__ __forceinline__ void seq_range(const DecParams& p, int n, int& base, 
 // The loads of tile t + 1 are issued as soon as tile t has been moved to
 // LDS.  (Keeping two to four tiles per wave in flight, at one wave per SIMD,
 // measured slower on the 128 x 1024 workload than one tile per wave at two
-// workgroups per CU, and so did two waves per KV head taking alternate tiles.)
-// kPaged: K/V rows are found through the block table (slot = position &
+// workgroups per CU, and so did two waves per KV head taking alternate
+// tiles; two waves per KV head taking contiguous halves, merged through LDS,
+// ran 34.2 against 32.6 us on the 128 x U{1..1024} workload.)
+// kPaged != 0: K/V rows are found through the block table (slot = position &
 // ring_mask, page = bt[n][slot >> ps_shift], row = slot & ps_mask); the page
 // indices of a tile are loaded one tile ahead of its K/V rows.
-template <bool kPaged>
+//   kPaged == 1 (pages of 1-4 tokens): every lane loads the page of each of
+//     its 8 rows (8 vector loads per tile).
+//   kPaged == 2 (pages of 8 or more tokens): the rows a lane group reads in
+//     step j are 8 consecutive positions, which cross at most one page
+//     boundary (the ring, a multiple of the page size, wraps only at one), so
+//     the wave needs two page indices per step, both wave-uniform: scalar
+//     loads, which leave the vector memory path to the K/V rows.
+template <int kPaged>
 __global__ void __launch_bounds__(kThreads, 2)
 decode_split_kernel(DecParams p) {
     __shared__ uint4 ksm[kWaves][kTileUnits];  // one row-major K tile per wave
@@ -93,7 +102,7 @@ decode_split_kernel(DecParams p) {
     seq_range(p, n, base, L, vis_lo);
     const int n_vis = L - vis_lo;
     const int n_act = (n_vis + p.chunk_keys - 1) / p.chunk_keys;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int kvh = kvg * kWaves + wave;
     if (n_act == 0) {
         // empty sequence: only the sink is visible (out = 0, lse = sink)
@@ -121,7 +130,7 @@ decode_split_kernel(DecParams p) {
     const size_t row_stride = (size_t)p.Hkv * kHeadDim;
     const uint16_t* kb = p.kc + ((size_t)base * p.Hkv + kvh) * kHeadDim;
     const uint16_t* vb = p.vc + ((size_t)base * p.Hkv + kvh) * kHeadDim;
-    const int* bt_row = kPaged ? p.bt + (size_t)n * p.pps : nullptr;
+    const int* bt_row = kPaged != 0 ? p.bt + (size_t)n * p.pps : nullptr;
 
     // the sink is only needed when a single-chunk sequence is finished, but
     // is loaded here so that its latency hides behind the tiles
@@ -149,18 +158,56 @@ decode_split_kernel(DecParams p) {
     // tiles.  Rows past the chunk end re-read its last row: their scores are
     // masked to -inf, so they add exactly 0 to l and to O.
     uint4 kr[8], vr[8];
-    int pid[8];  // paged: page of each of this lane's 8 rows of the next tile to load
+    int pid[8];  // kPaged == 1: page of each of this lane's 8 rows of the next tile to load
+    // kPaged == 2: slot page of the first row of step j and the page indices
+    // of that slot page and of the step's last row (wave-uniform)
+    int sp_first[8], pg_first[8], pg_last[8];
     auto tile_key = [&](int t, int j) { return min(c0 + t * kTileKeys + (lane >> 3) + 8 * j, c1 - 1); };
     auto load_pids = [&](int t) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) pid[j] = bt_row[(tile_key(t, j) & p.ring_mask) >> p.ps_shift];
+        for (int j = 0; j < 8; ++j) {
+            if (kPaged == 2) {
+                // the table through the constant address space: scalar loads
+                const __attribute__((address_space(4))) int* btc =
+                    (const __attribute__((address_space(4))) int*)bt_row;
+                const int k0 = __builtin_amdgcn_readfirstlane(min(c0 + t * kTileKeys + 8 * j, c1 - 1));
+                const int k7 = __builtin_amdgcn_readfirstlane(min(c0 + t * kTileKeys + 8 * j + 7, c1 - 1));
+                sp_first[j] = (k0 & p.ring_mask) >> p.ps_shift;
+                pg_first[j] = btc[sp_first[j]];
+                pg_last[j] = btc[(k7 & p.ring_mask) >> p.ps_shift];
+            } else {
+                pid[j] = bt_row[(tile_key(t, j) & p.ring_mask) >> p.ps_shift];
+            }
+        }
     };
+    // packed cache: one uniform base address per tile (scalar arithmetic) and
+    // 32-bit per-lane offsets, so a row pair's loads need one clamp (the row
+    // offsets of a tile stay below 2^32: the entry points bound Hkv through
+    // the grid size)
+    const uint32_t row_bytes = (uint32_t)p.Hkv * kHeadDim * 2;
+    const uint32_t unit_off = 16u * (lane & 7);
+    const uint32_t lane_off = (uint32_t)(lane >> 3) * row_bytes + unit_off;
     auto load_tile = [&](int t) {
+        if (kPaged == 0) {
+            const int t0 = c0 + t * kTileKeys;
+            const char* kt = reinterpret_cast<const char*>(kb) + (size_t)t0 * row_bytes;
+            const char* vt = reinterpret_cast<const char*>(vb) + (size_t)t0 * row_bytes;
+            const uint32_t lim = (uint32_t)(c1 - 1 - t0) * row_bytes + unit_off;  // the chunk's last row
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const uint32_t off = min(lane_off + (uint32_t)(8 * j) * row_bytes, lim);
+                kr[j] = ld16(kt + off);
+                vr[j] = ld16(vt + off);
+            }
+            return;
+        }
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             const int key = tile_key(t, j);
-            size_t row = (size_t)key;
-            if (kPaged) row = ((size_t)pid[j] << p.ps_shift) + (size_t)(key & p.ring_mask & p.ps_mask);
+            int page;
+            if (kPaged == 1) page = pid[j];
+            else page = ((key & p.ring_mask) >> p.ps_shift) == sp_first[j] ? pg_first[j] : pg_last[j];
+            const size_t row = ((size_t)page << p.ps_shift) + (size_t)(key & p.ring_mask & p.ps_mask);
             kr[j] = ld16(kb + row * row_stride + 8 * (lane & 7));
             vr[j] = ld16(vb + row * row_stride + 8 * (lane & 7));
         }
@@ -173,7 +220,7 @@ decode_split_kernel(DecParams p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[db][r] = 0.0f;
 
-    if (kPaged) {
+    if (kPaged != 0) {
         load_pids(0);
         load_tile(0);
         if (n_tiles > 1) load_pids(1);
@@ -203,6 +250,11 @@ decode_split_kernel(DecParams p) {
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) qf[ks] = as_bf16x8(qraw[ks]);
     for (int t = 0; t < n_tiles; ++t) {
+        // kPaged == 2: the next tile's page indices (scalar loads issued at
+        // the end of the previous iteration) share the LDS counter; waiting
+        // for them here, before this tile's LDS writes, keeps the wait that
+        // their use needs from also waiting for those writes
+        if (kPaged == 2) __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0) only
         // K and V tiles -> this wave's LDS tiles.  Only this wave touches
         // them and a wave's LDS operations complete in order, so the previous
         // tile's reads are done; the signal fences keep the compiler from
@@ -216,7 +268,7 @@ decode_split_kernel(DecParams p) {
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
         if (t + 1 < n_tiles) {  // in flight during this tile's compute
             load_tile(t + 1);
-            if (kPaged && t + 2 < n_tiles) load_pids(t + 2);
+            if (kPaged == 1 && t + 2 < n_tiles) load_pids(t + 2);
         }
         // S^T = K Q^T; A operand rows are keys in the forward's permuted
         // order, K slots 8 g + 0..7 of step ks are d = 16 ks + 8 g + 0..7
@@ -275,6 +327,15 @@ decode_split_kernel(DecParams p) {
             for (int kk = 0; kk < 4; ++kk)
                 oacc[db] = mfma32(tile_read_tr8(vsm[wave], 16 * kk + 8 * g, 32 * db + 16 * (l32 >> 4), l32 & 15),
                                   pb[kk], oacc[db]);
+        // kPaged == 2: the page indices of tile t + 2 are loaded after this
+        // tile's last LDS read, so that they arrive while the next iteration
+        // waits for the K/V loads of tile t + 1 (scalar loads count with the
+        // LDS operations, and every LDS wait issued while they are in flight
+        // would wait for them too)
+        if (kPaged == 2) {
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);
+            if (t + 2 < n_tiles) load_pids(t + 2);
+        }
     }
 
     const float l_tot = sum_across_halves(l_run);
@@ -434,10 +495,12 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
     p.pps = a.pages_per_seq;
     p.ring_mask = a.ring_tokens > 0 ? a.ring_tokens - 1 : 0x7fffffff;
     dim3 grid(p.n_splits, ((a.Hkv + kWaves - 1) / kWaves) * p.n_hblk, a.N);
-    if (p.bt != nullptr)
-        hipLaunchKernelGGL(decode_split_kernel<true>, grid, dim3(kThreads), 0, stream, p);
+    if (p.bt != nullptr && p.ps_shift >= 3)
+        hipLaunchKernelGGL(decode_split_kernel<2>, grid, dim3(kThreads), 0, stream, p);
+    else if (p.bt != nullptr)
+        hipLaunchKernelGGL(decode_split_kernel<1>, grid, dim3(kThreads), 0, stream, p);
     else
-        hipLaunchKernelGGL(decode_split_kernel<false>, grid, dim3(kThreads), 0, stream, p);
+        hipLaunchKernelGGL(decode_split_kernel<0>, grid, dim3(kThreads), 0, stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.n_splits == 1) return e;  // one chunk per sequence: nothing to merge
     if (p.n_splits <= kFewChunks)

@@ -144,6 +144,18 @@ def test_decode_rejects_bad_arguments(lib, kw, frag):
     assert frag in lib.gptoss_attn_last_error().decode()
 
 
+def test_decode_refuses_more_kv_heads_than_its_grid_holds(lib):
+    # ceil(262144 / 4) = 65536 workgroup rows: one more than a launch takes
+    for call in (lambda: _dec(lib, Hq=262144, Hkv=262144),
+                 lambda: _paged(lib, Hq=262144, Hkv=262144)):
+        assert call() == 2
+        assert "more than 65535" in lib.gptoss_attn_last_error().decode()
+    # the largest accepted count gets past the check (and fails later, on the
+    # host, at the missing cu_seqlens)
+    assert _dec(lib, Hq=262140, Hkv=262140, cu=None) == 1
+    assert "cu_seqlens is NULL" in lib.gptoss_attn_last_error().decode()
+
+
 def test_workspace_size_queries(lib):
     # a long single sequence is cut into chunks whose partials need a workspace
     assert lib.gptoss_attn_decode_workspace_size(1, 64, 8, 64, 65536, 0) > 0

@@ -28,7 +28,8 @@ def _oracle(case, window):
                             case.seq_lens.numpy(), f64(case.sinks), case.ring_tokens, window, case.scale)
 
 
-@pytest.mark.parametrize("page_size", [1, 16, 64, 256])
+# pages of 1-4 tokens take the per-lane lookup, 8 and more the wave-uniform one
+@pytest.mark.parametrize("page_size", [1, 4, 8, 16, 64, 256])
 @pytest.mark.parametrize("window", [0, 128])
 @pytest.mark.parametrize("heads", [(64, 8), (8, 1), (128, 2)])
 def test_paged_linear(page_size, window, heads):
@@ -74,3 +75,17 @@ def test_paged_long_sequence_chunked():
     out, lse = _run(case, 0, dev)
     ro, rl = _oracle(case, 0)
     check_out_lse(f64(out), f64(lse), ro, rl, "paged long")
+
+
+@pytest.mark.parametrize("page_size", [8, 16, 4])
+def test_paged_window_chunked(page_size):
+    """Few sequences with a window of 1000: the visible range starts at
+    L - 1000 (not a multiple of 8) and is cut into chunks, so a lane group's
+    8 rows often straddle a page boundary."""
+    dev = need_gpu()
+    lengths = [20000, 3001, 1000, 999]
+    case = synth.make_paged_decode(len(lengths), 64, 8, page_size, lengths=lengths, seed=40 + page_size)
+    print(f"paged window chunked ps={page_size}", flush=True)
+    out, lse = _run(case, 1000, dev)
+    ro, rl = _oracle(case, 1000)
+    check_out_lse(f64(out), f64(lse), ro, rl, f"paged W=1000 ps={page_size}")
