@@ -49,11 +49,11 @@ gptoss_status check_decode_seqlen(int max_seqlen) {
     return GPTOSS_OK;
 }
 
-// Decode launches ceil(Hkv / 4) * ceil(G / 32) workgroup rows per sequence
+// Decode launches ceil(Hkv / 2) * ceil(G / 32) workgroup rows per sequence
 // chunk, at most 65535; the bound also keeps a K/V tile's row offsets (64
 // rows of Hkv * 128 bytes) below 2^32, which the split kernel relies on.
 gptoss_status check_decode_heads(int Hq, int Hkv) {
-    const long long rows = (long long)((Hkv + gptoss::kDecodeKvPerBlock - 1) / gptoss::kDecodeKvPerBlock) *
+    const long long rows = (long long)((Hkv + gptoss::kDecodeMinKvPerBlock - 1) / gptoss::kDecodeMinKvPerBlock) *
                            ((Hq / Hkv + 31) / 32);
     if (rows > 65535)
         return fail(GPTOSS_ERR_UNSUPPORTED, "decode of %d KV heads needs %lld workgroup rows, more than 65535",

@@ -37,8 +37,6 @@
 namespace gptoss {
 namespace {
 
-constexpr int kWaves = kDecodeKvPerBlock;  // KV heads per workgroup, one per wave
-constexpr int kThreads = 64 * kWaves;
 constexpr int kTileKeys = kDecodeKeyTile;  // keys per wave step
 constexpr int kPartStride = kDecodePartStride;
 
@@ -58,6 +56,7 @@ struct DecParams {
     int ps_shift, ps_mask, pps, ring_mask;  // page size = 1 << ps_shift; slot = position & ring_mask
     int Hq, Hkv, G, window, n_splits, n_hblk, max_seqlen;
     int chunk_keys;   // visible keys per chunk (a multiple of 64)
+    int ranked;       // one chunk per sequence, N <= kDecodeRankMaxSeqs: items in ranked order
     float c;          // scale * log2(e)
 };
 
@@ -96,18 +95,75 @@ __device__ __forceinline__ void seq_range(const DecParams& p, int n, int& base, 
 //     boundary (the ring, a multiple of the page size, wraps only at one), so
 //     the wave needs two page indices per step, both wave-uniform: scalar
 //     loads, which leave the vector memory path to the K/V rows.
-template <int kPaged>
-__global__ void __launch_bounds__(kThreads, 2)
+template <int kPaged, int kWaves>
+__global__ void __launch_bounds__(64 * kWaves, 2)
 decode_split_kernel(DecParams p) {
+    constexpr int kThreads = 64 * kWaves;  // kWaves KV heads per workgroup, one per wave
     __shared__ uint4 ksm[kWaves][kTileUnits];  // one row-major K tile per wave
     __shared__ uint4 vsm[kWaves][kTileUnits];  // one row-major V tile per wave
 
     const int chunk = blockIdx.x;
-    const int kvg = blockIdx.y / p.n_hblk;
-    const int hb = blockIdx.y % p.n_hblk;
-    const int n = blockIdx.z;
+    int item_y = blockIdx.y, n = blockIdx.z;
     int base, L, vis_lo;
-    seq_range(p, n, base, L, vis_lo);
+    if (p.ranked) {
+        // One CU streams a few tens of GB/s at most, so the workgroups that
+        // hold the longest sequences set the time unless every CU gets an
+        // even share.  Workgroups start in id order and the first half of the
+        // ids fills the CUs once, so the items (sequence, head block) go out
+        // longest first over the first half and shortest first over the
+        // second: each CU pairs a long item with a short one.  The workgroup
+        // ranks the sequences itself, all workgroups alike, by a unique key:
+        // visible tiles (capped at 2^23), then lower index first.
+        static_assert(kDecodeRankMaxSeqs <= 2 * kThreads && kDecodeRankMaxSeqs <= 256, "two candidates a thread");
+        __shared__ uint4 s_key[kDecodeRankMaxSeqs / 4];
+        __shared__ int s_pick[4];  // sequence, base, L, vis_lo
+        const int N = gridDim.z, N4 = (N + 3) / 4;
+        const int Y = gridDim.y, ni = Y * N, id = blockIdx.y + Y * blockIdx.z, half = ni / 2;
+        const int r = id < half ? id : ni - 1 - (id - half);
+        const int want = r / Y;  // rank of this item's sequence
+        item_y = r % Y;
+        uint32_t key[2];
+        int b_c[2], L_c[2], lo_c[2];
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            const int i = threadIdx.x + kThreads * c;
+            key[c] = 0;  // below every real key (pads the last uint4)
+            if (i < N) {
+                seq_range(p, i, b_c[c], L_c[c], lo_c[c]);
+                const uint32_t tiles = min((uint32_t)(L_c[c] - lo_c[c] + kTileKeys - 1) / kTileKeys, 1u << 23);
+                key[c] = ((tiles + 1) << 8) | (uint32_t)(255 - i);
+            }
+            if (i < 4 * N4) reinterpret_cast<uint32_t*>(s_key)[i] = key[c];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            const int i = threadIdx.x + kThreads * c;
+            if (i < N) {
+                int rank = 0;
+#pragma unroll 4
+                for (int j = 0; j < N4; ++j) {
+                    const uint4 u = s_key[j];
+                    rank += (u.x > key[c]) + (u.y > key[c]) + (u.z > key[c]) + (u.w > key[c]);
+                }
+                if (rank == want) {
+                    s_pick[0] = i;
+                    s_pick[1] = b_c[c];
+                    s_pick[2] = L_c[c];
+                    s_pick[3] = lo_c[c];
+                }
+            }
+        }
+        __syncthreads();
+        n = s_pick[0];
+        base = s_pick[1];
+        L = s_pick[2];
+        vis_lo = s_pick[3];
+    } else {
+        seq_range(p, n, base, L, vis_lo);
+    }
+    const int kvg = item_y / p.n_hblk;
+    const int hb = item_y % p.n_hblk;
     const int n_vis = L - vis_lo;
     const int n_act = (n_vis + p.chunk_keys - 1) / p.chunk_keys;
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -493,6 +549,7 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
     p.n_splits = cp.n_splits;
     p.chunk_keys = cp.chunk_keys;
     p.n_hblk = (p.G + 31) / 32;
+    p.ranked = decode_kv_per_block(a.window) == 2 && cp.n_splits == 1 && a.N <= kDecodeRankMaxSeqs;
     p.c = a.scale * kLog2e;
     p.bt = a.block_table;
     p.lens = a.seq_lens;
@@ -502,13 +559,20 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
     p.ps_mask = a.page_size > 0 ? a.page_size - 1 : 0;
     p.pps = a.pages_per_seq;
     p.ring_mask = a.ring_tokens > 0 ? a.ring_tokens - 1 : 0x7fffffff;
-    dim3 grid(p.n_splits, ((a.Hkv + kWaves - 1) / kWaves) * p.n_hblk, a.N);
-    if (p.bt != nullptr && p.ps_shift >= 3)
-        hipLaunchKernelGGL(decode_split_kernel<2>, grid, dim3(kThreads), 0, stream, p);
-    else if (p.bt != nullptr)
-        hipLaunchKernelGGL(decode_split_kernel<1>, grid, dim3(kThreads), 0, stream, p);
-    else
-        hipLaunchKernelGGL(decode_split_kernel<0>, grid, dim3(kThreads), 0, stream, p);
+    const int kvpb = decode_kv_per_block(a.window);
+    dim3 grid(p.n_splits, ((a.Hkv + kvpb - 1) / kvpb) * p.n_hblk, a.N);
+    const int mode = p.bt == nullptr ? 0 : p.ps_shift >= 3 ? 2 : 1;
+    if (kvpb == 2) {
+        const dim3 block(128);
+        if (mode == 2) hipLaunchKernelGGL((decode_split_kernel<2, 2>), grid, block, 0, stream, p);
+        else if (mode == 1) hipLaunchKernelGGL((decode_split_kernel<1, 2>), grid, block, 0, stream, p);
+        else hipLaunchKernelGGL((decode_split_kernel<0, 2>), grid, block, 0, stream, p);
+    } else {
+        const dim3 block(256);
+        if (mode == 2) hipLaunchKernelGGL((decode_split_kernel<2, 4>), grid, block, 0, stream, p);
+        else if (mode == 1) hipLaunchKernelGGL((decode_split_kernel<1, 4>), grid, block, 0, stream, p);
+        else hipLaunchKernelGGL((decode_split_kernel<0, 4>), grid, block, 0, stream, p);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.n_splits == 1) return e;  // one chunk per sequence: nothing to merge
     if (p.n_splits <= kFewChunks)

@@ -73,11 +73,19 @@ size_t bwd_workspace_bytes(long long total_rows, int Hq);
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream);
 
 // Decode split plan (host side, no device access).  A split workgroup
-// covers kDecodeKvPerBlock KV heads (one wave each) of one sequence's chunk
-// of chunk_keys visible keys (a multiple of kDecodeKeyTile); a sequence has
-// at most n_splits chunks.  With more than one chunk the workspace holds one
+// covers kv_per_block KV heads (one wave each) of one sequence's chunk of
+// chunk_keys visible keys (a multiple of kDecodeKeyTile); a sequence has at
+// most n_splits chunks.  With more than one chunk the workspace holds one
 // partial of kDecodePartStride floats per (sequence, query head, chunk).
-constexpr int kDecodeKvPerBlock = 4;
+// Windows of at most kDecodeSmallWindow keys (a sliding layer: visible
+// lengths differ little) take 4 KV heads per workgroup; otherwise 2, and
+// with one chunk per sequence and at most kDecodeRankMaxSeqs sequences the
+// workgroups take the (sequence, head block) items in an order ranked by
+// visible length (the split kernel ranks them itself).
+constexpr int kDecodeSmallWindow = 256;
+constexpr int kDecodeMinKvPerBlock = 2;  // the most workgroup rows a launch can have
+constexpr int kDecodeRankMaxSeqs = 256;
+constexpr int decode_kv_per_block(int window) { return window > 0 && window <= kDecodeSmallWindow ? 4 : 2; }
 constexpr int kDecodeKeyTile = 64;
 constexpr int kDecodePartStride = 68;  // O[64], m, l, pad
 struct DecodePlan {

@@ -9,12 +9,12 @@ namespace gptoss {
 
 namespace {
 constexpr size_t align256(size_t n) { return (n + 255) / 256 * 256; }
-// Decode split workgroups the plan aims for: one per CU.  A sequence is cut
-// into chunks only when there are too few (sequence, KV-head group) pairs to
-// fill the chip; every chunk but the last per sequence costs a partial write
-// and read plus the merge launch, which on the 128 x U{1..1024} workload
-// cost more than they gain.
-constexpr long long kDecodeTargetWorkgroups = 256;
+// Decode split workgroups the plan aims for: two per CU (a workgroup is two
+// waves).  A sequence is cut into chunks only when there are too few
+// (sequence, KV-head block) pairs to fill the chip; every chunk but the last
+// per sequence costs a partial write and read plus the merge launch, which
+// on the 128 x U{1..1024} workload cost more than they gain.
+constexpr long long kDecodeTargetWorkgroups = 512;
 // Shortest chunk the plan cuts (a multiple of the key tile).  Two tiles:
 // a one-tile chunk saves less than the merge launch it brings (a sliding
 // layer's 128 visible keys decode fastest unsplit).
@@ -36,7 +36,7 @@ DecodePlan decode_plan(int N, int Hq, int Hkv, int max_seqlen, int window) {
     const int G = Hq / Hkv;
     const long long vis = window > 0 ? std::min<long long>(max_seqlen, window) : (long long)max_seqlen;
     const long long groups =
-        (long long)N * ((Hkv + kDecodeKvPerBlock - 1) / kDecodeKvPerBlock) * ((G + 31) / 32);
+        (long long)N * ((Hkv + decode_kv_per_block(window) - 1) / decode_kv_per_block(window)) * ((G + 31) / 32);
     const long long want = std::max(1LL, (kDecodeTargetWorkgroups + groups - 1) / std::max(1LL, groups));
     const long long max_chunks = std::max(1LL, (vis + kDecodeMinChunkKeys - 1) / kDecodeMinChunkKeys);
     const long long n = std::min(want, max_chunks);

@@ -32,7 +32,7 @@
  *     lse [B, Hq, S]; sinks/dsinks [Hq].
  *   - head_dim D must be 64 and the group size Hq / Hkv at most 128
  *     (GPTOSS_ERR_UNSUPPORTED otherwise).  The decode entry points also need
- *     ceil(Hkv / 4) * ceil(Hq / Hkv / 32) <= 65535 (their launch's workgroup
+ *     ceil(Hkv / 2) * ceil(Hq / Hkv / 32) <= 65535 (their launch's workgroup
  *     rows; GPTOSS_ERR_UNSUPPORTED otherwise).
  *   - The caller owns every buffer (inputs, outputs, workspace).  The library
  *     allocates no device memory and keeps no state between calls beyond a

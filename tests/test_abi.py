@@ -145,14 +145,14 @@ def test_decode_rejects_bad_arguments(lib, kw, frag):
 
 
 def test_decode_refuses_more_kv_heads_than_its_grid_holds(lib):
-    # ceil(262144 / 4) = 65536 workgroup rows: one more than a launch takes
-    for call in (lambda: _dec(lib, Hq=262144, Hkv=262144),
-                 lambda: _paged(lib, Hq=262144, Hkv=262144)):
+    # ceil(131072 / 2) = 65536 workgroup rows: one more than a launch takes
+    for call in (lambda: _dec(lib, Hq=131072, Hkv=131072),
+                 lambda: _paged(lib, Hq=131072, Hkv=131072)):
         assert call() == 2
         assert "more than 65535" in lib.gptoss_attn_last_error().decode()
     # the largest accepted count gets past the check (and fails later, on the
     # host, at the missing cu_seqlens)
-    assert _dec(lib, Hq=262140, Hkv=262140, cu=None) == 1
+    assert _dec(lib, Hq=131070, Hkv=131070, cu=None) == 1
     assert "cu_seqlens is NULL" in lib.gptoss_attn_last_error().decode()
 
 
