@@ -56,6 +56,7 @@ struct DecParams {
     int ps_shift, ps_mask, pps, ring_mask;  // page size = 1 << ps_shift; slot = position & ring_mask
     int Hq, Hkv, G, window, n_splits, n_hblk, max_seqlen;
     int chunk_keys;   // visible keys per chunk (a multiple of 64)
+    uint32_t page_bytes;  // paged cache: bytes per page (page_size * Hkv * 128; below 2^32 where used)
     int ranked;       // one chunk per sequence, N <= kDecodeRankMaxSeqs: items in ranked order
     float c;          // scale * log2(e)
 };
@@ -90,11 +91,18 @@ __device__ __forceinline__ void seq_range(const DecParams& p, int n, int& base, 
 // indices of a tile are loaded one tile ahead of its K/V rows.
 //   kPaged == 1 (pages of 1-4 tokens): every lane loads the page of each of
 //     its 8 rows (8 vector loads per tile).
-//   kPaged == 2 (pages of 8 or more tokens): the rows a lane group reads in
-//     step j are 8 consecutive positions, which cross at most one page
-//     boundary (the ring, a multiple of the page size, wraps only at one), so
-//     the wave needs two page indices per step, both wave-uniform: scalar
-//     loads, which leave the vector memory path to the K/V rows.
+//   kPaged == 2 (pages of 8 or more tokens, page bytes below 2^32, a
+//     window): the rows a lane group reads in step j are 8 consecutive
+//     positions, which cross at most one page boundary (the ring, a multiple
+//     of the page size, wraps only at one), so the wave needs two page
+//     indices per step, both wave-uniform: scalar loads, which leave the
+//     vector memory path to the K/V rows; each lane picks its page and forms
+//     its 64-bit row address.
+//   kPaged == 3 (the same pages, no window): every chunk starts on an 8-row
+//     boundary, so a step never crosses a page: one page index per step and
+//     a uniform page base plus a 32-bit offset within the page.  (A kernel
+//     holding both this path and the per-lane one ran 13% slower on the full
+//     layer than this path alone, even where it never took the other.)
 template <int kPaged, int kWaves>
 __global__ void __launch_bounds__(64 * kWaves, 2)
 decode_split_kernel(DecParams p) {
@@ -223,34 +231,42 @@ decode_split_kernel(DecParams p) {
     // masked to -inf, so they add exactly 0 to l and to O.
     uint4 kr[8], vr[8];
     int pid[8];  // kPaged == 1: page of each of this lane's 8 rows of the next tile to load
-    // kPaged == 2: slot page of the first row of step j and the page indices
-    // of that slot page and of the step's last row (wave-uniform)
-    int sp_first[8], pg_first[8], pg_last[8];
+    // kPaged >= 2 (wave-uniform): page indices of step j's first and (mode 2)
+    // last rows, and (mode 2) how many of its 8 rows lie in the first one
+    int pg_first[8], pg_last[8], cut[8];
     auto tile_key = [&](int t, int j) { return min(c0 + t * kTileKeys + (lane >> 3) + 8 * j, c1 - 1); };
+    // packed cache: one uniform base address per tile (scalar arithmetic) and
+    // 32-bit per-lane offsets, so a row pair's loads need one clamp (the row
+    // offsets of a tile stay below 2^32: the entry points bound Hkv through
+    // the grid size); the paged path's 32-bit offsets are bounded where taken
+    const uint32_t row_bytes = (uint32_t)p.Hkv * kHeadDim * 2;
+    const uint32_t unit_off = 16u * (lane & 7);
+    const uint32_t lane_off = (uint32_t)(lane >> 3) * row_bytes + unit_off;
     auto load_pids = [&](int t) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            if (kPaged == 2) {
-                // the table through the constant address space: scalar loads
+            if (kPaged == 3) {
+                // steps start on 8-row boundaries: one page per step
                 const __attribute__((address_space(4))) int* btc =
                     (const __attribute__((address_space(4))) int*)bt_row;
                 const int k0 = __builtin_amdgcn_readfirstlane(min(c0 + t * kTileKeys + 8 * j, c1 - 1));
-                const int k7 = __builtin_amdgcn_readfirstlane(min(c0 + t * kTileKeys + 8 * j + 7, c1 - 1));
-                sp_first[j] = (k0 & p.ring_mask) >> p.ps_shift;
-                pg_first[j] = btc[sp_first[j]];
+                pg_first[j] = btc[(k0 & p.ring_mask) >> p.ps_shift];
+            } else if (kPaged == 2) {
+                // the table through the constant address space: scalar loads
+                const __attribute__((address_space(4))) int* btc =
+                    (const __attribute__((address_space(4))) int*)bt_row;
+                const int kb0 = __builtin_amdgcn_readfirstlane(c0 + t * kTileKeys + 8 * j);
+                const int k0 = min(kb0, c1 - 1), k7 = min(kb0 + 7, c1 - 1);
+                pg_first[j] = btc[(k0 & p.ring_mask) >> p.ps_shift];
                 pg_last[j] = btc[(k7 & p.ring_mask) >> p.ps_shift];
+                // rows past the chunk end repeat row c1 - 1, which lies in
+                // the page of k7
+                cut[j] = kb0 > c1 - 1 ? 8 : min(8, (p.ps_mask + 1) - (kb0 & p.ps_mask));
             } else {
                 pid[j] = bt_row[(tile_key(t, j) & p.ring_mask) >> p.ps_shift];
             }
         }
     };
-    // packed cache: one uniform base address per tile (scalar arithmetic) and
-    // 32-bit per-lane offsets, so a row pair's loads need one clamp (the row
-    // offsets of a tile stay below 2^32: the entry points bound Hkv through
-    // the grid size)
-    const uint32_t row_bytes = (uint32_t)p.Hkv * kHeadDim * 2;
-    const uint32_t unit_off = 16u * (lane & 7);
-    const uint32_t lane_off = (uint32_t)(lane >> 3) * row_bytes + unit_off;
     auto load_tile = [&](int t) {
         if (kPaged == 0) {
             const int t0 = c0 + t * kTileKeys;
@@ -265,12 +281,27 @@ decode_split_kernel(DecParams p) {
             }
             return;
         }
+        if (kPaged == 3) {
+            // every step within one page: a uniform page base per step
+            // (scalar arithmetic) plus a 32-bit offset within the page (a
+            // slot is below 2^16 and a row below 2^24 bytes: the entry points
+            // bound Hkv, so the 24-bit multiply is exact; the launcher takes
+            // this path only for pages below 2^32 bytes)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const size_t page_off = (size_t)(uint32_t)pg_first[j] * p.page_bytes;
+                const uint32_t in_page = __umul24((uint32_t)(tile_key(t, j) & p.ring_mask & p.ps_mask), row_bytes) + unit_off;
+                kr[j] = ld16_stream(reinterpret_cast<const char*>(kb) + page_off + in_page);
+                vr[j] = ld16_stream(reinterpret_cast<const char*>(vb) + page_off + in_page);
+            }
+            return;
+        }
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             const int key = tile_key(t, j);
             int page;
             if (kPaged == 1) page = pid[j];
-            else page = ((key & p.ring_mask) >> p.ps_shift) == sp_first[j] ? pg_first[j] : pg_last[j];
+            else page = (lane >> 3) < cut[j] ? pg_first[j] : pg_last[j];
             const size_t row = ((size_t)page << p.ps_shift) + (size_t)(key & p.ring_mask & p.ps_mask);
             kr[j] = ld16_stream(kb + row * row_stride + 8 * (lane & 7));
             vr[j] = ld16_stream(vb + row * row_stride + 8 * (lane & 7));
@@ -314,11 +345,11 @@ decode_split_kernel(DecParams p) {
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) qf[ks] = as_bf16x8(qraw[ks]);
     for (int t = 0; t < n_tiles; ++t) {
-        // kPaged == 2: the next tile's page indices (scalar loads issued at
+        // kPaged >= 2: the next tile's page indices (scalar loads issued at
         // the end of the previous iteration) share the LDS counter; waiting
         // for them here, before this tile's LDS writes, keeps the wait that
         // their use needs from also waiting for those writes
-        if (kPaged == 2) __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0) only
+        if (kPaged >= 2) __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0) only
         // K and V tiles -> this wave's LDS tiles.  Only this wave touches
         // them and a wave's LDS operations complete in order, so the previous
         // tile's reads are done; the signal fences keep the compiler from
@@ -391,12 +422,12 @@ decode_split_kernel(DecParams p) {
             for (int kk = 0; kk < 4; ++kk)
                 oacc[db] = mfma32(tile_read_tr8(vsm[wave], 16 * kk + 8 * g, 32 * db + 16 * (l32 >> 4), l32 & 15),
                                   pb[kk], oacc[db]);
-        // kPaged == 2: the page indices of tile t + 2 are loaded after this
+        // kPaged >= 2: the page indices of tile t + 2 are loaded after this
         // tile's last LDS read, so that they arrive while the next iteration
         // waits for the K/V loads of tile t + 1 (scalar loads count with the
         // LDS operations, and every LDS wait issued while they are in flight
         // would wait for them too)
-        if (kPaged == 2) {
+        if (kPaged >= 2) {
             __atomic_signal_fence(__ATOMIC_SEQ_CST);
             if (t + 2 < n_tiles) load_pids(t + 2);
         }
@@ -559,17 +590,26 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
     p.ps_mask = a.page_size > 0 ? a.page_size - 1 : 0;
     p.pps = a.pages_per_seq;
     p.ring_mask = a.ring_tokens > 0 ? a.ring_tokens - 1 : 0x7fffffff;
+
     const int kvpb = decode_kv_per_block(a.window);
     dim3 grid(p.n_splits, ((a.Hkv + kvpb - 1) / kvpb) * p.n_hblk, a.N);
-    const int mode = p.bt == nullptr ? 0 : p.ps_shift >= 3 ? 2 : 1;
+    // pages of 8+ tokens whose byte size fits 32 bits take the wave-uniform
+    // page paths; without a window every chunk starts on an 8-row boundary,
+    // so no load step crosses a page (mode 3)
+    const long long page_bytes = (long long)a.page_size * a.Hkv * kHeadDim * 2;
+    const bool uniform_pages = p.ps_shift >= 3 && page_bytes < (1LL << 32);
+    p.page_bytes = uniform_pages ? (uint32_t)page_bytes : 0u;
+    const int mode = p.bt == nullptr ? 0 : !uniform_pages ? 1 : p.window == 0 ? 3 : 2;
     if (kvpb == 2) {
         const dim3 block(128);
-        if (mode == 2) hipLaunchKernelGGL((decode_split_kernel<2, 2>), grid, block, 0, stream, p);
+        if (mode == 3) hipLaunchKernelGGL((decode_split_kernel<3, 2>), grid, block, 0, stream, p);
+        else if (mode == 2) hipLaunchKernelGGL((decode_split_kernel<2, 2>), grid, block, 0, stream, p);
         else if (mode == 1) hipLaunchKernelGGL((decode_split_kernel<1, 2>), grid, block, 0, stream, p);
         else hipLaunchKernelGGL((decode_split_kernel<0, 2>), grid, block, 0, stream, p);
     } else {
         const dim3 block(256);
-        if (mode == 2) hipLaunchKernelGGL((decode_split_kernel<2, 4>), grid, block, 0, stream, p);
+        if (mode == 3) hipLaunchKernelGGL((decode_split_kernel<3, 4>), grid, block, 0, stream, p);
+        else if (mode == 2) hipLaunchKernelGGL((decode_split_kernel<2, 4>), grid, block, 0, stream, p);
         else if (mode == 1) hipLaunchKernelGGL((decode_split_kernel<1, 4>), grid, block, 0, stream, p);
         else hipLaunchKernelGGL((decode_split_kernel<0, 4>), grid, block, 0, stream, p);
     }
