@@ -91,6 +91,48 @@ def test_decode_many_sequences(N):
     check_out_lse(f64(out), f64(lse), ro, rl, f"N={N}")
 
 
+@pytest.mark.parametrize("N", [255, 256, 257])
+def test_decode_ranked_order(N):
+    """With one chunk per sequence and at most 256 sequences (two KV heads
+    per workgroup, no small window) every workgroup ranks the sequences by
+    visible tiles itself and takes its item from that order.  Lengths with
+    many ties (the rank breaks them by index) and empty sequences; outputs
+    start as NaN, so an item taken twice or never shows.  Every sequence's
+    result must also not depend on where it sits in the batch: a permuted
+    batch gives the same bits per sequence."""
+    dev = need_gpu()
+    gen = np.random.default_rng(900 + N)
+    lengths = gen.choice([0, 1, 63, 64, 65, 500, 1000, 1024], size=N).tolist()
+    lengths[: 4] = [1024, 0, 1024, 1]
+    case = synth.make_decode(N, 64, 8, lengths=lengths, seed=31 + N)
+    print(f"ranked decode N={N}", flush=True)
+
+    def run(c):
+        t = [x.to(dev) for x in (c.q, c.k_cache, c.v_cache, c.cu_seqlens, c.sinks)]
+        o = torch.full((N, 64, 64), float("nan"), dtype=torch.bfloat16, device=dev)
+        l = torch.full((N, 64), float("nan"), device=dev)
+        attn.decode(*t, c.max_seqlen, 0, c.scale, out=o, lse=l)
+        torch.cuda.synchronize()
+        return o, l
+
+    out, lse = run(case)
+    ro, rl = _oracle(case, 0)
+    check_out_lse(f64(out), f64(lse), ro, rl, f"ranked N={N}")
+
+    perm = gen.permutation(N)
+    lp = [lengths[i] for i in perm]
+    cu = case.cu_seqlens.long()
+    rows = torch.cat([torch.arange(int(cu[i]), int(cu[i + 1])) for i in perm]) if sum(lp) else torch.zeros(0, dtype=torch.long)
+    cup = torch.zeros(N + 1, dtype=torch.int32)
+    cup[1:] = torch.cumsum(torch.tensor(lp, dtype=torch.int64), 0).to(torch.int32)
+    pt = torch.as_tensor(perm, dtype=torch.long)
+    pc = synth.DecodeCase(case.q[pt], case.k_cache[rows], case.v_cache[rows], cup, case.sinks, case.max_seqlen,
+                          case.scale)
+    out_p, lse_p = run(pc)
+    pd = torch.as_tensor(perm, dtype=torch.long, device=dev)
+    assert torch.equal(out_p, out[pd]) and torch.equal(lse_p, lse[pd])
+
+
 @pytest.mark.parametrize("window", [0, 128])
 def test_decode_multi_step(window):
     """Append one token per sequence and decode again, five times over; every
