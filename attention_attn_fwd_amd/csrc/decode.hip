@@ -512,13 +512,15 @@ decode_merge_few_kernel(DecParams p) {
     if (lane == 0) p.lse[(size_t)n * p.Hq + head] = (mtot + fast_log2(l)) * kLn2;
 }
 
-// Many chunks: one workgroup per (sequence, head) with more than one chunk.  The
-// block-wide maximum over the chunks' m (and the sink) comes first; then wave
-// w sums chunks w, w + 4, ... with lane = d, and wave 0 adds the four sums.
+// Many chunks: one workgroup per (sequence, head) with more than one chunk.
+// Wave w merges chunks w, w + 4, ... online (lane = d; running maximum and
+// rescale, so the loads of several chunks are in flight at once and the
+// partials are read in one pass), then wave 0 merges the four waves' (m, l,
+// O) with the sink.
 __global__ void __launch_bounds__(256)
 decode_merge_kernel(DecParams p) {
     __shared__ float red_o[4][64];
-    __shared__ float red_x[4];
+    __shared__ float red_m[4], red_l[4];
     const int head = blockIdx.x, n = blockIdx.y;
     int base, L, vis_lo;
     seq_range(p, n, base, L, vis_lo);
@@ -527,32 +529,38 @@ decode_merge_kernel(DecParams p) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const float* src = p.part + ((size_t)n * p.Hq + head) * p.n_splits * kPartStride;
     const float sink = p.sinks[head];
-    // maximum over the sink and every chunk's m (log2 units)
-    float mx = sink * kLog2e;
-    for (int s = tid; s < n_act; s += 256) mx = fmaxf(mx, src[s * kPartStride + 64]);
-    for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
-    if (lane == 0) red_x[wave] = mx;
-    __syncthreads();
-    const float mtot = fmaxf(fmaxf(red_x[0], red_x[1]), fmaxf(red_x[2], red_x[3]));
-    __syncthreads();  // red_x is reused below
-    float o = 0.0f, l = 0.0f;
-#pragma unroll 4
+    // every chunk holds a visible key, so its m is finite; a wave without
+    // chunks keeps m = -inf, l = 0, O = 0 and adds nothing below
+    float m = -INFINITY, l = 0.0f, o = 0.0f;
+#pragma unroll 8
     for (int s = wave; s < n_act; s += 4) {
         const float* c = src + s * kPartStride;
-        const float a = fast_exp2(c[64] - mtot);
-        o = fmaf(c[lane], a, o);
-        l = fmaf(c[65], a, l);
+        const float ms = c[64], ls = c[65], os = c[lane];
+        const float mn = fmaxf(m, ms);
+        const float a = fast_exp2(m - mn), b = fast_exp2(ms - mn);
+        l = fmaf(l, a, ls * b);
+        o = fmaf(o, a, os * b);
+        m = mn;
     }
     red_o[wave][lane] = o;
-    if (lane == 0) red_x[wave] = l;
+    if (lane == 0) {
+        red_m[wave] = m;
+        red_l[wave] = l;
+    }
     __syncthreads();
     if (wave != 0) return;
-    o = (red_o[0][lane] + red_o[1][lane]) + (red_o[2][lane] + red_o[3][lane]);
-    l = (red_x[0] + red_x[1]) + (red_x[2] + red_x[3]);
-    if (sink != -INFINITY) l += fast_exp2(sink * kLog2e - mtot);
-    const __bf16 rb = (__bf16)(o / l);
+    const float s2 = sink * kLog2e;
+    const float mtot = fmaxf(fmaxf(fmaxf(red_m[0], red_m[1]), fmaxf(red_m[2], red_m[3])), s2);
+    float lt = sink == -INFINITY ? 0.0f : fast_exp2(s2 - mtot), ot = 0.0f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        const float a = fast_exp2(red_m[w] - mtot);
+        lt = fmaf(red_l[w], a, lt);
+        ot = fmaf(red_o[w][lane], a, ot);
+    }
+    const __bf16 rb = (__bf16)(ot / lt);
     p.out[((size_t)n * p.Hq + head) * kHeadDim + lane] = __builtin_bit_cast(uint16_t, rb);
-    if (lane == 0) p.lse[(size_t)n * p.Hq + head] = (mtot + fast_log2(l)) * kLn2;
+    if (lane == 0) p.lse[(size_t)n * p.Hq + head] = (mtot + fast_log2(lt)) * kLn2;
 }
 
 }  // namespace
