@@ -10,19 +10,22 @@
 //
 // The work is memory bound: every K/V byte is read once and serves all G
 // query heads of its KV head.
-//   split kernel : grid (chunk of visible keys, group of 4 KV heads x head
-//     block, sequence); chunks are only cut when too few (sequence, group)
-//     pairs would fill the chip.  Each wave owns one KV head, so the 4 waves of a
-//     workgroup stream adjacent 128-byte rows of the same tokens (512
-//     contiguous bytes per token for K and again for V).  A wave walks its
-//     chunk in 64-key tiles: whole K and V rows (8 lanes per 128-byte row)
-//     go through wave-private LDS tiles, K read back as MFMA A operands and V
-//     transposed, S^T = K Q^T and O^T = V^T P^T on 32x32x16 bf16 MFMAs with the G query
-//     heads as columns, an online softmax across tiles, and the next tile's
-//     loads in flight while the current one is computed.  Waves never
-//     synchronise.  A sequence that fits in one chunk is finished in place
-//     (sink folded in, out and lse written); otherwise the wave writes one
-//     partial (unnormalised O, running max m in log2 units, sum l) per head.
+//   split kernel : grid (chunk of visible keys, block of 2 KV heads -- 4 for
+//     windows of at most 256 keys -- x head block, sequence); chunks are only
+//     cut when too few (sequence, block) pairs would fill the chip, and with
+//     one chunk per sequence and at most 256 sequences the workgroups take
+//     their items in a length-ranked order (below).  Each wave owns one KV
+//     head, so the waves of a workgroup stream adjacent 128-byte rows of the
+//     same tokens.  A wave walks its chunk in 64-key tiles: whole K and V
+//     rows (8 lanes per 128-byte row, non-temporal loads) go through
+//     wave-private LDS tiles, K read back as MFMA A operands and V
+//     transposed, S^T = K Q^T and O^T = V^T P^T on 32x32x16 bf16 MFMAs with
+//     the G query heads as columns, an online softmax across tiles, and the
+//     next tile's loads in flight while the current one is computed.  Waves
+//     synchronise only in the ranking prologue.  A sequence that fits in one
+//     chunk is finished in place (sink folded in, out and lse written);
+//     otherwise the wave writes one partial (unnormalised O, running max m in
+//     log2 units, sum l) per head.
 //   merge kernels (one wave per (sequence, head) when there are at most 16
 //     chunks, one workgroup per (sequence, head) otherwise):
 //     m = max(sink, m_s), l = 2^(sink - m) + sum l_s 2^(m_s - m),
@@ -89,8 +92,8 @@ __device__ __forceinline__ void seq_range(const DecParams& p, int n, int& base, 
 // kPaged != 0: K/V rows are found through the block table (slot = position &
 // ring_mask, page = bt[n][slot >> ps_shift], row = slot & ps_mask); the page
 // indices of a tile are loaded one tile ahead of its K/V rows.
-//   kPaged == 1 (pages of 1-4 tokens): every lane loads the page of each of
-//     its 8 rows (8 vector loads per tile).
+//   kPaged == 1 (pages of 1-4 tokens, or of 2^32 bytes or more): every lane
+//     loads the page of each of its 8 rows (8 vector loads per tile).
 //   kPaged == 2 (pages of 8 or more tokens, page bytes below 2^32, a
 //     window): the rows a lane group reads in step j are 8 consecutive
 //     positions, which cross at most one page boundary (the ring, a multiple
