@@ -13,8 +13,8 @@
 //   split kernel : grid (chunk of visible keys, block of 2 KV heads -- 4 for
 //     windows of at most 256 keys -- x head block, sequence); chunks are only
 //     cut when too few (sequence, block) pairs would fill the chip, and with
-//     one chunk per sequence and at most 256 sequences the workgroups take
-//     their items in a length-ranked order (below).  Each wave owns one KV
+//     two-head blocks, one chunk per sequence and at most 256 sequences the
+//     workgroups take their items in a length-ranked order (below).  Each wave owns one KV
 //     head, so the waves of a workgroup stream adjacent 128-byte rows of the
 //     same tokens.  A wave walks its chunk in 64-key tiles: whole K and V
 //     rows (8 lanes per 128-byte row, non-temporal loads) go through
