@@ -20,7 +20,8 @@
 //            with lse*log2(e) in the workspace for dkdv.
 //   dkdv   : key-outer.  A workgroup owns 128 keys of one KV head (32 per
 //            wave) and walks the query columns (position, head-of-group) that
-//            can see them, 64 columns per step.  S = Q K^T and dP = dO V^T
+//            can see them, 128 columns per step (four 32-column blocks, each
+//            skipped when none of its columns sees the wave's keys).  S = Q K^T and dP = dO V^T
 //            put one key per lane and the columns in the accumulator
 //            registers, which is the operand layout of the two products
 //            that contract over columns: dV^T += dO^T P and dK^T += Q^T dS.
@@ -47,6 +48,9 @@ namespace {
 #endif
 #ifndef GPTOSS_DQ_WAVES
 #define GPTOSS_DQ_WAVES 4
+#endif
+#ifndef GPTOSS_DKDV_COLS
+#define GPTOSS_DKDV_COLS 128
 #endif
 
 struct BwdParams {
@@ -121,7 +125,8 @@ bwd_dsink_kernel(BwdParams p) {
 constexpr int kKvWaves = GPTOSS_DKDV_WAVES;
 constexpr int kKvThreads = 64 * kKvWaves;
 constexpr int kKeysPerBlock = 32 * kKvWaves;  // 32 keys per wave
-constexpr int kColsPerStep = 64;
+constexpr int kColsPerStep = GPTOSS_DKDV_COLS;  // 64 or 128
+constexpr int kKvBlocks = kColsPerStep / 32;    // 32-column blocks per step
 constexpr int kKvStRows = kKvThreads / 8;            // columns staged per pass
 constexpr int kKvStPasses = kColsPerStep / kKvStRows;
 
@@ -145,8 +150,8 @@ __device__ __forceinline__ void dkdv_coords(const BwdParams& p, int n_kt, int bi
 
 __global__ void __launch_bounds__(kKvThreads, 2)
 bwd_dkdv_kernel(BwdParams p, int n_kt) {
-    __shared__ uint4 sQ[2][kTileUnits];
-    __shared__ uint4 sO[2][kTileUnits];
+    __shared__ uint4 sQ[2][kColsPerStep / 64 * kTileUnits];
+    __shared__ uint4 sO[2][kColsPerStep / 64 * kTileUnits];
     __shared__ float4 sL[2][kColsPerStep / 4];  // lse * log2(e) per column
     __shared__ float4 sD[2][kColsPerStep / 4];  // Dvec per column
     __shared__ int4 sP[2][kColsPerStep / 4];    // position per column
@@ -206,11 +211,12 @@ bwd_dkdv_kernel(BwdParams p, int n_kt) {
         for (int r = 0; r < 16; ++r) dkacc[db][r] = dvacc[db][r] = 0.0f;
 
     // staging: thread stages rows (columns) st_row + kKvStRows j (unit
-    // st_unit) of each 64-column step, and threads 0..63 the per-column
-    // scalars.  A column c maps to (pos_lo + c / G, kvh * G + c % G); when G
-    // divides 64 a step advances every staged column by 64 / G positions.
+    // st_unit) of each step, and threads 0 .. kColsPerStep - 1 the
+    // per-column scalars.  A column c maps to (pos_lo + c / G, kvh * G + c % G); when G
+    // divides the step's columns a step advances every staged column by
+    // kColsPerStep / G positions.
     const int st_row = tid >> 3, st_unit = tid & 7;
-    const bool g64 = (kColsPerStep % G) == 0;
+    const bool g_div = (kColsPerStep % G) == 0;
     const size_t pos_stride = (size_t)Hq * kHeadDim;  // elements per position
     const uint16_t* qsrc = p.rope != nullptr ? p.q_rot : p.q;  // with RoPE: q as the dq kernel rotated it
     const uint16_t* qcol_base = qsrc + ((size_t)sr.row0 * Hq + (size_t)kvh * G) * kHeadDim + 8 * st_unit;
@@ -219,7 +225,7 @@ bwd_dkdv_kernel(BwdParams p, int n_kt) {
     uint4 rq[kKvStPasses], ro[kKvStPasses];
     float2 rld = make_float2(INFINITY, 0.0f);
     int rpos = 0x3fffffff;
-    // per-thread column offsets within a step (constant across steps when G divides 64)
+    // per-thread column offsets within a step (constant across steps when G divides kColsPerStep)
     int st_pos[kKvStPasses], st_head[kKvStPasses];
 #pragma unroll
     for (int j = 0; j < kKvStPasses; ++j) {
@@ -228,7 +234,14 @@ bwd_dkdv_kernel(BwdParams p, int n_kt) {
     }
     const int ld_pos = tid / G, ld_head = tid % G;
     const int pos_per_step = kColsPerStep / G;
-    // Whole steps with G dividing 64 (all but possibly the first one
+    // position offsets of the 32-column blocks within a whole step
+    int blk_lo[kKvBlocks], blk_hi[kKvBlocks];
+#pragma unroll
+    for (int mb = 0; mb < kKvBlocks; ++mb) {
+        blk_lo[mb] = (32 * mb) / G;
+        blk_hi[mb] = (32 * mb + 31) / G;
+    }
+    // Whole steps with G dividing kColsPerStep (all but possibly the first one
     // processed): the rows a thread stages in step st lie st * pos_per_step
     // positions above its rows of step 0, so their addresses are one
     // multiply-add from these step-0 addresses.
@@ -241,11 +254,13 @@ bwd_dkdv_kernel(BwdParams p, int n_kt) {
         o_row0[j] = reinterpret_cast<const char*>(ocol_base + off);
     }
     const char* ld_row0 = reinterpret_cast<const char*>(ld_base + (size_t)(pos_lo + ld_pos) * Hq + ld_head);
-    const uint32_t step_bytes = (uint32_t)(pos_per_step * pos_stride * sizeof(uint16_t));  // <= 1 MiB
-    const uint32_t ld_step_bytes = (uint32_t)(pos_per_step * Hq * sizeof(float2));
+    // (64-bit: with G = 1 a step spans 128 positions of Hq heads, and only
+    // the row count T * Hq is bounded)
+    const uint64_t step_bytes = (uint64_t)pos_per_step * pos_stride * sizeof(uint16_t);
+    const uint64_t ld_step_bytes = (uint64_t)pos_per_step * Hq * sizeof(float2);
     auto load_step = [&](int st) {
         const int c0 = st * kColsPerStep;
-        if (g64 && c0 + kColsPerStep <= n_cols) {  // wave-uniform
+        if (g_div && c0 + kColsPerStep <= n_cols) {  // wave-uniform
             const uint64_t dq = (uint64_t)(uint32_t)st * step_bytes;
 #pragma unroll
             for (int j = 0; j < kKvStPasses; ++j) {
@@ -374,16 +389,37 @@ bwd_dkdv_kernel(BwdParams p, int n_kt) {
         if (has_next) load_step(st - 1);
 
         const int c0 = st * kColsPerStep;
-        const bool whole = g64 && c0 + kColsPerStep <= n_cols;  // no scalar divisions by G then
+        const bool whole = g_div && c0 + kColsPerStep <= n_cols;  // no scalar divisions by G then
         const int tp_min = pos_lo + (whole ? st * pos_per_step : c0 / G);
         const int tp_max = min(whole ? tp_min + pos_per_step - 1 : pos_lo + (min(c0 + kColsPerStep, n_cols) - 1) / G,
                                S - 1);
         const bool skip = !wave_active || tp_max < kw0 || (W > 0 && tp_min - kw1 >= W);
         if (!skip) {
-            const bool need_mask = !(tp_min >= kw1 && (W == 0 || tp_max - kw0 < W));
-            block(sQ[buf], sO[buf], sL[buf], sD[buf], sP[buf], 0, need_mask);
-            __builtin_amdgcn_sched_barrier(0);  // keep the two blocks' live ranges apart
-            block(sQ[buf], sO[buf], sL[buf], sD[buf], sP[buf], 1, need_mask);
+            // Per 32-column block: its position range; live if one of its
+            // columns sees one of the wave's keys, masked unless every column
+            // sees all of them (a block none sees contributes exactly nothing).
+            bool live[kKvBlocks], need_mask[kKvBlocks];
+#pragma unroll
+            for (int mb = 0; mb < kKvBlocks; ++mb) {
+                int bmin, bmax;
+                bool any = true;
+                if (whole) {
+                    bmin = tp_min + blk_lo[mb];
+                    bmax = tp_min + blk_hi[mb];
+                } else {
+                    const int cb = c0 + 32 * mb;
+                    any = cb < n_cols;
+                    bmin = pos_lo + cb / G;
+                    bmax = pos_lo + (min(cb + 31, n_cols - 1)) / G;
+                }
+                live[mb] = any && bmax >= kw0 && (W == 0 || bmin - kw1 < W);
+                need_mask[mb] = !(bmin >= kw1 && (W == 0 || bmax - kw0 < W));
+            }
+#pragma unroll
+            for (int mb = 0; mb < kKvBlocks; ++mb) {
+                if (live[mb]) block(sQ[buf], sO[buf], sL[buf], sD[buf], sP[buf], mb, need_mask[mb]);
+                __builtin_amdgcn_sched_barrier(0);  // keep the blocks' live ranges apart
+            }
         }
 
         if (has_next) store_step(buf ^ 1);

@@ -550,15 +550,35 @@ def digest_traffic(d):
     --window <w>` (each of the part's kernels averaged over its dispatches),
     scaled by what the counters read for a plain copy of COPY_BYTES: reads
     by COPY_BYTES / FETCH_SIZE of the copy, writes by COPY_BYTES /
-    WRITE_SIZE of the copy."""
+    WRITE_SIZE of the copy.  A part with no runs under `d` keeps its
+    entries from the existing file while its sources still hash to the
+    digest recorded there (its bytes were measured on the same kernels);
+    otherwise it is left out."""
     def copy_kib(counter):
         v = read_counter(os.path.join(d, f"copy_{counter}", "run_counter_collection.csv"), counter)
         big = [x for vals in v.values() for x in vals if x * 1024 > COPY_BYTES / 8]
         return sum(big) / len(big)
+    try:
+        with open(os.path.join(ROOT, "profiles", "traffic.json")) as f:
+            old = json.load(f)
+    except (OSError, ValueError):
+        old = {}
     rk, wk = copy_kib("FETCH_SIZE"), copy_kib("WRITE_SIZE")
     rcal, wcal = COPY_BYTES / (rk * 1024), COPY_BYTES / (wk * 1024)
-    per_launch, per_kernel = {}, {}
+    per_launch, per_kernel, digests = {}, {}, {}
     for part, kernels in PART_KERNELS.items():
+        if not any(os.path.isdir(os.path.join(d, f"{part}_{w}_{c}"))
+                   for w in WINDOWS for c in ("FETCH_SIZE", "WRITE_SIZE")):
+            if old.get("source_sha256", {}).get(part) == source_digest(part):
+                digests[part] = old["source_sha256"][part]
+                for w in WINDOWS:
+                    key = f"{part}_{'full' if w == 0 else 'w%d' % w}"
+                    if key in old.get("bytes_per_launch", {}):
+                        per_launch[key] = old["bytes_per_launch"][key]
+                    per_kernel.update({k: v for k, v in old.get("per_kernel_bytes", {}).items()
+                                       if k.startswith(key + ":")})
+            continue
+        digests[part] = source_digest(part)
         for w in WINDOWS:
             key = f"{part}_{'full' if w == 0 else 'w%d' % w}"
             vals = [read_counter(os.path.join(d, f"{part}_{w}_{c}", "run_counter_collection.csv"), c)
@@ -572,7 +592,7 @@ def digest_traffic(d):
                 per_kernel[f"{key}:{kname}"] = [round(r), round(wb)]
                 total += r + wb
             per_launch[key] = round(total)
-    out = {"source_sha256": {part: source_digest(part) for part in PART_KERNELS},
+    out = {"source_sha256": digests,
            "read_calibration": rcal, "write_calibration": wcal,
            "calibration": f"plain device copy of {COPY_BYTES} bytes: FETCH_SIZE {rk:.0f} KiB, "
                           f"WRITE_SIZE {wk:.0f} KiB",
