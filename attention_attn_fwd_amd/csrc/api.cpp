@@ -12,6 +12,8 @@
 #include <cstdint>
 #include <cstdio>
 #include <cstring>
+#include <memory>
+#include <mutex>
 #include <string>
 
 #include "launch.h"
@@ -85,19 +87,32 @@ gptoss_status check_common(int Hq, int Hkv, int D, int window, float scale) {
     return GPTOSS_OK;
 }
 
-// gfx950 check, cached per device (0 = unknown, 1 = ok, 2 = not gfx950).
-std::atomic<int> g_dev_ok[64];
+// gfx950 check, cached per device (0 = unknown, 1 = ok, 2 = not gfx950) in a
+// table sized once, from the process's device count, on first use (every
+// index hipGetDevice can return has an entry; if the count cannot be read
+// the table is empty and every call asks the runtime again).
+std::once_flag g_dev_once;
+std::unique_ptr<std::atomic<int>[]> g_dev_ok;
+int g_dev_count = 0;
 
 gptoss_status check_device() {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return fail(GPTOSS_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
-    if (dev >= 0 && dev < 64 && g_dev_ok[dev].load(std::memory_order_relaxed) == 1) return GPTOSS_OK;
+    std::call_once(g_dev_once, [] {
+        int n = 0;
+        if (hipGetDeviceCount(&n) != hipSuccess || n < 0) n = 0;
+        g_dev_ok.reset(new std::atomic<int>[n > 0 ? n : 1]);
+        for (int i = 0; i < (n > 0 ? n : 1); ++i) g_dev_ok[i].store(0, std::memory_order_relaxed);
+        g_dev_count = n;
+    });
+    const bool cached = dev >= 0 && dev < g_dev_count;
+    if (cached && g_dev_ok[dev].load(std::memory_order_relaxed) == 1) return GPTOSS_OK;
     hipDeviceProp_t prop;
     e = hipGetDeviceProperties(&prop, dev);
     if (e != hipSuccess) return fail(GPTOSS_ERR_HIP, "hipGetDeviceProperties: %s", hipGetErrorString(e));
     const bool is950 = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
-    if (dev >= 0 && dev < 64) g_dev_ok[dev].store(is950 ? 1 : 2, std::memory_order_relaxed);
+    if (cached) g_dev_ok[dev].store(is950 ? 1 : 2, std::memory_order_relaxed);
     if (!is950)
         return fail(GPTOSS_ERR_UNSUPPORTED, "device %d is %s; this library is built for gfx950 only", dev,
                     prop.gcnArchName);
