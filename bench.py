@@ -278,6 +278,11 @@ def main():
     ms_per_step = timed(lambda: g_steps[next(it) % NSETS].replay(), args.steps)
     total_flops = sum(f for (name, _), f in flops.items() if not name.startswith("varlen"))
     value = total_flops / (ms_per_step * 1e-3) / 1e12
+    # the clocks under this load, after the timed region: sampled while about
+    # 3 s of step replays keep the GPU busy
+    n_load = max(1, int(3000 / ms_per_step))
+    clocks = sample_clocks(lambda: ([g_steps[i % NSETS].replay() for i in range(n_load)],
+                                    torch.cuda.synchronize()))
     del g_steps
 
     # ---- per-part launch durations: a graph of `reps` back-to-back calls of
@@ -520,6 +525,7 @@ def main():
         "roofline_fwd": roofline_fwd,
         "roofline_decode": roofline_decode,
         "cpu_baseline": cpu,
+        "clocks": clocks,
     }
     print(json.dumps(line), flush=True)
 
@@ -601,6 +607,61 @@ def digest_traffic(d):
         json.dump(out, f, indent=1)
         f.write("\n")
     print(json.dumps(out, indent=1))
+
+
+def parse_dpm_level(text):
+    """Current level of an amdgpu pp_dpm_* file ("1: 2100Mhz *" marks it) in
+    MHz, or None."""
+    import re
+    for line in text.splitlines():
+        if line.rstrip().endswith("*"):
+            m = re.search(r"(\d+(?:\.\d+)?)\s*mhz", line, re.I)
+            if m:
+                return float(m.group(1))
+    return None
+
+
+def sample_clocks(load):
+    """The GPU's clock levels as the amdgpu driver reports them
+    (/sys/class/drm/card*/device/pp_dpm_{sclk,mclk,fclk}, the files rocm-smi
+    reads) while `load` (launches that keep the GPU busy for a few seconds)
+    runs: a thread reads them every 0.1 s and the median of each is kept.
+    None where no such file exists (one GPU per box: the first card that
+    has them).  Reported beside the results, never used in them."""
+    import glob
+    import threading
+    import time
+    cards = sorted(os.path.dirname(f) for f in glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+    if not cards:
+        return None
+    dev = cards[0]
+    seen = {"sclk": [], "mclk": [], "fclk": []}
+    stop = threading.Event()
+
+    def reader():
+        time.sleep(0.5)
+        while not stop.is_set():
+            for k in seen:
+                try:
+                    with open(os.path.join(dev, f"pp_dpm_{k}")) as f:
+                        v = parse_dpm_level(f.read())
+                except OSError:
+                    v = None
+                if v is not None:
+                    seen[k].append(v)
+            time.sleep(0.1)
+
+    th = threading.Thread(target=reader, daemon=True)
+    th.start()
+    load()
+    stop.set()
+    th.join()
+    out = {f"{k}_mhz": sorted(v)[len(v) // 2] for k, v in seen.items() if v}
+    if not out:
+        return None
+    out["samples"] = max(len(v) for v in seen.values())
+    out["source"] = "amdgpu pp_dpm_* current levels, median over ~3 s of step replays after the timed region"
+    return out
 
 
 def capture(fn):

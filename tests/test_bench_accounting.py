@@ -65,3 +65,9 @@ def test_traffic_digest_keeps_unmeasured_parts_only_on_unchanged_sources(tmp_pat
     assert "decode_full" not in new["bytes_per_launch"] and "decode" not in new["source_sha256"]
     assert not any(k.startswith("decode") for k in new["per_kernel_bytes"])
     assert "varlen_bwd" not in new["source_sha256"]
+
+
+def test_dpm_level_parsing():
+    assert bench.parse_dpm_level("0: 500Mhz\n1: 1400Mhz\n2: 2100Mhz *\n") == 2100.0
+    assert bench.parse_dpm_level("S: 1733Mhz *\n") == 1733.0
+    assert bench.parse_dpm_level("0: 500Mhz\n1: 2100Mhz\n") is None
