@@ -308,6 +308,8 @@ def main():
 
     def train(i):
         qq, kk, vv = leaves[i % NSETS]
+        for t in (qq, kk, vv, sk_leaf):  # as zero_grad(set_to_none=True): no accumulation kernels
+            t.grad = None
         sink_attention(qq, kk, vv, sk_leaf, 0, scale).backward(sets[i % NSETS]["dout"])
 
     for i in range(NSETS):
@@ -584,6 +586,10 @@ def digest_traffic(d):
                     per_kernel.update({k: v for k, v in old.get("per_kernel_bytes", {}).items()
                                        if k.startswith(key + ":")})
             continue
+        missing = [f"{part}_{w}_{c}" for w in WINDOWS for c in ("FETCH_SIZE", "WRITE_SIZE")
+                   if not os.path.isdir(os.path.join(d, f"{part}_{w}_{c}"))]
+        if missing:
+            raise SystemExit(f"{d}: part {part} was measured only in part (missing runs: {', '.join(missing)})")
         digests[part] = source_digest(part)
         for w in WINDOWS:
             key = f"{part}_{'full' if w == 0 else 'w%d' % w}"

@@ -71,3 +71,17 @@ def test_dpm_level_parsing():
     assert bench.parse_dpm_level("0: 500Mhz\n1: 1400Mhz\n2: 2100Mhz *\n") == 2100.0
     assert bench.parse_dpm_level("S: 1733Mhz *\n") == 1733.0
     assert bench.parse_dpm_level("0: 500Mhz\n1: 2100Mhz\n") is None
+
+
+def test_traffic_digest_refuses_a_part_measured_in_part(tmp_path, monkeypatch):
+    (tmp_path / "profiles").mkdir()
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    monkeypatch.setattr(bench, "source_digest", lambda part: "X")
+    runs = tmp_path / "runs"
+    kib = bench.COPY_BYTES // 1024
+    _counter_csv(runs / "copy_FETCH_SIZE", "FETCH_SIZE", [("copy_kernel", kib // 2)])
+    _counter_csv(runs / "copy_WRITE_SIZE", "WRITE_SIZE", [("copy_kernel", kib)])
+    _counter_csv(runs / "bwd_0_FETCH_SIZE", "FETCH_SIZE", [("bwd_dq_kernel", 1)])
+    with pytest.raises(SystemExit, match="bwd_128_FETCH_SIZE"):
+        bench.digest_traffic(str(runs))
+    assert not (tmp_path / "profiles" / "traffic.json").exists()
