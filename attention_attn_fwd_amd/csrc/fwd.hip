@@ -26,7 +26,7 @@
 //   (ds_read_b64_tr_b16), 8 consecutive keys per lane and MFMA slot group.
 //   Only tiles that intersect the causal/window band are visited; inside a
 //   wave, tiles fully outside its rows' band are skipped and tiles fully
-//   inside it skip the mask.
+//   inside it skip the mask (32-column waves decide that per 32-key half).
 //
 // Per key tile and wave (scores transposed, S^T = K Q^T, so that each lane
 // holds one column's scores and the row reductions are in-lane):
@@ -302,6 +302,17 @@ fwd_kernel(FwdParams p) {
         const bool skip = !wave_active || kt0 > wpmax || (W > 0 && wpmin - (kt0 + kBk - 1) >= W);
         if (!skip) {
             const bool need_mask = !(kt0 + kBk - 1 <= wpmin && (W == 0 || wpmax - kt0 < W));
+            // Within an edge tile, 32-column waves skip the mask of a 32-key
+            // block that every row of the wave sees whole (about 1% faster on
+            // the sliding layer); 64-column waves mask whole tiles (the per-block
+            // branch changed how the compiler interleaves the two blocks and
+            // cost the full-causal layer 2%).
+            bool block_mask[2];
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb) {
+                const int kb0 = kt0 + 32 * mb;
+                block_mask[mb] = !(kb0 + 31 <= wpmin && (W == 0 || wpmax - kb0 < W));
+            }
             const uint4* ks = smem[buf][0];
             const uint4* vs = smem[buf][1];
 
@@ -330,13 +341,17 @@ fwd_kernel(FwdParams p) {
                     for (int nb = 0; nb < kNb; ++nb) {
                         const int dd = col_pos[nb] - kt0 - 8 * g;
 #pragma unroll
-                        for (int mb = 0; mb < 2; ++mb)
+                        for (int mb = 0; mb < 2; ++mb) {
+                            if constexpr (kNb == 1) {
+                                if (!block_mask[mb]) continue;  // wave-uniform
+                            }
 #pragma unroll
                             for (int r = 0; r < 16; ++r) {
                                 const int cr = 32 * mb + 16 * (r >> 3) + (r & 7);
                                 const bool vis = (unsigned)(dd - cr) < Weff;
                                 sacc[mb][nb][r] = vis ? sacc[mb][nb][r] : -INFINITY;
                             }
+                        }
                     }
                 }
             };

@@ -278,11 +278,7 @@ def main():
     ms_per_step = timed(lambda: g_steps[next(it) % NSETS].replay(), args.steps)
     total_flops = sum(f for (name, _), f in flops.items() if not name.startswith("varlen"))
     value = total_flops / (ms_per_step * 1e-3) / 1e12
-    # the clocks under this load, after the timed region: sampled while about
-    # 3 s of step replays keep the GPU busy
-    n_load = max(1, int(3000 / ms_per_step))
-    clocks = sample_clocks(lambda: ([g_steps[i % NSETS].replay() for i in range(n_load)],
-                                    torch.cuda.synchronize()))
+    g_clock = g_steps[0]  # replayed again at the very end to sample the clocks under this load
     del g_steps
 
     # ---- per-part launch durations: a graph of `reps` back-to-back calls of
@@ -510,6 +506,13 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(case, dout_cpu)
+
+    # the clocks under the step's load, after everything else was timed (so
+    # that the load cannot change another measurement): sampled while about
+    # 3 s of step replays keep the GPU busy
+    n_load = max(1, int(3000 / ms_per_step))
+    clocks = sample_clocks(lambda: ([g_clock.replay() for _ in range(n_load)], torch.cuda.synchronize()))
+    del g_clock
 
     line = {
         "metric": "attn fwd/bwd TFLOP/s (unmasked FLOPs) + decode GB/s, % of MI355X roofline",
