@@ -8,6 +8,7 @@ import os
 import shutil
 import subprocess
 import sys
+import tempfile
 
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG_DIR)
@@ -20,10 +21,17 @@ SOURCES = ["api.cpp", "plan.cpp", "fwd.hip", "decode.hip", "bwd.hip", "rope.hip"
 # Packed-fp32 VALU forms are kept out of generated code; hipcc's host pass
 # warns that it does not know the feature, which is harmless.
 HIP_FLAGS = [
-    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-munsafe-fp-atomics", "-Wall", "-Wno-unused-function",
 ]
+
+# Per-source additions.  The forward is scheduled with LLVM's iterative ILP
+# machine scheduler: the full-causal forward runs about 3% faster with it
+# (589-592 against 606-619 us at B=4 S=4096, interleaved timing, results
+# bit-identical); the backward kernels ran 2-6% slower with it and keep the
+# default scheduler.
+SOURCE_FLAGS = {"fwd.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"]}
 
 
 def hipcc_path():
@@ -34,21 +42,43 @@ def hipcc_path():
 
 
 def build(verbose=False):
-    """Compile every source into LIB_PATH (always recompiles)."""
+    """Compile every source (in parallel, each into its own object) and link
+    them into LIB_PATH (always recompiles)."""
+    hipcc = hipcc_path()
+    tmpdir = tempfile.mkdtemp(prefix="gptoss_build_")
     tmp = LIB_PATH + ".tmp%d" % os.getpid()
-    cmd = [hipcc_path(), *HIP_FLAGS, "-I", os.path.join(ROOT, "include"), "-I", CSRC,
-           *[os.path.join(CSRC, s) for s in SOURCES], "-o", tmp]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    if res.returncode != 0:
+    try:
+        procs = []
+        for src in SOURCES:
+            obj = os.path.join(tmpdir, src + ".o")
+            cmd = [hipcc, *HIP_FLAGS, *SOURCE_FLAGS.get(src, []), "-I", os.path.join(ROOT, "include"),
+                   "-I", CSRC, "-c", os.path.join(CSRC, src), "-o", obj]
+            if verbose:
+                print(" ".join(cmd), flush=True)
+            procs.append((src, obj, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE,
+                                                     text=True)))
+        objs, errors, noise = [], [], []
+        for src, obj, proc in procs:
+            out, err = proc.communicate()
+            if proc.returncode != 0:
+                errors.append(f"{src}:\n{out}{err}")
+            noise += [ln for ln in err.splitlines() if "packed-fp32-ops" not in ln]
+            objs.append(obj)
+        if errors:
+            raise RuntimeError("hipcc failed:\n" + "\n".join(errors))
+        link = [hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
+        if verbose:
+            print(" ".join(link), flush=True)
+        res = subprocess.run(link, capture_output=True, text=True)
+        if res.returncode != 0:
+            raise RuntimeError("hipcc link failed:\n" + res.stdout + res.stderr)
+        if verbose and noise:
+            print("\n".join(noise), file=sys.stderr)
+        os.replace(tmp, LIB_PATH)
+    finally:
         if os.path.exists(tmp):
             os.unlink(tmp)
-        raise RuntimeError("hipcc failed:\n" + res.stdout + res.stderr)
-    noise = [ln for ln in res.stderr.splitlines() if "packed-fp32-ops" not in ln]
-    if verbose and noise:
-        print("\n".join(noise), file=sys.stderr)
-    os.replace(tmp, LIB_PATH)
+        shutil.rmtree(tmpdir, ignore_errors=True)
     return LIB_PATH
 
 

@@ -49,15 +49,30 @@ PART_SOURCES = {"fwd": ("fwd.hip", "common.h", "launch.h"),
                 "decode": ("decode.hip", "common.h", "launch.h", "plan.cpp")}
 
 
+def build_source_flags():
+    """The build's per-source compiler flags (attention_attn_fwd_amd/build.py
+    SOURCE_FLAGS), read without importing the package."""
+    import importlib.util
+    spec = importlib.util.spec_from_file_location(
+        "_gptoss_build", os.path.join(ROOT, "attention_attn_fwd_amd", "build.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod.SOURCE_FLAGS
+
+
 def source_digest(part):
     """sha256 over the library sources of `part` (fwd, bwd or decode, the
-    packed-document parts as their dense kind)."""
+    packed-document parts as their dense kind) and the extra compiler flags
+    the build gives each of them."""
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "attention_attn_fwd_amd", "csrc")
+    flags = build_source_flags()
     for name in PART_SOURCES[part.replace("varlen_", "")]:
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + b"\0" + f.read())
+        if flags.get(name):
+            h.update(b"\0flags\0" + " ".join(flags[name]).encode())
     return h.hexdigest()
 
 

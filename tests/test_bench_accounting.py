@@ -85,3 +85,13 @@ def test_traffic_digest_refuses_a_part_measured_in_part(tmp_path, monkeypatch):
     with pytest.raises(SystemExit, match="bwd_128_FETCH_SIZE"):
         bench.digest_traffic(str(runs))
     assert not (tmp_path / "profiles" / "traffic.json").exists()
+
+
+def test_source_digest_covers_per_source_build_flags(monkeypatch):
+    base = bench.source_digest("fwd")
+    flags = dict(bench.build_source_flags())
+    assert bench.source_digest("bwd") != base
+    flags["fwd.hip"] = ["-mllvm", "-some-other-flag"]
+    monkeypatch.setattr(bench, "build_source_flags", lambda: flags)
+    assert bench.source_digest("fwd") != base
+    assert bench.source_digest("varlen_fwd") == bench.source_digest("fwd")
