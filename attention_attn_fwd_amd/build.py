@@ -26,12 +26,15 @@ HIP_FLAGS = [
     "-munsafe-fp-atomics", "-Wall", "-Wno-unused-function",
 ]
 
-# Per-source additions.  The forward is scheduled with LLVM's iterative ILP
-# machine scheduler: the full-causal forward runs about 3% faster with it
-# (589-592 against 606-619 us at B=4 S=4096, interleaved timing, results
-# bit-identical); the backward kernels ran 2-6% slower with it and keep the
-# default scheduler.
-SOURCE_FLAGS = {"fwd.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"]}
+# Per-source additions: LLVM machine-scheduler strategies chosen by
+# interleaved timing of builds that differ only in the flag (results
+# bit-identical).  The forward with the iterative ILP scheduler: full-causal
+# forward about 3% faster (589-592 against 606-619 us at B=4 S=4096).  The
+# decode with the max-ILP scheduler: the 128-sequence full layer 25.5-25.8
+# against 26.4-26.7 us, the sliding layer unchanged.  The backward kernels
+# ran 2-6% slower with either and keep the default scheduler.
+SOURCE_FLAGS = {"fwd.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"],
+                "decode.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]}
 
 
 def hipcc_path():
