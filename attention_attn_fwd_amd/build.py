@@ -16,7 +16,7 @@ CSRC = os.path.join(PKG_DIR, "csrc")
 LIB_NAME = "libgptoss_attn.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 
-SOURCES = ["api.cpp", "plan.cpp", "fwd.hip", "decode.hip", "bwd.hip", "rope.hip"]
+SOURCES = ["api.cpp", "plan.cpp", "fwd.hip", "decode.hip", "decode_paged.hip", "bwd.hip", "rope.hip"]
 
 # Packed-fp32 VALU forms are kept out of generated code; hipcc's host pass
 # warns that it does not know the feature, which is harmless.
@@ -30,9 +30,10 @@ HIP_FLAGS = [
 # interleaved timing of builds that differ only in the flag (results
 # bit-identical).  The forward with the iterative ILP scheduler: full-causal
 # forward about 3% faster (589-592 against 606-619 us at B=4 S=4096).  The
-# decode with the max-ILP scheduler: the 128-sequence full layer 25.5-25.8
-# against 26.4-26.7 us, the sliding layer unchanged.  The backward kernels
-# ran 2-6% slower with either and keep the default scheduler.
+# packed-cache decode with the max-ILP scheduler: the 128-sequence full layer
+# 25.5-25.8 against 26.4-26.7 us, the sliding layer unchanged; the
+# paged-cache decode kernels (decode_paged.hip) ran 2.3% slower with it and
+# keep the default, as do the backward kernels (2-6% slower with either).
 SOURCE_FLAGS = {"fwd.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"],
                 "decode.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]}
 

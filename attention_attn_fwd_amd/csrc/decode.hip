@@ -43,7 +43,10 @@ namespace {
 constexpr int kTileKeys = kDecodeKeyTile;  // keys per wave step
 constexpr int kPartStride = kDecodePartStride;
 
+}  // namespace
 
+// (Named, not file-local: this file and the paged-cache unit that includes
+// it pass it to each other.)
 struct DecParams {
     const uint16_t* q;
     const uint16_t* kc;
@@ -63,6 +66,15 @@ struct DecParams {
     int ranked;       // one chunk per sequence, N <= kDecodeRankMaxSeqs: items in ranked order
     float c;          // scale * log2(e)
 };
+
+// The paged-cache instantiations of the split kernel (kPaged = 1, 2, 3) are
+// compiled in a unit of their own (decode_paged.hip, which includes this
+// file with GPTOSS_DECODE_PAGED_UNIT defined), so that the build can give
+// the packed-cache kernel and them different instruction schedulers.
+hipError_t launch_decode_split_paged(const DecParams& p, int mode, int kv_per_block, dim3 grid,
+                                     hipStream_t stream);
+
+namespace {
 
 // K/V rows are read once per call: non-temporal loads (the hint that lets
 // the caches evict them first) stream 10-12% faster than plain ones, both
@@ -474,6 +486,7 @@ decode_split_kernel(DecParams p) {
     }
 }
 
+#ifndef GPTOSS_DECODE_PAGED_UNIT
 // Few chunks (at most kFewChunks): one wave per (sequence, head), four heads
 // per workgroup; lane = d, the chunks' partials are read in one unrolled pass.
 constexpr int kFewChunks = 16;
@@ -565,9 +578,27 @@ decode_merge_kernel(DecParams p) {
     p.out[((size_t)n * p.Hq + head) * kHeadDim + lane] = __builtin_bit_cast(uint16_t, rb);
     if (lane == 0) p.lse[(size_t)n * p.Hq + head] = (mtot + fast_log2(lt)) * kLn2;
 }
+#endif  // GPTOSS_DECODE_PAGED_UNIT
 
 }  // namespace
 
+#ifdef GPTOSS_DECODE_PAGED_UNIT
+hipError_t launch_decode_split_paged(const DecParams& p, int mode, int kv_per_block, dim3 grid,
+                                     hipStream_t stream) {
+    if (kv_per_block == 2) {
+        const dim3 block(128);
+        if (mode == 3) hipLaunchKernelGGL((decode_split_kernel<3, 2>), grid, block, 0, stream, p);
+        else if (mode == 2) hipLaunchKernelGGL((decode_split_kernel<2, 2>), grid, block, 0, stream, p);
+        else hipLaunchKernelGGL((decode_split_kernel<1, 2>), grid, block, 0, stream, p);
+    } else {
+        const dim3 block(256);
+        if (mode == 3) hipLaunchKernelGGL((decode_split_kernel<3, 4>), grid, block, 0, stream, p);
+        else if (mode == 2) hipLaunchKernelGGL((decode_split_kernel<2, 4>), grid, block, 0, stream, p);
+        else hipLaunchKernelGGL((decode_split_kernel<1, 4>), grid, block, 0, stream, p);
+    }
+    return hipGetLastError();
+}
+#else
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
     DecParams p;
     p.q = a.q;
@@ -611,20 +642,14 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
     const bool uniform_pages = p.ps_shift >= 3 && page_bytes < (1LL << 32);
     p.page_bytes = uniform_pages ? (uint32_t)page_bytes : 0u;
     const int mode = p.bt == nullptr ? 0 : !uniform_pages ? 1 : p.window == 0 ? 3 : 2;
-    if (kvpb == 2) {
-        const dim3 block(128);
-        if (mode == 3) hipLaunchKernelGGL((decode_split_kernel<3, 2>), grid, block, 0, stream, p);
-        else if (mode == 2) hipLaunchKernelGGL((decode_split_kernel<2, 2>), grid, block, 0, stream, p);
-        else if (mode == 1) hipLaunchKernelGGL((decode_split_kernel<1, 2>), grid, block, 0, stream, p);
-        else hipLaunchKernelGGL((decode_split_kernel<0, 2>), grid, block, 0, stream, p);
+    hipError_t e;
+    if (mode != 0) {
+        e = launch_decode_split_paged(p, mode, kvpb, grid, stream);
     } else {
-        const dim3 block(256);
-        if (mode == 3) hipLaunchKernelGGL((decode_split_kernel<3, 4>), grid, block, 0, stream, p);
-        else if (mode == 2) hipLaunchKernelGGL((decode_split_kernel<2, 4>), grid, block, 0, stream, p);
-        else if (mode == 1) hipLaunchKernelGGL((decode_split_kernel<1, 4>), grid, block, 0, stream, p);
-        else hipLaunchKernelGGL((decode_split_kernel<0, 4>), grid, block, 0, stream, p);
+        if (kvpb == 2) hipLaunchKernelGGL((decode_split_kernel<0, 2>), grid, dim3(128), 0, stream, p);
+        else hipLaunchKernelGGL((decode_split_kernel<0, 4>), grid, dim3(256), 0, stream, p);
+        e = hipGetLastError();
     }
-    hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.n_splits == 1) return e;  // one chunk per sequence: nothing to merge
     if (p.n_splits <= kFewChunks)
         hipLaunchKernelGGL(decode_merge_few_kernel, dim3((a.Hq + 3) / 4, a.N), dim3(256), 0, stream, p);
@@ -681,5 +706,7 @@ hipError_t launch_decode_noalloc(const DecodeArgs& args, hipStream_t stream) {
     }
     return launch_decode(a, stream);
 }
+
+#endif  // GPTOSS_DECODE_PAGED_UNIT
 
 }  // namespace gptoss

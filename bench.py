@@ -46,7 +46,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 # part stays valid while these files are unchanged)
 PART_SOURCES = {"fwd": ("fwd.hip", "common.h", "launch.h"),
                 "bwd": ("bwd.hip", "common.h", "launch.h", "plan.cpp"),
-                "decode": ("decode.hip", "common.h", "launch.h", "plan.cpp")}
+                "decode": ("decode.hip", "decode_paged.hip", "common.h", "launch.h", "plan.cpp")}
 
 
 def build_source_flags():
